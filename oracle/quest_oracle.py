@@ -1,0 +1,413 @@
+"""Plain, slow fp64 CPU oracle of the QuEST quantiser hot path.
+
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The
+product library (libquest, HIP) never calls it and shares no code with it:
+no kernels, headers, helpers, tables or constant generators.
+
+What it computes (sources are the web pages about QuEST, arXiv 2502.05003;
+each function names the page and section it follows):
+
+* Forward: each row of x is cut into blocks of n entries and every block is
+  multiplied by the orthonormal Hadamard matrix; the row is RMS-normalised;
+  the result is projected onto a b-bit symmetric uniform grid whose clip
+  scale alpha_b * RMS minimises the expected squared error for a standard
+  Gaussian; the trust mask marks entries whose quantisation error is at most
+  half a grid step.
+* Backward: the Hadamard-domain gradient is multiplied by the stored mask and
+  transformed back by the inverse Hadamard matrix.
+
+Everything is float64 NumPy.  The Hadamard product is the dense O(n^2)
+definition (a matrix product against the explicit n x n matrix), the clip
+scale alpha_b is found by numerical minimisation, and rounding, masking and
+bit packing are written elementwise.  ``quantize_rows_loop`` repeats the
+quantiser as a literal per-element Python loop for small inputs.
+
+Readings taken where the pages are silent (each listed with its reason in the
+design notes of this repository):
+
+* grid: 2^b levels, outermost levels at +-s with s = alpha_b * RMS, step
+  Delta = 2 s / (L - 1), values beyond +-s clip to the outer level;
+* RMS over the whole row, in the Hadamard domain;
+* a zero row gives s = 0, the middle code L/2, q = 0 and mask 1;
+* codes are offset-binary u = clamp(floor(y / Delta) + L/2, 0, L-1); an exact
+  tie y = j * Delta goes to the larger code;
+* mask = [|q - y| <= Delta / 2], inclusive;
+* Sylvester natural order, orthonormal scaling 1/sqrt(n), no random signs;
+* codes and mask are packed as LSB-first bit streams per row;
+* the backward pass treats the scale as a constant: dX = H (M * G).
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (closed forms, a published table, brute force,
+invariants and hand-packed bytes).  End-to-end values on real tensors are
+not printed on the pages, so beyond those pins the oracle is the reference.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "sylvester_hadamard",
+    "normalized_hadamard",
+    "blockwise_hadamard",
+    "grid_levels",
+    "grid_thresholds",
+    "gaussian_mse",
+    "gaussian_mse_derivative",
+    "fit_alpha",
+    "quantize_rows",
+    "quantize_rows_loop",
+    "pack_lsb_first",
+    "unpack_lsb_first",
+    "quantize_fwd",
+    "dequantize",
+    "trust_bwd",
+]
+
+
+# ---------------------------------------------------------------------------
+# Hadamard transform
+# pith.science review of QuEST, "Assumptions & free parameters" (the
+# standard-math item: Hadamard matrices are orthogonal and fast transforms
+# exist) and "What carries the argument" (the forward step applies a Hadamard
+# transform to weights and activations).
+# ---------------------------------------------------------------------------
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix H_n (entries +-1).
+
+    Built by the doubling recursion H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]],
+    which puts it in natural (Sylvester) order.
+    """
+    if n < 1 or (n & (n - 1)) != 0:
+        raise ValueError(f"Hadamard size must be a power of two, got {n}")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def normalized_hadamard(n: int) -> np.ndarray:
+    """Orthonormal Hadamard matrix H_n / sqrt(n); symmetric and its own inverse."""
+    return sylvester_hadamard(n) / math.sqrt(n)
+
+
+def blockwise_hadamard(x: np.ndarray, n: int) -> np.ndarray:
+    """Apply the orthonormal Hadamard matrix to every length-n block of every row.
+
+    y[r, k*n:(k+1)*n] = (H_n / sqrt(n)) @ x[r, k*n:(k+1)*n], computed as a
+    dense matrix product against the explicit n x n matrix.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    if cols % n != 0:
+        raise ValueError(f"cols={cols} is not a multiple of the block size {n}")
+    h = normalized_hadamard(n)
+    blocks = x.reshape(rows, cols // n, n)
+    # For each block vector v (a row of `blocks`), v @ h.T == (h @ v) as a row.
+    y = blocks @ h.T
+    return y.reshape(rows, cols)
+
+
+# ---------------------------------------------------------------------------
+# The Gaussian-optimal clip scale alpha_b
+# pith.science review of QuEST, "What carries the argument" (the grid scale
+# minimises the L2 error against a standard Gaussian) and "Assumptions & free
+# parameters" (alpha* comes from a fixed N(0,1) target, not from data);
+# atlas.scime.ai summary of QuEST, "Approach" (MSE-optimal clipping fitted to
+# a Gaussian).
+# ---------------------------------------------------------------------------
+
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+def _std_normal_cdf(t: float) -> float:
+    if t == math.inf:
+        return 1.0
+    if t == -math.inf:
+        return 0.0
+    return 0.5 * math.erfc(-t / math.sqrt(2.0))
+
+
+def _std_normal_pdf(t: float) -> float:
+    if math.isinf(t):
+        return 0.0
+    return _INV_SQRT_2PI * math.exp(-0.5 * t * t)
+
+
+def _t_times_pdf(t: float) -> float:
+    if math.isinf(t):
+        return 0.0
+    return t * _std_normal_pdf(t)
+
+
+def grid_levels(alpha: float, b: int) -> list[float]:
+    """The L = 2^b reconstruction levels (2k - L + 1) * alpha / (L - 1), k = 0..L-1.
+
+    The outermost levels sit at +-alpha and neighbours are 2 alpha / (L - 1) apart.
+    """
+    big_l = 1 << b
+    return [(2 * k - big_l + 1) * alpha / (big_l - 1) for k in range(big_l)]
+
+
+def grid_thresholds(alpha: float, b: int) -> list[float]:
+    """Decision thresholds t_0 = -inf < t_1 < ... < t_{L-1} < t_L = +inf.
+
+    Interior thresholds are the midpoints of neighbouring levels, so cell k
+    is [t_k, t_{k+1}) and maps to level k (nearest-level rounding).
+    """
+    lv = grid_levels(alpha, b)
+    inner = [0.5 * (lv[k - 1] + lv[k]) for k in range(1, len(lv))]
+    return [-math.inf] + inner + [math.inf]
+
+
+def gaussian_mse(alpha: float, b: int) -> float:
+    """E[(Q_{alpha,b}(X) - X)^2] for X ~ N(0, 1), in closed form.
+
+    Over a cell [a, c] mapped to level l:
+      int (x - l)^2 phi(x) dx
+        = (1 + l^2) (Phi(c) - Phi(a)) - (c phi(c) - a phi(a)) + 2 l (phi(c) - phi(a)),
+    using int phi = Phi, int x phi = -phi and int x^2 phi = Phi - x phi.
+    """
+    lv = grid_levels(alpha, b)
+    th = grid_thresholds(alpha, b)
+    total = 0.0
+    for k, level in enumerate(lv):
+        a, c = th[k], th[k + 1]
+        mass = _std_normal_cdf(c) - _std_normal_cdf(a)
+        total += (1.0 + level * level) * mass
+        total -= _t_times_pdf(c) - _t_times_pdf(a)
+        total += 2.0 * level * (_std_normal_pdf(c) - _std_normal_pdf(a))
+    return total
+
+
+def gaussian_mse_derivative(alpha: float, b: int) -> float:
+    """d/d alpha of ``gaussian_mse``.
+
+    With level k = c_k alpha, c_k = (2k - L + 1)/(L - 1), the moving cell
+    edges contribute nothing (the integrand is continuous across a midpoint),
+    so  dMSE/d alpha = -2 sum_k c_k [ (phi(t_k) - phi(t_{k+1}))
+                                      - c_k alpha (Phi(t_{k+1}) - Phi(t_k)) ].
+    """
+    big_l = 1 << b
+    th = grid_thresholds(alpha, b)
+    total = 0.0
+    for k in range(big_l):
+        ck = (2 * k - big_l + 1) / (big_l - 1)
+        a, c = th[k], th[k + 1]
+        first_moment = _std_normal_pdf(a) - _std_normal_pdf(c)
+        mass = _std_normal_cdf(c) - _std_normal_cdf(a)
+        total += ck * (first_moment - ck * alpha * mass)
+    return -2.0 * total
+
+
+def _golden_section_min(f, lo: float, hi: float, tol: float) -> float:
+    inv_phi = (math.sqrt(5.0) - 1.0) / 2.0
+    a, b = lo, hi
+    c = b - inv_phi * (b - a)
+    d = a + inv_phi * (b - a)
+    fc, fd = f(c), f(d)
+    while (b - a) > tol:
+        if fc < fd:
+            b, d, fd = d, c, fc
+            c = b - inv_phi * (b - a)
+            fc = f(c)
+        else:
+            a, c, fc = c, d, fd
+            d = a + inv_phi * (b - a)
+            fd = f(d)
+    return 0.5 * (a + b)
+
+
+def fit_alpha(b: int) -> float:
+    """alpha_b = argmin_alpha E[(Q_{alpha,b}(X) - X)^2], X ~ N(0, 1).
+
+    Golden-section search of ``gaussian_mse`` on [0.05, 8], then bisection on
+    the sign of ``gaussian_mse_derivative`` around that point.  The minimum is
+    flat (the MSE is quadratic there), so the golden-section result alone is
+    good to only about 1e-8 relative; the derivative has a clean sign change
+    and bisection takes it to the last bit.
+    """
+    if not 1 <= b <= 16:
+        raise ValueError(f"b must be in [1, 16], got {b}")
+    guess = _golden_section_min(lambda a: gaussian_mse(a, b), 0.05, 8.0, 1e-9)
+    lo, hi = guess * (1.0 - 1e-4), guess * (1.0 + 1e-4)
+    while gaussian_mse_derivative(lo, b) > 0.0:
+        lo *= 0.9
+    while gaussian_mse_derivative(hi, b) < 0.0:
+        hi *= 1.1
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            break
+        if gaussian_mse_derivative(mid, b) < 0.0:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+# ---------------------------------------------------------------------------
+# RMS scale, grid projection and trust mask
+# atlas.scime.ai summary of QuEST, "Approach" (Hadamard transform followed by
+# RMS normalisation and MSE-optimal clipping; gradients are masked for
+# entries whose quantisation error exceeds a trust threshold); pith.science
+# review, "What carries the argument" (projection onto the uniform grid; the
+# mask zeroes entries whose error exceeds half a quantisation interval) and
+# Figure 7 caption (the mask M_alpha*).
+# ---------------------------------------------------------------------------
+
+def quantize_rows(y: np.ndarray, b: int, alpha: float):
+    """Quantise Hadamard-domain rows y (R x C).
+
+    Returns (u, s, m, q):
+      s[r]    = alpha * RMS_r with RMS_r = sqrt(mean_c y[r, c]^2)   (clip scale)
+      u[r, c] = clamp(floor(y / Delta_r) + L/2, 0, L - 1), Delta_r = 2 s_r / (L - 1)
+      q[r, c] = (2 u - L + 1) * Delta_r / 2                      (the grid value)
+      m[r, c] = |q - y| <= Delta_r / 2                            (trust mask)
+    A row of zeros has s = 0; it takes the middle code L/2 and q = 0, m = 1.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    big_l = 1 << b
+    rms = np.sqrt(np.mean(y * y, axis=1))
+    s = alpha * rms
+    delta = 2.0 * s / (big_l - 1)
+    zero_row = delta == 0.0
+    safe_delta = np.where(zero_row, 1.0, delta)
+    u = np.floor(y / safe_delta[:, None]) + big_l // 2
+    u = np.clip(u, 0, big_l - 1)
+    u[zero_row, :] = big_l // 2
+    u = u.astype(np.int64)
+    q = (2 * u - big_l + 1) * delta[:, None] / 2.0
+    m = np.abs(q - y) <= delta[:, None] / 2.0
+    return u, s, m, q
+
+
+def quantize_rows_loop(y, b: int, alpha: float):
+    """The same quantiser as ``quantize_rows`` written as a scalar Python loop.
+
+    Used on small inputs to cross-check the vectorised form.
+    """
+    big_l = 1 << b
+    rows = len(y)
+    cols = len(y[0])
+    u = np.zeros((rows, cols), dtype=np.int64)
+    m = np.zeros((rows, cols), dtype=bool)
+    q = np.zeros((rows, cols), dtype=np.float64)
+    s = np.zeros(rows, dtype=np.float64)
+    for r in range(rows):
+        acc = 0.0
+        for c in range(cols):
+            acc += float(y[r][c]) * float(y[r][c])
+        s_r = alpha * math.sqrt(acc / cols)
+        d_r = 2.0 * s_r / (big_l - 1)
+        s[r] = s_r
+        for c in range(cols):
+            v = float(y[r][c])
+            if d_r == 0.0:
+                code = big_l // 2
+            else:
+                code = math.floor(v / d_r) + big_l // 2
+                code = min(max(code, 0), big_l - 1)
+            level = (2 * code - big_l + 1) * d_r / 2.0
+            u[r, c] = code
+            q[r, c] = level
+            m[r, c] = abs(level - v) <= d_r / 2.0
+    return u, s, m, q
+
+
+# ---------------------------------------------------------------------------
+# Bit packing (a storage layout; the pages only say that INT4 codes are
+# stored and that the mask is kept from the forward pass for the backward).
+# ---------------------------------------------------------------------------
+
+def pack_lsb_first(values: np.ndarray, width: int) -> np.ndarray:
+    """Pack each row of unsigned ints (< 2^width) into an LSB-first byte stream.
+
+    Element c occupies stream bits [c*width, (c+1)*width), low bit first;
+    stream bit 8j + i is bit i of byte j.  Returns R x (C*width/8) uint8.
+    """
+    values = np.asarray(values, dtype=np.int64)
+    rows, cols = values.shape
+    nbits = cols * width
+    if nbits % 8 != 0:
+        raise ValueError("cols * width must be a multiple of 8")
+    if values.size and (values.min() < 0 or values.max() >= (1 << width)):
+        raise ValueError("value out of range for the bit width")
+    bits = (values[:, :, None] >> np.arange(width)[None, None, :]) & 1
+    stream = bits.reshape(rows, nbits)
+    byte_bits = stream.reshape(rows, nbits // 8, 8)
+    packed = (byte_bits << np.arange(8)[None, None, :]).sum(axis=2)
+    return packed.astype(np.uint8)
+
+
+def unpack_lsb_first(packed: np.ndarray, width: int, cols: int) -> np.ndarray:
+    """Inverse of ``pack_lsb_first``: R x (C*width/8) uint8 -> R x C int64."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    if packed.shape[1] * 8 != cols * width:
+        raise ValueError("packed width does not match cols * width / 8")
+    stream = (packed[:, :, None].astype(np.int64) >> np.arange(8)[None, None, :]) & 1
+    stream = stream.reshape(rows, cols, width)
+    return (stream << np.arange(width)[None, None, :]).sum(axis=2)
+
+
+# ---------------------------------------------------------------------------
+# The three calls of the path
+# ---------------------------------------------------------------------------
+
+def quantize_fwd(x: np.ndarray, block: int, b: int, alpha: float | None = None) -> dict:
+    """Forward QuEST quantisation of x (R x C): Hadamard -> RMS -> clip/round -> mask.
+
+    QuEST abstract (codewithpapers.app record; Hadamard normalisation and
+    MSE-optimal fitting), atlas.scime.ai summary "Approach", pith.science
+    review "What carries the argument".
+    Returns packed codes (R x C*b/8 uint8), the clip scale s (R, float64),
+    the packed mask (R x C/8 uint8) and the unpacked intermediates.
+    """
+    if alpha is None:
+        alpha = fit_alpha(b)
+    y = blockwise_hadamard(x, block)
+    u, s, m, q = quantize_rows(y, b, alpha)
+    return {
+        "codes": pack_lsb_first(u, b),
+        "scale": s,
+        "mask": pack_lsb_first(m.astype(np.int64), 1),
+        "y": y,
+        "u": u,
+        "m": m,
+        "q": q,
+        "alpha": alpha,
+    }
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray, cols: int, b: int) -> np.ndarray:
+    """Grid values (2u - L + 1) * s / (L - 1), in the Hadamard domain.
+
+    The conceptual twin of the official repository's ``dequantize_dense``
+    entry (named in the codewithpapers.app record).  Quantised operands stay
+    in the Hadamard domain because the transform is orthogonal and is applied
+    to both operands of a product (pith.science review, "Assumptions & free
+    parameters").
+    """
+    big_l = 1 << b
+    u = unpack_lsb_first(codes, b, cols)
+    s = np.asarray(scale, dtype=np.float64)
+    return (2 * u - big_l + 1) * s[:, None] / (big_l - 1)
+
+
+def trust_bwd(grad: np.ndarray, mask: np.ndarray, block: int) -> np.ndarray:
+    """Trust-gradient backward: dX = H (M * G) per block.
+
+    pith.science review, "What carries the argument" (the Hadamard-domain
+    gradient is multiplied by the binary trust mask) and Figure 2 caption
+    (inverse Hadamard transforms on the backward pass).  H is symmetric and
+    orthonormal, so the inverse transform is the same block product.
+    """
+    grad = np.asarray(grad, dtype=np.float64)
+    m = unpack_lsb_first(mask, 1, grad.shape[1]).astype(np.float64)
+    return blockwise_hadamard(m * grad, block)

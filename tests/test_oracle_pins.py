@@ -1,0 +1,456 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compare the oracle with itself: each check uses a closed form,
+a published table, a library routine (scipy quadrature, brute-force nearest
+level), an exact invariant, or bytes packed by hand.  Together they are meant
+to fail on any plausible slip in the oracle: a dropped term, a wrong sign or
+index, a transposed operand, a wrong reduction axis or bit order.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+from oracle import quest_oracle as qo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load_max_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "max1960_uniform_gaussian.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            levels, step, mse = line.split()
+            rows.append((int(levels), float(step), float(mse)))
+    return rows
+
+
+def _load_packing_examples():
+    out = []
+    with open(os.path.join(GOLDEN, "packing_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            w, vals, byts = (p.strip() for p in line.split("|"))
+            out.append((int(w), [int(v) for v in vals.split(",")], [int(h, 16) for h in byts.split(",")]))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Hadamard (P-H1, P-H2)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_orthonormal_symmetric_involution(n):
+    h = qo.normalized_hadamard(n)
+    assert np.array_equal(h, h.T)
+    assert np.max(np.abs(h @ h - np.eye(n))) <= 1e-14
+    assert np.max(np.abs(h @ h.T - np.eye(n))) <= 1e-14
+
+
+def test_hadamard_2_literal():
+    h = qo.normalized_hadamard(2)
+    r = 1.0 / math.sqrt(2.0)
+    assert np.allclose(h, [[r, r], [r, -r]], rtol=0, atol=1e-16)
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 128, 256])
+def test_hadamard_matches_popcount_formula(n):
+    # Sylvester order: H[i][j] = (-1)^popcount(i & j), an independent definition.
+    h = qo.sylvester_hadamard(n)
+    ref = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(n)] for i in range(n)])
+    assert np.array_equal(h, ref)
+
+
+def test_blockwise_hadamard_impulse_response():
+    # A unit impulse at column k*n + j must land only in block k, as column j of H/sqrt(n).
+    n, k_blocks = 64, 3
+    hn = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(n)] for i in range(n)]) / 8.0
+    for k in range(k_blocks):
+        for j in (0, 1, 5, 63):
+            x = np.zeros((1, n * k_blocks))
+            x[0, k * n + j] = 1.0
+            y = qo.blockwise_hadamard(x, n)
+            expect = np.zeros(n * k_blocks)
+            expect[k * n : (k + 1) * n] = hn[:, j]
+            assert np.max(np.abs(y[0] - expect)) <= 1e-15
+
+
+def test_blockwise_hadamard_first_basis_vector_and_norm():
+    rng = np.random.default_rng(11)
+    n = 128
+    e0 = np.zeros((1, n))
+    e0[0, 0] = 1.0
+    assert np.allclose(qo.blockwise_hadamard(e0, n), np.full((1, n), 1 / math.sqrt(n)), rtol=0, atol=1e-16)
+    x = rng.standard_normal((5, 4 * n)) * rng.uniform(0.1, 10, size=(5, 1))
+    y = qo.blockwise_hadamard(x, n)
+    for r in range(5):
+        for k in range(4):
+            nx = np.linalg.norm(x[r, k * n : (k + 1) * n])
+            ny = np.linalg.norm(y[r, k * n : (k + 1) * n])
+            assert abs(nx - ny) <= 1e-13 * nx
+
+
+def test_blockwise_hadamard_round_trip():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((7, 512))
+    for n in (64, 128, 256):
+        back = qo.blockwise_hadamard(qo.blockwise_hadamard(x, n), n)
+        assert np.max(np.abs(back - x)) <= 1e-13
+
+
+def test_blockwise_hadamard_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        qo.blockwise_hadamard(np.zeros((2, 100)), 64)
+    with pytest.raises(ValueError):
+        qo.normalized_hadamard(96)
+
+
+# ---------------------------------------------------------------------------
+# Gaussian MSE and alpha_b (P-A1 .. P-A4)
+# ---------------------------------------------------------------------------
+
+def _quad_mse(alpha, b):
+    """MSE of the grid by numerical quadrature of (Q(x) - x)^2 phi(x), cell by cell."""
+    big_l = 1 << b
+    step = 2 * alpha / (big_l - 1)
+    total = 0.0
+    for k in range(big_l):
+        level = -alpha + k * step
+        lo = -np.inf if k == 0 else level - step / 2
+        hi = np.inf if k == big_l - 1 else level + step / 2
+        val, _ = integrate.quad(lambda x: (x - level) ** 2 * stats.norm.pdf(x), lo, hi, epsabs=1e-14, epsrel=1e-12)
+        total += val
+    return total
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 6])
+@pytest.mark.parametrize("alpha", [0.3, 0.9, 1.7, 2.6, 4.0])
+def test_gaussian_mse_closed_form_matches_quadrature(b, alpha):
+    assert abs(qo.gaussian_mse(alpha, b) - _quad_mse(alpha, b)) <= 1e-10
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("alpha", [0.5, 1.3, 2.2, 3.1])
+def test_gaussian_mse_derivative_matches_finite_difference(b, alpha):
+    h = 1e-5
+    fd = (qo.gaussian_mse(alpha + h, b) - qo.gaussian_mse(alpha - h, b)) / (2 * h)
+    assert abs(qo.gaussian_mse_derivative(alpha, b) - fd) <= 1e-8
+
+
+def test_one_bit_closed_form():
+    # b = 1: levels +-alpha, threshold 0; E[(X - alpha sgn X)^2] = 1 - 2 alpha sqrt(2/pi) + alpha^2,
+    # minimised at alpha = sqrt(2/pi) (the Gaussian mean absolute value) with MSE = 1 - 2/pi.
+    a1 = qo.fit_alpha(1)
+    assert abs(a1 - math.sqrt(2 / math.pi)) <= 1e-12
+    for a in (0.2, 0.7978, 1.5):
+        assert abs(qo.gaussian_mse(a, 1) - (1 - 2 * a * math.sqrt(2 / math.pi) + a * a)) <= 1e-13
+    assert abs(qo.gaussian_mse(a1, 1) - (1 - 2 / math.pi)) <= 1e-13
+
+
+def test_alpha_matches_max_1960_table():
+    for levels, step, mse in _load_max_table():
+        b = int(math.log2(levels))
+        a = qo.fit_alpha(b)
+        assert abs(2 * a / (levels - 1) - step) <= 6e-4 * step, (levels, 2 * a / (levels - 1), step)
+        assert abs(qo.gaussian_mse(a, b) - mse) <= 6e-4 * mse, (levels, qo.gaussian_mse(a, b), mse)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 8])
+def test_alpha_is_a_strict_local_minimum(b):
+    a = qo.fit_alpha(b)
+    m0 = qo.gaussian_mse(a, b)
+    assert qo.gaussian_mse(a * (1 - 1e-3), b) > m0
+    assert qo.gaussian_mse(a * (1 + 1e-3), b) > m0
+    assert abs(qo.gaussian_mse_derivative(a, b)) <= 1e-12
+
+
+def test_mse_strictly_decreasing_in_bits():
+    mses = [qo.gaussian_mse(qo.fit_alpha(b), b) for b in range(1, 9)]
+    assert all(x > y for x, y in zip(mses, mses[1:]))
+
+
+def test_empirical_mse_decreasing_in_bits():
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal((1, 4096))
+    errs = []
+    for b in range(1, 9):
+        _, _, _, q = qo.quantize_rows(y, b, qo.fit_alpha(b))
+        errs.append(float(np.mean((q - y) ** 2)))
+    assert all(x > y for x, y in zip(errs, errs[1:]))
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_mse_monte_carlo(b):
+    # 10^7 N(0,1) samples quantised by brute-force nearest level of the fitted grid.
+    rng = np.random.default_rng(1234 + b)
+    a = qo.fit_alpha(b)
+    big_l = 1 << b
+    levels = np.array([-a + k * 2 * a / (big_l - 1) for k in range(big_l)])
+    sq = []
+    for _ in range(10):
+        x = rng.standard_normal(1_000_000)
+        idx = np.argmin(np.abs(x[:, None] - levels[None, :]), axis=1)
+        sq.append((levels[idx] - x) ** 2)
+    sq = np.concatenate(sq)
+    est, se = sq.mean(), sq.std() / math.sqrt(sq.size)
+    assert abs(est - qo.gaussian_mse(a, b)) <= 4 * se
+
+
+# ---------------------------------------------------------------------------
+# Quantiser (P-Q1 .. P-Q5)
+# ---------------------------------------------------------------------------
+
+def _brute_force_codes(y, s, b):
+    big_l = 1 << b
+    out = np.zeros(y.shape, dtype=np.int64)
+    for r in range(y.shape[0]):
+        # symmetric form of the levels, so that y = 0 is an exact tie for even L
+        levels = np.array([(2 * k - big_l + 1) * s[r] / (big_l - 1) for k in range(big_l)])
+        dist = np.abs(y[r][:, None] - levels[None, :])
+        # ties go to the larger code (argmin of the reversed order)
+        out[r] = big_l - 1 - np.argmin(dist[:, ::-1], axis=1)
+    return out
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+def test_codes_equal_brute_force_nearest_level(b):
+    rng = np.random.default_rng(100 + b)
+    y = rng.standard_normal((8, 256)) * rng.uniform(0.5, 3, size=(8, 1))
+    y[0, :5] = [10.0, -10.0, 0.0, 1e-9, -1e-9]  # clipped both sides, around zero
+    u, s, _, _ = qo.quantize_rows(y, b, qo.fit_alpha(b))
+    bf = _brute_force_codes(y, s, b)
+    assert np.array_equal(u, bf)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_scale_from_original_domain_norm(b):
+    # Orthogonality: the Hadamard-domain RMS equals ||x_row|| / sqrt(C); s = alpha_b * that.
+    rng = np.random.default_rng(200 + b)
+    x = rng.standard_normal((6, 512)) * np.array([[0.1], [1], [3], [10], [0.01], [7]])
+    x[2, 128:256] *= 50  # a block much louder than the rest of its row
+    out = qo.quantize_fwd(x, 128, b)
+    expect = qo.fit_alpha(b) * np.linalg.norm(x, axis=1) / math.sqrt(512)
+    assert np.max(np.abs(out["scale"] - expect) / expect) <= 1e-13
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_mask_closed_form(b):
+    rng = np.random.default_rng(300 + b)
+    y = rng.standard_normal((16, 512)) * 1.7
+    u, s, m, q = qo.quantize_rows(y, b, qo.fit_alpha(b))
+    big_l = 1 << b
+    thr = s[:, None] * big_l / (big_l - 1)
+    closed = np.abs(y) <= thr
+    away = np.abs(np.abs(y) - thr) > 1e-9 * s[:, None]
+    assert np.array_equal(m[away], closed[away])
+    # every entry inside the clip range is trusted
+    assert np.all(m[np.abs(y) <= s[:, None]])
+    # and untrusted entries exist for Gaussian data
+    assert not np.all(m)
+
+
+def _place_at_fraction_of_threshold(rest, b, kappa, j_steps):
+    """Return y0 with y0 = kappa * j_steps * Delta(row), Delta computed from the row incl. y0.
+
+    With S = sum of the other squares and C entries, Delta = 2 alpha RMS / (L - 1) and
+    RMS^2 = (S + y0^2) / C, the fixed point is y0 = c sqrt(S / (C - c^2)), c = kappa j 2 alpha / (L - 1).
+    """
+    big_l = 1 << b
+    alpha = qo.fit_alpha(b)
+    c = kappa * j_steps * 2 * alpha / (big_l - 1)
+    cols = rest.size + 1
+    return c * math.sqrt(float(np.sum(rest**2)) / (cols - c * c))
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_mask_and_codes_on_both_sides_of_each_threshold(b):
+    # Trust threshold: the outer level sits at s, so a clipped entry is within half a step
+    # exactly when |y| <= s + Delta/2 = (L/2) Delta.  Decision thresholds sit at j Delta.
+    big_l = 1 << b
+    rng = np.random.default_rng(350 + b)
+    rest = rng.standard_normal(511)
+    for kappa, trusted in ((1 - 1e-9, True), (1 + 1e-9, False)):
+        for sign in (1.0, -1.0):
+            y0 = sign * _place_at_fraction_of_threshold(rest, b, kappa, big_l / 2)
+            row = np.concatenate([[y0], rest])[None, :]
+            u, s, m, _ = qo.quantize_rows(row, b, qo.fit_alpha(b))
+            assert bool(m[0, 0]) is trusted, (b, kappa, sign)
+            assert u[0, 0] == (big_l - 1 if sign > 0 else 0)
+    for j in range(1, big_l // 2):
+        for kappa, above in ((1 - 1e-9, False), (1 + 1e-9, True)):
+            for sign in (1.0, -1.0):
+                y0 = sign * _place_at_fraction_of_threshold(rest, b, kappa, j)
+                row = np.concatenate([[y0], rest])[None, :]
+                u, _, m, _ = qo.quantize_rows(row, b, qo.fit_alpha(b))
+                # y = sign * kappa * j * Delta: floor(y / Delta) is j-1 / j above zero,
+                # -j / -j-1 below it.
+                fl = (j if above else j - 1) if sign > 0 else (-j if not above else -j - 1)
+                assert u[0, 0] == fl + big_l // 2, (b, j, kappa, sign)
+                assert m[0, 0]
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_scale_invariance_and_sign_symmetry(b):
+    rng = np.random.default_rng(400 + b)
+    x = rng.standard_normal((4, 256))
+    base = qo.quantize_fwd(x, 128, b)
+    for k in (-7, 3, 20):
+        out = qo.quantize_fwd(x * 2.0**k, 128, b)
+        assert np.array_equal(out["u"], base["u"])
+        assert np.array_equal(out["m"], base["m"])
+        assert np.array_equal(out["scale"], base["scale"] * 2.0**k)
+    neg = qo.quantize_fwd(-x, 128, b)
+    big_l = 1 << b
+    assert np.array_equal(neg["u"], big_l - 1 - base["u"])
+    assert np.array_equal(neg["m"], base["m"])
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_untrusted_fraction_for_gaussian_rows(b):
+    # iid N(0,1) stays iid N(0,1) under an orthonormal transform, so the untrusted
+    # fraction is P(|X| > alpha_b L/(L-1)) = 2 (1 - Phi(alpha_b L/(L-1))).
+    rng = np.random.default_rng(500 + b)
+    x = rng.standard_normal((256, 4096))
+    out = qo.quantize_fwd(x, 128, b)
+    big_l = 1 << b
+    p = 2 * stats.norm.sf(qo.fit_alpha(b) * big_l / (big_l - 1))
+    frac = 1.0 - out["m"].mean()
+    n = out["m"].size
+    assert abs(frac - p) <= 4 * math.sqrt(p * (1 - p) / n) + 2e-4 * p, (frac, p)
+
+
+def test_one_bit_special_case():
+    rng = np.random.default_rng(600)
+    x = rng.standard_normal((5, 256))
+    out = qo.quantize_fwd(x, 64, 1)
+    y = out["y"]
+    s = math.sqrt(2 / math.pi) * np.sqrt(np.mean(y**2, axis=1))
+    assert np.allclose(out["scale"], s, rtol=1e-13, atol=0)
+    assert np.array_equal(out["u"], (y >= 0).astype(np.int64))
+    deq = qo.dequantize(out["codes"], out["scale"], 256, 1)
+    assert np.array_equal(np.abs(deq), np.broadcast_to(out["scale"][:, None], deq.shape))
+    assert np.array_equal(np.sign(deq), np.where(y >= 0, 1.0, -1.0))
+    assert np.array_equal(out["m"], np.abs(y) <= 2 * out["scale"][:, None])
+
+
+def test_zero_row_reading():
+    x = np.zeros((2, 128))
+    x[1] = np.linspace(-1, 1, 128)
+    for b in (1, 2, 3, 4):
+        out = qo.quantize_fwd(x, 128, b)
+        assert out["scale"][0] == 0.0
+        assert np.all(out["u"][0] == (1 << b) // 2)
+        assert np.all(out["m"][0])
+        assert np.all(qo.dequantize(out["codes"], out["scale"], 128, b)[0] == 0.0)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_vectorised_quantiser_matches_scalar_loop(b):
+    rng = np.random.default_rng(700 + b)
+    y = rng.standard_normal((4, 128)) * 2.0
+    y[1] = 0.0
+    vec = qo.quantize_rows(y, b, qo.fit_alpha(b))
+    loop = qo.quantize_rows_loop(y.tolist(), b, qo.fit_alpha(b))
+    for a, c in zip(vec, loop):
+        assert np.allclose(a, c, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Packing and dequantisation (P-P1, P-D1)
+# ---------------------------------------------------------------------------
+
+def test_packing_hand_examples():
+    for width, vals, byts in _load_packing_examples():
+        packed = qo.pack_lsb_first(np.array([vals]), width)
+        assert packed.tolist() == [byts], (width, vals)
+        assert qo.unpack_lsb_first(packed, width, len(vals)).tolist() == [vals]
+
+
+@pytest.mark.parametrize("width", [1, 2, 3, 4, 5, 8])
+def test_packing_round_trip(width):
+    rng = np.random.default_rng(800 + width)
+    v = rng.integers(0, 1 << width, size=(3, 64))
+    assert np.array_equal(qo.unpack_lsb_first(qo.pack_lsb_first(v, width), width, 64), v)
+
+
+def test_packing_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        qo.pack_lsb_first(np.array([[16, 0]]), 4)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_dequantize_returns_grid_values(b):
+    rng = np.random.default_rng(900 + b)
+    x = rng.standard_normal((6, 384)) * 3
+    out = qo.quantize_fwd(x, 128, b)
+    deq = qo.dequantize(out["codes"], out["scale"], 384, b)
+    assert np.allclose(deq, out["q"], rtol=1e-15, atol=0)
+    big_l = 1 << b
+    delta = 2 * out["scale"] / (big_l - 1)
+    err = np.abs(deq - out["y"])
+    assert np.all(err[out["m"]] <= (delta[:, None] / 2 * (1 + 1e-12)).repeat(384, 1)[out["m"]])
+    # every dequantised value is one of the L grid levels of its row
+    levels = (2 * np.arange(big_l) - big_l + 1)[None, :] * (out["scale"][:, None] / (big_l - 1))
+    for r in range(6):
+        assert np.all(np.min(np.abs(deq[r][:, None] - levels[r][None, :]), axis=1) <= 1e-15 * out["scale"][r])
+
+
+# ---------------------------------------------------------------------------
+# Backward (P-B1)
+# ---------------------------------------------------------------------------
+
+def _ones_mask(rows, cols):
+    return qo.pack_lsb_first(np.ones((rows, cols), dtype=np.int64), 1)
+
+
+def test_bwd_all_ones_is_plain_inverse_transform():
+    # With every entry trusted the estimator is the straight-through one: dX = H G.
+    rng = np.random.default_rng(1000)
+    x = rng.standard_normal((4, 512))
+    y = qo.blockwise_hadamard(x, 128)
+    back = qo.trust_bwd(y, _ones_mask(4, 512), 128)
+    assert np.max(np.abs(back - x)) <= 1e-13
+
+
+def test_bwd_all_zeros_and_masked_impulse():
+    rng = np.random.default_rng(1001)
+    g = rng.standard_normal((3, 256))
+    zeros = qo.pack_lsb_first(np.zeros((3, 256), dtype=np.int64), 1)
+    assert np.all(qo.trust_bwd(g, zeros, 128) == 0.0)
+    # an impulse at a masked-out entry contributes nothing; at a trusted one it is a Hadamard column
+    m = np.ones((1, 256), dtype=np.int64)
+    m[0, 70] = 0
+    imp = np.zeros((1, 256))
+    imp[0, 70] = 1.0
+    assert np.all(qo.trust_bwd(imp, qo.pack_lsb_first(m, 1), 128) == 0.0)
+    imp2 = np.zeros((1, 256))
+    imp2[0, 130] = 1.0
+    out = qo.trust_bwd(imp2, qo.pack_lsb_first(m, 1), 128)
+    col = np.array([(-1.0) ** bin(i & 2).count("1") for i in range(128)]) / math.sqrt(128)
+    assert np.allclose(out[0, 128:], col, rtol=0, atol=1e-15)
+    assert np.all(out[0, :128] == 0.0)
+
+
+def test_bwd_linear_and_norm_preserving():
+    rng = np.random.default_rng(1002)
+    g1 = rng.standard_normal((4, 256))
+    g2 = rng.standard_normal((4, 256))
+    mbits = (rng.random((4, 256)) < 0.9).astype(np.int64)
+    mask = qo.pack_lsb_first(mbits, 1)
+    lhs = qo.trust_bwd(2.5 * g1 - 0.75 * g2, mask, 64)
+    rhs = 2.5 * qo.trust_bwd(g1, mask, 64) - 0.75 * qo.trust_bwd(g2, mask, 64)
+    assert np.max(np.abs(lhs - rhs)) <= 1e-13
+    out = qo.trust_bwd(g1, mask, 64)
+    masked = g1 * mbits
+    for r in range(4):
+        for k in range(4):
+            a = np.linalg.norm(out[r, 64 * k : 64 * (k + 1)])
+            c = np.linalg.norm(masked[r, 64 * k : 64 * (k + 1)])
+            assert abs(a - c) <= 1e-13 * max(c, 1e-300)
