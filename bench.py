@@ -1,0 +1,284 @@
+"""Throughput of the QuEST quantiser hot path on one MI355X.
+
+One step = the whole path over one batch: forward quantisation (Hadamard,
+RMS scale, codes, trust mask) of a 16384 x 2048 bf16 activation at b = 4,
+block 128, then the trust-masked inverse-Hadamard backward of a 16384 x 2048
+bf16 gradient with that step's mask.  Inputs are synthetic (seeded
+Student-t(4) activations with 20 outlier channels x20, N(0, 1e-3^2)
+gradients) and resident in HBM before timing starts.  Steps rotate over
+several buffer sets so that no step finds its data in the 256 MB last-level
+cache.
+
+Prints one JSON line: throughput in quantised elements/s, the roofline of
+the dominant kernel (algorithmic bytes per launch over its mean duration,
+timed with HIP events on the launch stream), and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantised elements/s and % HBM roofline for fused Hadamard-quantize fwd+bwd"
+HBM_PEAK_GBPS = 8000.0
+ROWS, COLS, BLOCK, BITS = 16384, 2048, 128, 4
+N_SETS = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_16384x2048.txt")
+KERNEL_SOURCES = ["quest_device.h", "quest_kernels.hip"]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain elementwise copy of known size (for counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantization_aware_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernels."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    key = f"{kernel_tag}_hbm_bytes_per_launch"
+    return float(vals[key]) if key in vals else None
+
+
+def alg_bytes_fwd(rows, cols, in_bytes, bits):
+    return rows * cols * in_bytes + rows * cols * bits // 8 + rows * cols // 8 + 4 * rows
+
+
+def alg_bytes_bwd(rows, cols, g_bytes):
+    return 2 * rows * cols * g_bytes + rows * cols // 8
+
+
+def cpu_baseline(x_dev, g_dev, target_seconds):
+    """Time the fp64 oracle (fwd then bwd) on a bounded row sample of the same tensors."""
+    import numpy as np
+
+    from oracle import quest_oracle as qo
+    from quest_inputs import to_float64
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    qo.fit_alpha(BITS)  # the fit is a one-off per bit width, outside the per-tensor work
+    rows = 64
+    elapsed = 0.0
+    done = 0
+    while True:
+        x64 = to_float64(x_dev[done : done + rows])
+        g64 = to_float64(g_dev[done : done + rows])
+        t0 = time.perf_counter()
+        ref = qo.quantize_fwd(x64, BLOCK, BITS)
+        qo.trust_bwd(g64, ref["mask"], BLOCK)
+        elapsed += time.perf_counter() - t0
+        done += rows
+        if elapsed >= target_seconds or done >= ROWS:
+            break
+        per_row = elapsed / done
+        rows = int(min(ROWS - done, max(64, (target_seconds - elapsed) / per_row)))
+    return {
+        "value": done * COLS / elapsed,
+        "unit": "elements/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"rows 0..{done - 1} of the 16384x2048 workload ({done * COLS} elements), fwd then bwd, "
+        f"{elapsed:.1f} s wall",
+        "cpu_count": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(
+            f"bench.py runs on one GPU: this path shards by rows with no communication, and only the "
+            f"single-GPU measurement is made here (asked for --gpus {args.gpus}).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import quantization_aware_amd as qa
+    from quest_inputs import WORKLOADS, make_tensor
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = qa.load_library()
+    dev = torch.device("cuda", 0)
+    wl = WORKLOADS["T"]
+    x0 = make_tensor(wl.fwd[0], dev)
+    g0 = make_tensor(wl.grad[0], dev)
+    xs = [x0] + [x0.clone() for _ in range(N_SETS - 1)]
+    gs = [g0] + [g0.clone() for _ in range(N_SETS - 1)]
+    codes = [torch.empty((ROWS, COLS * BITS // 8), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    scales = [torch.empty((ROWS,), dtype=torch.float32, device=dev) for _ in range(N_SETS)]
+    masks = [torch.empty((ROWS, COLS // 8), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    dxs = [torch.empty_like(g0) for _ in range(N_SETS)]
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    # The timed loop calls the C ABI directly with prepared arguments.
+    fwd_args = [
+        (ctypes.c_void_p(xs[i].data_ptr()), qa.QUEST_BF16, ROWS, COLS, BLOCK, BITS, ctypes.c_void_p(codes[i].data_ptr()),
+         ctypes.c_void_p(scales[i].data_ptr()), ctypes.c_void_p(masks[i].data_ptr()), sh)
+        for i in range(N_SETS)
+    ]
+    bwd_args = [
+        (ctypes.c_void_p(gs[i].data_ptr()), qa.QUEST_BF16, ctypes.c_void_p(masks[i].data_ptr()), ROWS, COLS, BLOCK,
+         ctypes.c_void_p(dxs[i].data_ptr()), sh)
+        for i in range(N_SETS)
+    ]
+    f_fwd, f_bwd = lib.quest_quantize_fwd, lib.quest_trust_bwd
+
+    def step(i):
+        s = i % N_SETS
+        st = f_fwd(*fwd_args[s])
+        if st:
+            raise qa.QuestError("quest_quantize_fwd", st, lib.quest_status_string(st).decode())
+        st = f_bwd(*bwd_args[s])
+        if st:
+            raise qa.QuestError("quest_trust_bwd", st, lib.quest_status_string(st).decode())
+
+    if args.copy_calibration:
+        src = torch.empty((256 << 20) // 2, dtype=torch.bfloat16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x elementwise neg of {src.numel() * 2} bytes", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; HIP events on the launch stream around every kernel.
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        s = i % N_SETS
+        f_fwd(*fwd_args[s])
+        ev[2 * i + 1].record(stream)
+        f_bwd(*bwd_args[s])
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    fwd_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)]
+    bwd_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)]
+    event_total_ms = ev[0].elapsed_time(ev[2 * K])
+
+    # The same K steps with no events in between, for the step time itself.
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t2 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    bare_ms = e0.elapsed_time(e1)
+    bare_wall = t3 - t2
+
+    ms_per_step = max(bare_ms, 1000.0 * bare_wall) / K
+    elements = ROWS * COLS
+    value = elements / (ms_per_step / 1000.0)
+
+    fwd_avg = sum(fwd_ms) / K
+    bwd_avg = sum(bwd_ms) / K
+    fwd_bytes = alg_bytes_fwd(ROWS, COLS, 2, BITS)
+    bwd_bytes = alg_bytes_bwd(ROWS, COLS, 2)
+    kernels = {
+        "quest_fwd_kernel": {"avg_us": 1000 * fwd_avg, "alg_bytes": fwd_bytes,
+                             "gbps": fwd_bytes / (fwd_avg * 1e6)},
+        "quest_bwd_kernel": {"avg_us": 1000 * bwd_avg, "alg_bytes": bwd_bytes,
+                             "gbps": bwd_bytes / (bwd_avg * 1e6)},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dom = kernels[dom_name]
+    traffic = read_traffic("fwd" if dom_name == "quest_fwd_kernel" else "bwd")
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(dom["gbps"], 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(dom["gbps"] / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": dom_name,
+    }
+    step_bytes = fwd_bytes + bwd_bytes
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "16384x2048 bf16 activation (Student-t(4), 20 channels x20) quantised at b=4, block 128, "
+            "then trust-masked backward of a 16384x2048 bf16 gradient",
+            "rows": ROWS,
+            "cols": COLS,
+            "block": BLOCK,
+            "bits": BITS,
+            "input_dtype": "bf16",
+            "buffer_sets": N_SETS,
+        },
+        "roofline": roofline,
+        "step_hbm_gbps": step_bytes / (ms_per_step * 1e6),
+        "step_roofline_frac": step_bytes / (ms_per_step * 1e6) / HBM_PEAK_GBPS,
+        "kernels": kernels,
+        "timing": {
+            "events_total_ms": event_total_ms,
+            "events_wall_s": wall,
+            "bare_events_ms": bare_ms,
+            "bare_wall_s": bare_wall,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x0, g0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * libquest - the QuEST quantiser hot path on AMD Instinct MI355X (gfx950).
+ *
+ * QuEST (arXiv 2502.05003) quantises weights and activations for
+ * quantisation-aware training.  Forward: each row is cut into blocks of n
+ * entries, every block is multiplied by the orthonormal Hadamard matrix, the
+ * row is RMS-normalised and projected onto a b-bit symmetric uniform grid
+ * whose clip scale alpha_b * RMS minimises the expected squared error for a
+ * standard Gaussian; entries whose quantisation error is at most half a grid
+ * step are marked as trusted.  Backward: the Hadamard-domain gradient is
+ * multiplied by that trust mask and transformed back.
+ * Sources: the QuEST abstract (codewithpapers.app record of arXiv
+ * 2502.05003: Hadamard normalisation, MSE-optimal fitting, trust gradient
+ * estimator); atlas.scime.ai summary of QuEST, "Approach"; pith.science
+ * review of QuEST, "What carries the argument", "Assumptions & free
+ * parameters" and the Figure 2 caption.
+ *
+ * Conventions shared by every call
+ *   - Tensors are row-major and contiguous: element (r, c) of a rows x cols
+ *     tensor is at index r * cols + c.
+ *   - Every buffer is allocated, owned and freed by the caller.  Device
+ *     buffers are HIP device memory on the current device; the library never
+ *     allocates, frees or synchronises.
+ *   - Device calls enqueue their kernels on `stream` (a hipStream_t; NULL is
+ *     the null stream) and return without waiting.  A status other than
+ *     QUEST_EHIP means nothing was enqueued.
+ *   - Arguments are checked before anything is launched.  On any error the
+ *     call writes nothing and returns a status code; no C++ exception crosses
+ *     this interface.
+ *   - rows == 0 is a valid empty call: it returns QUEST_OK, touches no
+ *     buffer and may be given NULL pointers.
+ *   - Calls are thread-safe.  The only global state is the table of clip
+ *     scales alpha_b, filled once on first use.
+ *   - Inputs must be finite, and every row's RMS must lie in [2^-60, 2^50]
+ *     (about 8.7e-19 to 1.1e15) or the row must be exactly zero: the sum of
+ *     squares is accumulated in fp32 and must neither overflow nor underflow.
+ *
+ * Data layouts
+ *   codes : per row, an LSB-first stream of b-bit unsigned codes: element c
+ *           occupies bits [c*b, (c+1)*b) of the row's cols*b/8 bytes, and
+ *           bit i of byte j is stream bit 8j+i (at b=4 element 2i is the low
+ *           nibble of byte i).  Codes are offset binary u in [0, 2^b - 1];
+ *           the grid value of code u is (2u - L + 1) * s / (L - 1), L = 2^b.
+ *           XOR with 2^(b-1) gives the two's-complement form.
+ *   mask  : per row, an LSB-first stream of cols bits; 1 = trusted (the
+ *           gradient passes), 0 = masked.
+ *   scale : one fp32 per row, the clip scale s_r = alpha_b * RMS_r (the
+ *           outermost grid level), not the RMS and not the step.
+ */
+#ifndef QUEST_H
+#define QUEST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QUEST_OK = 0,
+  QUEST_EINVAL = 1,       /* bad pointer, size, dtype or forbidden aliasing */
+  QUEST_EUNSUPPORTED = 2, /* block, bit width or row width outside what is built */
+  QUEST_EALIGN = 3,       /* a buffer is not 16-byte aligned */
+  QUEST_EHIP = 4          /* the HIP runtime reported an error at launch */
+} quest_status;
+
+typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1 } quest_dtype;
+
+/* Largest row width handled in one pass (a row is reduced by one workgroup). */
+#define QUEST_MAX_COLS 32768
+
+/*
+ * Clip scale alpha_b of the b-bit grid: the alpha minimising
+ * E[(Q_{alpha,b}(X) - X)^2] for X ~ N(0, 1), where Q_{alpha,b} rounds to the
+ * nearest of the L = 2^b levels (2k - L + 1) alpha / (L - 1), k = 0..L-1.
+ * pith.science review of QuEST, "What carries the argument" (the grid scale
+ * minimises the L2 error against a standard Gaussian) and "Assumptions &
+ * free parameters" (alpha* is derived from a fixed N(0,1) target).
+ * Host only, float64; computed once per b and cached.  b in [1, 8];
+ * returns NaN for any other b.  alpha_1 = sqrt(2/pi).
+ */
+double quest_fit_alpha(int b);
+
+/*
+ * Forward QuEST quantisation of x (rows x cols):
+ *   y     = blockwise Hadamard transform of each row, blocks of `block`
+ *           entries, orthonormal Sylvester matrix (natural order);
+ *   s_r   = alpha_b * sqrt(mean_c y[r,c]^2),  Delta_r = 2 s_r / (2^b - 1);
+ *   u     = clamp(floor(y / Delta_r) + 2^(b-1), 0, 2^b - 1);
+ *   mask  = [ |grid(u) - y| <= Delta_r / 2 ]  (equivalently |y| <= s_r L/(L-1)).
+ * A row of zeros gives s_r = 0, u = 2^(b-1) everywhere and an all-ones mask.
+ * atlas.scime.ai summary of QuEST, "Approach"; pith.science review of
+ * QuEST, "What carries the argument" and the Figure 7 caption (mask M_alpha*).
+ *
+ *   x       device, rows*cols elements of x_dtype (QUEST_F32 or QUEST_BF16)
+ *   rows    >= 0
+ *   cols    > 0, a multiple of `block`, at most QUEST_MAX_COLS
+ *   block   Hadamard block size: 64, 128 or 256
+ *   b       bits per code: 1, 2, 3 or 4
+ *   codes   device output, quest_codes_bytes(rows, cols, b) bytes
+ *   scale   device output, rows floats (s_r)
+ *   mask    device output, quest_mask_bytes(rows, cols) bytes
+ * Pointers must be 16-byte aligned.  No output may overlap x or another
+ * output (QUEST_EINVAL).  The transform and the reduction run in fp32; an
+ * entry within about 1e-6 * s_r of a decision or trust threshold may round
+ * to the neighbouring outcome of the exact (fp64) definition.
+ */
+quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                int b, uint8_t* codes, float* scale, uint8_t* mask, void* stream);
+
+/*
+ * Dequantise codes to their grid values, in the Hadamard domain:
+ *   out[r, c] = (2 u[r, c] - L + 1) * s_r / (L - 1),  L = 2^b,
+ * rounded to out_dtype (bf16: round to nearest even).  The Hadamard domain
+ * is where the quantised operands of a product live, since the orthogonal
+ * transform is applied to both operands (pith.science review of QuEST,
+ * "Assumptions & free parameters"); the official repository names the same
+ * step `dequantize_dense` (codewithpapers.app record).
+ *   codes   device, quest_codes_bytes(rows, cols, b) bytes (layout above)
+ *   scale   device, rows floats
+ *   rows    >= 0;  cols > 0, a multiple of 64, at most QUEST_MAX_COLS
+ *   b       1, 2, 3 or 4
+ *   out     device output, rows*cols elements of out_dtype; must not
+ *           overlap codes or scale (QUEST_EINVAL)
+ */
+quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b,
+                              void* out, quest_dtype out_dtype, void* stream);
+
+/*
+ * Trust-gradient backward:  grad_out[r, block k] = H_n (M * G)[r, block k],
+ * H_n the orthonormal Hadamard matrix (its own inverse), M the stored mask.
+ * The scale is treated as a constant (no gradient through the RMS).
+ * pith.science review of QuEST, "What carries the argument" (the gradient in
+ * the Hadamard domain is multiplied by the binary mask) and the Figure 2
+ * caption (inverse Hadamard transforms on the backward pass).
+ *   grad     device, rows*cols elements of g_dtype: the gradient with respect
+ *            to the Hadamard-domain (quantised) tensor
+ *   mask     device, quest_mask_bytes(rows, cols) bytes from quest_quantize_fwd
+ *   rows     >= 0;  cols > 0, a multiple of `block`, at most QUEST_MAX_COLS
+ *   block    64, 128 or 256 (the block used in the forward pass)
+ *   grad_out device output, rows*cols elements of g_dtype (bf16 rounded to
+ *            nearest even).  grad_out == grad runs in place; any other
+ *            overlap with grad, or any overlap with mask, is QUEST_EINVAL.
+ */
+quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_t* mask, int64_t rows, int64_t cols,
+                             int block, void* grad_out, void* stream);
+
+/* Bytes of the packed codes: rows * cols * b / 8 (0 on invalid sizes). */
+size_t quest_codes_bytes(int64_t rows, int64_t cols, int b);
+
+/* Bytes of the packed mask: rows * cols / 8 (0 on invalid sizes). */
+size_t quest_mask_bytes(int64_t rows, int64_t cols);
+
+/* Static English name of a status code ("unknown status" otherwise). */
+const char* quest_status_string(quest_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUEST_H */

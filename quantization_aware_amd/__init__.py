@@ -1,0 +1,205 @@
+"""Python binding of libquest (the QuEST quantiser hot path on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libquest.so, reached through its C ABI (include/quest.h).  torch
+supplies device memory and the stream; the functions here check tensors,
+allocate outputs when none are given and pass raw pointers.  If libquest.so
+is missing the calls raise: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QuestError",
+    "LIB_PATH",
+    "load_library",
+    "fit_alpha",
+    "codes_bytes",
+    "mask_bytes",
+    "quantize_fwd",
+    "dequantize",
+    "trust_bwd",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquest.so")
+
+QUEST_OK, QUEST_EINVAL, QUEST_EUNSUPPORTED, QUEST_EALIGN, QUEST_EHIP = range(5)
+QUEST_F32, QUEST_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "quest_fit_alpha",
+    "quest_quantize_fwd",
+    "quest_dequantize",
+    "quest_trust_bwd",
+    "quest_codes_bytes",
+    "quest_mask_bytes",
+    "quest_status_string",
+)
+
+
+class QuestError(RuntimeError):
+    """A libquest call returned a status other than QUEST_OK."""
+
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call}: {message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libquest.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libquest.so not found at {path}; build it with `python -m quantization_aware_amd.build` "
+            "(there is no CPU fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.quest_fit_alpha.argtypes = [c_int]
+    lib.quest_fit_alpha.restype = ctypes.c_double
+    lib.quest_quantize_fwd.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp]
+    lib.quest_quantize_fwd.restype = c_int
+    lib.quest_dequantize.argtypes = [vp, vp, i64, i64, c_int, vp, c_int, vp]
+    lib.quest_dequantize.restype = c_int
+    lib.quest_trust_bwd.argtypes = [vp, c_int, vp, i64, i64, c_int, vp, vp]
+    lib.quest_trust_bwd.restype = c_int
+    lib.quest_codes_bytes.argtypes = [i64, i64, c_int]
+    lib.quest_codes_bytes.restype = ctypes.c_size_t
+    lib.quest_mask_bytes.argtypes = [i64, i64]
+    lib.quest_mask_bytes.restype = ctypes.c_size_t
+    lib.quest_status_string.argtypes = [c_int]
+    lib.quest_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(call: str, status: int) -> None:
+    if status != QUEST_OK:
+        msg = load_library().quest_status_string(status).decode()
+        raise QuestError(call, status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return QUEST_BF16
+    if t.dtype == torch.float32:
+        return QUEST_F32
+    raise TypeError(f"libquest takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _device_tensor(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def fit_alpha(b: int) -> float:
+    """Clip scale alpha_b of the b-bit Gaussian-MSE-optimal grid (host, float64)."""
+    return float(load_library().quest_fit_alpha(int(b)))
+
+
+def codes_bytes(rows: int, cols: int, b: int) -> int:
+    return int(load_library().quest_codes_bytes(int(rows), int(cols), int(b)))
+
+
+def mask_bytes(rows: int, cols: int) -> int:
+    return int(load_library().quest_mask_bytes(int(rows), int(cols)))
+
+
+def quantize_fwd(x: torch.Tensor, block: int, b: int, codes=None, scale=None, mask=None, stream=None):
+    """Forward QuEST quantisation of a 2-D tensor; returns (codes, scale, mask).
+
+    codes: uint8 (rows, cols*b/8); scale: float32 (rows,); mask: uint8 (rows, cols/8).
+    Outputs are allocated on x's device unless given.
+    """
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if mask is None:
+        mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
+    for name, t, dt in (("codes", codes, torch.uint8), ("scale", scale, torch.float32), ("mask", mask, torch.uint8)):
+        _device_tensor(name, t)
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}")
+    if codes.numel() < codes_bytes(rows, cols, b) or scale.numel() < rows or mask.numel() < mask_bytes(rows, cols):
+        raise ValueError("output buffer too small")
+    st = lib.quest_quantize_fwd(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b),
+        codes.data_ptr(), scale.data_ptr(), mask.data_ptr(), _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd", st)
+    return codes, scale, mask
+
+
+def dequantize(codes: torch.Tensor, scale: torch.Tensor, rows: int, cols: int, b: int,
+               out_dtype=torch.bfloat16, out=None, stream=None) -> torch.Tensor:
+    """Grid values (2u - L + 1) s / (L - 1) of packed codes, in the Hadamard domain."""
+    lib = load_library()
+    _device_tensor("codes", codes)
+    _device_tensor("scale", scale)
+    if codes.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise TypeError("codes must be uint8 and scale float32")
+    if codes.numel() < codes_bytes(rows, cols, b) or scale.numel() < rows:
+        raise ValueError("codes or scale smaller than rows x cols needs")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    _device_tensor("out", out)
+    if out.numel() < rows * cols:
+        raise ValueError("out smaller than rows x cols")
+    st = lib.quest_dequantize(
+        codes.data_ptr(), scale.data_ptr(), int(rows), int(cols), int(b),
+        out.data_ptr(), _dtype_code(out), _stream_handle(codes.device, stream),
+    )
+    _check("quest_dequantize", st)
+    return out
+
+
+def trust_bwd(grad: torch.Tensor, mask: torch.Tensor, block: int, out=None, stream=None) -> torch.Tensor:
+    """Trust-gradient backward H (M * G) per block; out may be grad itself (in place)."""
+    lib = load_library()
+    _device_tensor("grad", grad)
+    _device_tensor("mask", mask)
+    if grad.dim() != 2:
+        raise ValueError("grad must be 2-D (rows x cols)")
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8")
+    rows, cols = grad.shape
+    if mask.numel() < mask_bytes(rows, cols):
+        raise ValueError("mask smaller than rows x cols / 8 bytes")
+    if out is None:
+        out = torch.empty_like(grad)
+    _device_tensor("out", out)
+    if out.dtype != grad.dtype or out.shape != grad.shape:
+        raise ValueError("out must match grad in dtype and shape")
+    st = lib.quest_trust_bwd(
+        grad.data_ptr(), _dtype_code(grad), mask.data_ptr(), rows, cols, int(block),
+        out.data_ptr(), _stream_handle(grad.device, stream),
+    )
+    _check("quest_trust_bwd", st)
+    return out

@@ -1,0 +1,202 @@
+// C ABI of libquest: argument checks, the clip-scale table and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+#include <mutex>
+
+#include "../../include/quest.h"
+#include "quest_launch.h"
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// alpha_b: the clip scale of the b-bit grid that minimises the expected
+// squared error for a standard Gaussian (pith.science review of QuEST, "What
+// carries the argument" and "Assumptions & free parameters").
+//
+// With levels c_k alpha, c_k = (2k - L + 1)/(L - 1), and cells bounded by the
+// midpoints of neighbouring levels, let
+//   F(alpha) = sum_k c_k E[X; cell k] / sum_k c_k^2 P(cell k),
+// E[X; [a, c)] = phi(a) - phi(c),  P([a, c)) = Phi(c) - Phi(a): the
+// least-squares alpha for the cells that alpha itself defines.  The error's
+// derivative is dMSE/d alpha = -2 (sum_k c_k^2 P_k) (F(alpha) - alpha), so
+// F(alpha) - alpha is positive below the optimum and negative above it.
+// Bisection on that sign over [0.01, 32] pins alpha_b to the last bit.
+// ----------------------------------------------------------------------------
+double gauss_pdf(double t) {
+  if (std::isinf(t)) return 0.0;
+  return std::exp(-0.5 * t * t) * 0.39894228040143267793994605993438;
+}
+
+double gauss_cdf(double t) {
+  if (t == std::numeric_limits<double>::infinity()) return 1.0;
+  if (t == -std::numeric_limits<double>::infinity()) return 0.0;
+  return 0.5 * std::erfc(-t * 0.70710678118654752440084436210485);
+}
+
+double alpha_update(double alpha, int b) {
+  const int levels = 1 << b;
+  double num = 0.0, den = 0.0;
+  for (int k = 0; k < levels; ++k) {
+    const double ck = double(2 * k - levels + 1) / double(levels - 1);
+    const double lo = (k == 0) ? -std::numeric_limits<double>::infinity()
+                               : double(2 * k - levels) * alpha / double(levels - 1);
+    const double hi = (k == levels - 1) ? std::numeric_limits<double>::infinity()
+                                        : double(2 * k + 2 - levels) * alpha / double(levels - 1);
+    num += ck * (gauss_pdf(lo) - gauss_pdf(hi));
+    den += ck * ck * (gauss_cdf(hi) - gauss_cdf(lo));
+  }
+  return num / den;
+}
+
+double solve_alpha(int b) {
+  double lo = 0.01, hi = 32.0;
+  for (int it = 0; it < 400; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (alpha_update(mid, b) > mid)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+constexpr int kMaxBits = 8;
+double g_alpha[kMaxBits + 1];
+std::once_flag g_alpha_once;
+
+void fill_alpha_table() {
+  for (int b = 1; b <= kMaxBits; ++b) g_alpha[b] = solve_alpha(b);
+}
+
+// ----------------------------------------------------------------------------
+// Argument checks.
+// ----------------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int log2_block(int block) {
+  switch (block) {
+    case 64: return 6;
+    case 128: return 7;
+    case 256: return 8;
+    default: return -1;
+  }
+}
+
+size_t dtype_size(quest_dtype d) { return d == QUEST_BF16 ? 2 : 4; }
+
+bool dtype_ok(quest_dtype d) { return d == QUEST_F32 || d == QUEST_BF16; }
+
+// rows * cols must stay below 2^36 so that the number of 32-element runs fits
+// in 31 bits.
+constexpr int64_t kMaxElements = int64_t(1) << 36;
+
+quest_status check_shape(int64_t rows, int64_t cols, int multiple_of) {
+  if (rows < 0 || cols <= 0 || cols % multiple_of != 0) return QUEST_EINVAL;
+  if (cols > QUEST_MAX_COLS) return QUEST_EUNSUPPORTED;
+  if (rows > kMaxElements / cols) return QUEST_EUNSUPPORTED;
+  return QUEST_OK;
+}
+
+quest_status from_hip(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+double quest_fit_alpha(int b) {
+  if (b < 1 || b > kMaxBits) return std::numeric_limits<double>::quiet_NaN();
+  std::call_once(g_alpha_once, fill_alpha_table);
+  return g_alpha[b];
+}
+
+size_t quest_codes_bytes(int64_t rows, int64_t cols, int b) {
+  if (rows < 0 || cols <= 0 || b < 1 || b > kMaxBits || (cols * b) % 8 != 0) return 0;
+  if (rows > kMaxElements / cols) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(cols * b / 8);
+}
+
+size_t quest_mask_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return 0;
+  if (rows > kMaxElements / cols) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(cols / 8);
+}
+
+const char* quest_status_string(quest_status s) {
+  switch (s) {
+    case QUEST_OK: return "ok";
+    case QUEST_EINVAL: return "invalid argument";
+    case QUEST_EUNSUPPORTED: return "unsupported block, bit width or size";
+    case QUEST_EALIGN: return "buffer not 16-byte aligned";
+    case QUEST_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                uint8_t* codes, float* scale, uint8_t* mask, void* stream) {
+  const int lb = log2_block(block);
+  if (lb < 0 || b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(x_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, block);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!x || !codes || !scale || !mask) return QUEST_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(mask)) return QUEST_EALIGN;
+  const size_t nx = static_cast<size_t>(rows * cols) * dtype_size(x_dtype);
+  const size_t nc = quest_codes_bytes(rows, cols, b);
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t nm = quest_mask_bytes(rows, cols);
+  if (overlaps(x, nx, codes, nc) || overlaps(x, nx, scale, ns) || overlaps(x, nx, mask, nm) ||
+      overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm))
+    return QUEST_EINVAL;
+  const float alpha = static_cast<float>(quest_fit_alpha(b));
+  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, codes, scale, mask,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,
+                              quest_dtype out_dtype, void* stream) {
+  if (b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(out_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, 64);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!codes || !scale || !out) return QUEST_EINVAL;
+  if (!aligned16(codes) || !aligned16(scale) || !aligned16(out)) return QUEST_EALIGN;
+  const size_t nc = quest_codes_bytes(rows, cols, b);
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t no = static_cast<size_t>(rows * cols) * dtype_size(out_dtype);
+  if (overlaps(out, no, codes, nc) || overlaps(out, no, scale, ns)) return QUEST_EINVAL;
+  return from_hip(quest::launch_dequantize(codes, scale, rows, cols, b, out, out_dtype == QUEST_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_t* mask, int64_t rows, int64_t cols,
+                             int block, void* grad_out, void* stream) {
+  const int lb = log2_block(block);
+  if (lb < 0) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(g_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, block);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!grad || !mask || !grad_out) return QUEST_EINVAL;
+  if (!aligned16(grad) || !aligned16(mask) || !aligned16(grad_out)) return QUEST_EALIGN;
+  const size_t ng = static_cast<size_t>(rows * cols) * dtype_size(g_dtype);
+  const size_t nm = quest_mask_bytes(rows, cols);
+  if (grad_out != grad && overlaps(grad, ng, grad_out, ng)) return QUEST_EINVAL;
+  if (overlaps(grad_out, ng, mask, nm) || overlaps(grad, ng, mask, nm)) return QUEST_EINVAL;
+  return from_hip(quest::launch_trust_bwd(grad, g_dtype == QUEST_BF16, mask, rows, cols, lb, grad_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,19 @@
+// Internal launch entry points of libquest (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace quest {
+
+// x_is_bf16: 1 = bf16 input, 0 = fp32.  All sizes already validated.
+hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
+                               float alpha, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
+                             void* out, int out_is_bf16, hipStream_t stream);
+
+hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
+                            int log_block, void* grad_out, hipStream_t stream);
+
+}  // namespace quest

@@ -1,0 +1,355 @@
+"""Parity of libquest's HIP kernels with the fp64 CPU oracle, through the C ABI.
+
+Every GPU input comes from the seeded generators in quest_inputs; the oracle
+receives the same bits widened to float64.  Small workloads are compared in
+full; the full-size workloads run on the GPU in the launch configuration the
+benchmark times, and a seeded sample of rows (always including the first and
+the last) is recomputed by the oracle, which is exact because every row is
+independent.  The backward pass is always fed the oracle's own mask on the
+rows it checks, so the comparison has no boundary exemptions.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import quantization_aware_amd as qa
+from oracle import quest_oracle as qo
+from parity import TOL_BF16, TOL_F32, check_fwd, check_grad, check_values, exempt_entries
+from quest_inputs import WORKLOADS, TensorSpec, make_tensor, to_float64
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg: str) -> None:
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qa.load_library()
+    return torch.device("cuda", 0)
+
+
+def sample_rows(rows: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(rows, size=min(k, rows), replace=False)
+    return np.unique(np.concatenate([pick, [0, rows - 1]]))
+
+
+def fwd_gpu(x: torch.Tensor, block: int, b: int):
+    codes, scale, mask = qa.quantize_fwd(x, block, b)
+    torch.cuda.synchronize()
+    return codes, scale, mask
+
+
+def np_rows(t: torch.Tensor, rows) -> np.ndarray:
+    idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    return t.index_select(0, idx).cpu().numpy()
+
+
+def oracle_mask_tensor(ref, device) -> torch.Tensor:
+    return torch.from_numpy(ref["mask"]).to(device)
+
+
+# ---------------------------------------------------------------------------
+# Small workload, compared in full: 256 x 512 fp32, 4 outlier columns x10.
+# ---------------------------------------------------------------------------
+
+def test_c1_fwd_full(dev):
+    wl = WORKLOADS["C1"]
+    spec = wl.fwd[0]
+    log(f"C1 fwd {spec.rows}x{spec.cols} fp32 block {wl.block} b=4")
+    x = make_tensor(spec, dev)
+    codes, scale, mask = fwd_gpu(x, wl.block, 4)
+    st = check_fwd(to_float64(x), wl.block, 4, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy())
+    log(f"C1 fwd ok {st}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_c1_dequantize(dev, out_dtype):
+    wl = WORKLOADS["C1"]
+    spec = wl.fwd[0]
+    x = make_tensor(spec, dev)
+    x64 = to_float64(x)
+    ref = qo.quantize_fwd(x64, wl.block, 4)
+    # The dequantiser alone, on the oracle's codes and scale (scale rounded to fp32).
+    s32 = ref["scale"].astype(np.float32)
+    codes_t = torch.from_numpy(ref["codes"]).to(dev)
+    scale_t = torch.from_numpy(s32).to(dev)
+    log(f"C1 dequantize oracle codes -> {out_dtype}")
+    out = qa.dequantize(codes_t, scale_t, spec.rows, spec.cols, 4, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    expect = qo.dequantize(ref["codes"], s32.astype(np.float64), spec.cols, 4)
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_BF16
+    check_values(out.float().cpu().numpy(), expect, tol)
+    # End to end: GPU forward then GPU dequantise against the oracle's grid values.
+    codes, scale, mask = fwd_gpu(x, wl.block, 4)
+    out2 = qa.dequantize(codes, scale, spec.rows, spec.cols, 4, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ex = exempt_entries(ref["y"], ref["scale"], 4)
+    check_values(out2.float().cpu().numpy(), ref["q"], tol, skip=ex)
+
+
+@pytest.mark.parametrize("g_dtype", [torch.float32, torch.bfloat16])
+def test_c1_trust_bwd(dev, g_dtype):
+    wl = WORKLOADS["C1"]
+    spec = wl.fwd[0]
+    x = make_tensor(spec, dev)
+    ref = qo.quantize_fwd(to_float64(x), wl.block, 4)
+    gspec = TensorSpec("C1.grad", spec.rows, spec.cols, "f32" if g_dtype == torch.float32 else "bf16", "normal", 1.0, 11)
+    g = make_tensor(gspec, dev)
+    log(f"C1 trust_bwd {g_dtype}")
+    out = qa.trust_bwd(g, oracle_mask_tensor(ref, dev), wl.block)
+    torch.cuda.synchronize()
+    expect = qo.trust_bwd(to_float64(g), ref["mask"], wl.block)
+    tol = TOL_F32 if g_dtype == torch.float32 else TOL_BF16
+    ratio = check_grad(out.float().cpu().numpy(), expect, wl.block, tol)
+    log(f"C1 trust_bwd ok, max error / tolerance = {ratio:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# Activations 16384 x 512 bf16 Student-t(4), every bit width, in full.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_c2_fwd_full(dev, b):
+    wl = WORKLOADS["C2"]
+    spec = wl.fwd[0]
+    log(f"C2 fwd {spec.rows}x{spec.cols} bf16 b={b}")
+    x = make_tensor(spec, dev)
+    codes, scale, mask = fwd_gpu(x, wl.block, b)
+    st = check_fwd(to_float64(x), wl.block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy())
+    log(f"C2 b={b} ok {st}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled rows.
+# ---------------------------------------------------------------------------
+
+def _fwd_bwd_sampled(dev, wl, act_spec, grad_spec, b, n_rows, seed):
+    block = wl.block
+    log(f"{wl.name} fwd {act_spec.rows}x{act_spec.cols} b={b} (full size)")
+    x = make_tensor(act_spec, dev)
+    codes, scale, mask = fwd_gpu(x, block, b)
+    rows = sample_rows(act_spec.rows, n_rows, seed)
+    x64 = np_rows(x, rows).astype(np.float64) if x.dtype == torch.float32 else to_float64(
+        x.index_select(0, torch.as_tensor(rows, device=dev))
+    )
+    ref = qo.quantize_fwd(x64, block, b)
+    st = check_fwd(x64, block, b, np_rows(codes, rows), np_rows(scale, rows), np_rows(mask, rows), ref=ref)
+    log(f"{wl.name} fwd sampled {len(rows)} rows ok {st}")
+    if grad_spec is None:
+        return
+    del x, codes, scale
+    g = make_tensor(grad_spec, dev)
+    # Oracle mask on the sampled rows, the GPU's own elsewhere (those rows are not compared).
+    mask[torch.as_tensor(rows, device=dev)] = torch.from_numpy(ref["mask"]).to(dev)
+    log(f"{wl.name} trust_bwd {grad_spec.rows}x{grad_spec.cols} (full size)")
+    out = qa.trust_bwd(g, mask, block)
+    torch.cuda.synchronize()
+    g64 = to_float64(g.index_select(0, torch.as_tensor(rows, device=dev)))
+    expect = qo.trust_bwd(g64, ref["mask"], block)
+    tol = TOL_BF16 if g.dtype == torch.bfloat16 else TOL_F32
+    ratio = check_grad(np_rows(out, rows).astype(np.float64) if out.dtype == torch.float32
+                       else to_float64(out.index_select(0, torch.as_tensor(rows, device=dev))), expect, block, tol)
+    log(f"{wl.name} trust_bwd sampled ok, max error / tolerance = {ratio:.3g}")
+
+
+def test_headline_16384x2048_fwd_bwd(dev):
+    wl = WORKLOADS["T"]
+    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 4, 384, 606)
+
+
+def test_c3_weights_fwd(dev):
+    wl = WORKLOADS["C3"]
+    for i, spec in enumerate(wl.fwd):
+        _fwd_bwd_sampled(dev, wl, spec, None, 4, 96, 300 + i)
+
+
+def test_c4_trust_bwd(dev):
+    wl = WORKLOADS["C4"]
+    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 4, 128, 404)
+
+
+def test_c5_fwd_bwd(dev):
+    wl = WORKLOADS["C5"]
+    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 1, 48, 505)
+
+
+# ---------------------------------------------------------------------------
+# Shapes and launch paths: ragged row counts, rows spanning several
+# wavefronts, every block size, the widest rows, tiny rows.
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # rows, cols, block, dtype
+    (1, 64, 64, "bf16"),
+    (7, 128, 128, "f32"),
+    (1000, 640, 64, "bf16"),  # 20 runs per row: rows straddle wavefronts
+    (33, 384, 128, "f32"),  # 12 runs per row
+    (129, 1024, 256, "bf16"),
+    (17, 5632, 128, "bf16"),  # 176 runs per row, 11 wavefronts per 4 rows
+    (3, 32768, 256, "bf16"),  # the widest row, 1024 lanes
+    (5, 32768, 64, "f32"),
+    (257, 2048, 64, "bf16"),
+    (70, 2048, 256, "f32"),
+    (300, 768, 256, "bf16"),  # 24 runs per row
+]
+
+
+@pytest.mark.parametrize("rows,cols,block,dt", SHAPES)
+@pytest.mark.parametrize("b", [1, 3, 4])
+def test_shapes_fwd(dev, rows, cols, block, dt, b):
+    spec = TensorSpec(f"shape{rows}x{cols}", rows, cols, dt, "student_t", 4, 7000 + rows + cols + block,
+                      outlier_cols=max(1, cols // 100), outlier_scale=20.0)
+    log(f"shape fwd {rows}x{cols} block {block} {dt} b={b}")
+    x = make_tensor(spec, dev)
+    codes, scale, mask = fwd_gpu(x, block, b)
+    check_fwd(to_float64(x), block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy())
+
+
+@pytest.mark.parametrize("rows,cols,block,dt", SHAPES)
+def test_shapes_bwd(dev, rows, cols, block, dt):
+    rng = np.random.default_rng(rows * 31 + cols)
+    mbits = (rng.random((rows, cols)) < 0.9).astype(np.int64)
+    mask_np = qo.pack_lsb_first(mbits, 1)
+    gspec = TensorSpec("g", rows, cols, dt, "normal", 1e-3, 9000 + rows + cols)
+    g = make_tensor(gspec, dev)
+    log(f"shape bwd {rows}x{cols} block {block} {dt}")
+    out = qa.trust_bwd(g, torch.from_numpy(mask_np).to(dev), block)
+    torch.cuda.synchronize()
+    expect = qo.trust_bwd(to_float64(g), mask_np, block)
+    check_grad(out.float().cpu().numpy(), expect, block, TOL_F32 if dt == "f32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("cols", [64, 640, 5632])
+def test_shapes_dequantize(dev, b, cols):
+    rows = 37
+    rng = np.random.default_rng(b * 100 + cols)
+    u = rng.integers(0, 1 << b, size=(rows, cols))
+    s = (rng.random(rows) * 3).astype(np.float32)
+    s[3] = 0.0
+    codes = qo.pack_lsb_first(u, b)
+    log(f"dequantize {rows}x{cols} b={b}")
+    for dt, tol in ((torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)):
+        out = qa.dequantize(torch.from_numpy(codes).to(dev), torch.from_numpy(s).to(dev), rows, cols, b, out_dtype=dt)
+        torch.cuda.synchronize()
+        expect = qo.dequantize(codes, s.astype(np.float64), cols, b)
+        check_values(out.float().cpu().numpy(), expect, tol)
+
+
+# ---------------------------------------------------------------------------
+# Degenerate rows and edge cases.
+# ---------------------------------------------------------------------------
+
+def test_degenerate_rows(dev):
+    rows, cols = 8, 512
+    x = np.zeros((rows, cols), dtype=np.float32)
+    x[1] = 3.25  # constant row: all energy in the first entry of each block
+    x[2, 77] = -5.0  # single nonzero
+    x[3] = np.linspace(-1e-3, 1e-3, cols, dtype=np.float32)
+    x[4, ::2] = 1e15  # near the top of the supported RMS range
+    x[4, 1::2] = -1e15
+    x[5] = np.float32(1e-15)  # near the bottom
+    x[6, :128] = 1.0  # one loud block, three silent ones
+    x[7] = np.arange(cols, dtype=np.float32) % 7 - 3
+    for b in (1, 2, 3, 4):
+        for block in (64, 128, 256):
+            log(f"degenerate rows b={b} block={block}")
+            xt = torch.from_numpy(x).to(dev)
+            codes, scale, mask = fwd_gpu(xt, block, b)
+            # Many of these entries sit exactly on a threshold (exact zeros are the b = 1 decision
+            # threshold), where fp32 rounding legitimately picks either side: only entries outside
+            # the band must agree.
+            check_fwd(x.astype(np.float64), block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(),
+                      max_fraction=None)
+            codes16, scale16, mask16 = fwd_gpu(xt.to(torch.bfloat16), block, b)
+            check_fwd(to_float64(xt.to(torch.bfloat16)), block, b, codes16.cpu().numpy(), scale16.cpu().numpy(),
+                      mask16.cpu().numpy(), max_fraction=None)
+
+
+def test_empty_rows(dev):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    codes, scale, mask = qa.quantize_fwd(x, 128, 4)
+    assert codes.shape == (0, 128) and scale.shape == (0,) and mask.shape == (0, 32)
+    out = qa.trust_bwd(x, mask, 128)
+    assert out.shape == (0, 256)
+    deq = qa.dequantize(codes, scale, 0, 256, 4)
+    assert deq.shape == (0, 256)
+
+
+def test_inplace_bwd(dev):
+    spec = TensorSpec("g", 64, 2048, "bf16", "normal", 1e-3, 4242)
+    g = make_tensor(spec, dev)
+    rng = np.random.default_rng(4243)
+    mask_np = qo.pack_lsb_first((rng.random((64, 2048)) < 0.95).astype(np.int64), 1)
+    mask = torch.from_numpy(mask_np).to(dev)
+    expect = qo.trust_bwd(to_float64(g), mask_np, 128)
+    log("trust_bwd in place")
+    out = qa.trust_bwd(g, mask, 128, out=g)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == g.data_ptr()
+    check_grad(to_float64(g), expect, 128, TOL_BF16)
+
+
+def test_non_default_stream_and_determinism(dev):
+    spec = WORKLOADS["T"].fwd[0]
+    x = make_tensor(spec, dev, row_count=2048)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    log("fwd on a side stream, twice")
+    with torch.cuda.stream(side):
+        a = qa.quantize_fwd(x, 128, 4)
+        b_ = qa.quantize_fwd(x, 128, 4, stream=side)
+    side.synchronize()
+    for t1, t2 in zip(a, b_):
+        assert torch.equal(t1, t2)
+    c = qa.quantize_fwd(x, 128, 4)
+    torch.cuda.synchronize()
+    for t1, t2 in zip(a, c):
+        assert torch.equal(t1, t2)
+
+
+def test_outputs_stay_in_bounds(dev):
+    # Outputs carved out of larger buffers, guard bytes on both sides must survive.
+    rows, cols, b = 100, 640, 3
+    spec = TensorSpec("canary", rows, cols, "bf16", "student_t", 4, 5151)
+    x = make_tensor(spec, dev)
+    ncodes, nmask = qa.codes_bytes(rows, cols, b), qa.mask_bytes(rows, cols)
+    guard = 256
+    cbuf = torch.full((ncodes + 2 * guard,), 0xA5, dtype=torch.uint8, device=dev)
+    mbuf = torch.full((nmask + 2 * guard,), 0x5A, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((rows + 2 * guard // 4,), -7.0, dtype=torch.float32, device=dev)
+    codes = cbuf[guard : guard + ncodes]
+    mask = mbuf[guard : guard + nmask]
+    scale = sbuf[guard // 4 : guard // 4 + rows]
+    log("fwd with guarded outputs")
+    qa.quantize_fwd(x, 128, b, codes=codes, scale=scale, mask=mask)
+    gbuf = torch.full((rows * cols + 2 * guard,), 1.5, dtype=torch.bfloat16, device=dev)
+    gout = gbuf[guard : guard + rows * cols].view(rows, cols)
+    qa.trust_bwd(x, mask.view(rows, cols // 8), 128, out=gout)
+    dbuf = torch.full((rows * cols + 2 * guard,), -2.5, dtype=torch.float32, device=dev)
+    dout = dbuf[guard : guard + rows * cols].view(rows, cols)
+    qa.dequantize(codes, scale, rows, cols, b, out=dout)
+    torch.cuda.synchronize()
+    assert torch.all(cbuf[:guard] == 0xA5) and torch.all(cbuf[guard + ncodes :] == 0xA5)
+    assert torch.all(mbuf[:guard] == 0x5A) and torch.all(mbuf[guard + nmask :] == 0x5A)
+    assert torch.all(sbuf[: guard // 4] == -7.0) and torch.all(sbuf[guard // 4 + rows :] == -7.0)
+    assert torch.all(gbuf[:guard] == 1.5) and torch.all(gbuf[guard + rows * cols :] == 1.5)
+    assert torch.all(dbuf[:guard] == -2.5) and torch.all(dbuf[guard + rows * cols :] == -2.5)
+    check_fwd(to_float64(x), 128, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy())
+
+
+def test_binding_rejects_misaligned_view(dev):
+    buf = torch.zeros((4 * 256 + 8,), dtype=torch.bfloat16, device=dev)
+    x = buf[8:].view(4, 256)  # 16-byte offset: aligned
+    qa.quantize_fwd(x, 128, 4)
+    y = buf[4 : 4 + 4 * 256].view(4, 256)  # 8-byte offset: misaligned
+    with pytest.raises(qa.QuestError) as e:
+        qa.quantize_fwd(y, 128, 4)
+    assert e.value.status == qa.QUEST_EALIGN
+    torch.cuda.synchronize()
