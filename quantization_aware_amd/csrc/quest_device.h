@@ -29,6 +29,139 @@ namespace quest {
 constexpr int RUN = 32;
 
 // ----------------------------------------------------------------------------
+// Coalesced global traffic through a wave-private LDS stage.
+//
+// Lanes compute on runs of 32 consecutive elements, but a wave reading its 64
+// runs run-by-run (64 or 128 B per lane, lanes 64 or 128 B apart) only
+// reaches about half of HBM bandwidth.  Instead the wave moves its chunk of
+// 64 runs with fully coalesced 16-byte-per-lane non-temporal accesses
+// (instruction k touches the k-th kilobyte of the chunk) and transposes
+// through LDS.  A run is U 16-byte pieces (U = 4 for bf16, 8 for fp32);
+// piece c of run r lives in LDS slot 64 c + (r ^ h[c]).  The XOR offsets h
+// keep both the coalesced side and the run side free of bank conflicts
+// whether the LDS serves 8 lanes per pass over 32 banks or 16 lanes over 64.
+// LDS instructions of one wave complete in order, so no barrier is needed
+// between a wave's writes and its reads of its own stage.
+// ----------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// h[c] for U = 4 is {0, 10, 4, 14} and for U = 8 {0, 2, 4, 6, 9, 11, 13, 15};
+// both are linear in the bits of c, which keeps them arithmetic (no table).
+template <int U>
+__device__ __forceinline__ constexpr int stage_xor(int c) {
+  if constexpr (U == 4) {
+    return ((c & 1) * 10) ^ ((c & 2) * 2);
+  } else {
+    return ((c & 3) * 2) ^ ((c >> 2) * 9);
+  }
+}
+
+// Load the 64 runs of a wave: lane l receives the 4U dwords of run
+// first_piece / U + l.  Pieces at or past `total` (the tensor's piece count)
+// are read from the tensor's first piece instead; those lanes compute on
+// stand-in data and must not store.
+// (Runs are handed out as plain dword arrays: element access on
+// ext_vector_type values inside unrolled loops has been seen to miscompile.)
+template <int U>
+__device__ __forceinline__ void wave_load_runs(const u32x4* __restrict__ base, int64_t first_piece, int64_t total,
+                                               int lane, u32x4* stage, uint32_t (&out)[4 * U]) {
+  u32x4 t[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t idx = first_piece + 64 * k + lane;
+    t[k] = __builtin_nontemporal_load(base + (idx < total ? idx : 0));
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int q = 64 * k + lane;
+    const int r = q / U, c = q % U;
+    stage[64 * c + (r ^ stage_xor<U>(c))] = t[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+    const u32x4 w = stage[64 * c + (lane ^ stage_xor<U>(c))];
+    out[4 * c + 0] = w.x;
+    out[4 * c + 1] = w.y;
+    out[4 * c + 2] = w.z;
+    out[4 * c + 3] = w.w;
+  }
+}
+
+// Store the 64 runs of a wave (lane l holds the 4U dwords of run
+// first_piece / U + l); pieces at or past `total` are dropped.
+template <int U>
+__device__ __forceinline__ void wave_store_runs(u32x4* __restrict__ base, int64_t first_piece, int64_t total, int lane,
+                                                u32x4* stage, const uint32_t (&in)[4 * U]) {
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+    u32x4 w;
+    w.x = in[4 * c + 0];
+    w.y = in[4 * c + 1];
+    w.z = in[4 * c + 2];
+    w.w = in[4 * c + 3];
+    stage[64 * c + (lane ^ stage_xor<U>(c))] = w;
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int q = 64 * k + lane;
+    const int r = q / U, c = q % U;
+    const u32x4 t = stage[64 * c + (r ^ stage_xor<U>(c))];
+    const int64_t idx = first_piece + q;
+    if (idx < total) __builtin_nontemporal_store(t, base + idx);
+  }
+}
+
+// Widen a run held as raw dwords to fp32 (bf16: upper half of an fp32).
+__device__ __forceinline__ void widen_run(const uint32_t (&d)[16], float (&v)[RUN]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[2 * i] = __uint_as_float(d[i] << 16);
+    v[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void widen_run(const uint32_t (&d)[32], float (&v)[RUN]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(d[i]);
+}
+
+// The same with element j replaced by +0 unless bit j of m is set: the bit is
+// sign-extended to an all-ones or all-zeros dword and ANDed onto the bits.
+__device__ __forceinline__ void widen_run_masked(const uint32_t (&d)[16], uint32_t m, float (&v)[RUN]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t keep_lo = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), 2 * i, 1));
+    const uint32_t keep_hi = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), 2 * i + 1, 1));
+    v[2 * i] = __uint_as_float((d[i] << 16) & keep_lo);
+    v[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u & keep_hi);
+  }
+}
+
+__device__ __forceinline__ void widen_run_masked(const uint32_t (&d)[32], uint32_t m, float (&v)[RUN]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), i, 1));
+    v[i] = __uint_as_float(d[i] & keep);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi);
+
+// Narrow a run of fp32 results to raw dwords of the output type.
+__device__ __forceinline__ void narrow_run(const float (&v)[RUN], uint32_t (&d)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+}
+
+__device__ __forceinline__ void narrow_run(const float (&v)[RUN], uint32_t (&d)[32]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) d[i] = __float_as_uint(v[i]);
+}
+
+// ----------------------------------------------------------------------------
 // Loads: one run of 32 elements, widened exactly to fp32.
 // ----------------------------------------------------------------------------
 
@@ -59,6 +192,79 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, float (&v)
     v[4 * i + 2] = t.z;
     v[4 * i + 3] = t.w;
   }
+}
+
+// Raw bf16 pairs of one run: d[i] holds elements 2i (low half) and 2i+1.
+__device__ __forceinline__ void load_raw_bf16(const uint16_t* __restrict__ p, uint32_t (&d)[RUN / 2]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 t = q[i];
+    d[4 * i] = t.x;
+    d[4 * i + 1] = t.y;
+    d[4 * i + 2] = t.z;
+    d[4 * i + 3] = t.w;
+  }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// r = x.lo * c.lo + x.hi * c.hi (+ acc) for bf16 pairs, fp32 result.  The
+// VOP3P form keeps the accumulator a separate operand, so one partial sum can
+// feed two outputs without a copy.
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t c) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t c, float acc) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(c), "v"(acc));
+  return r;
+}
+
+// The first two butterfly stages (pairs 1 and 2 apart) fused with the
+// widening to fp32.  For packed pairs d0 = (x0, x1), d1 = (x2, x3):
+//   a = x0 + x1,  b = x0 - x1             (dot2 against (1,1) and (1,-1))
+//   y0 = a + (x2 + x3),  y2 = a - (x2 + x3)
+//   y1 = b + (x2 - x3),  y3 = b - (x2 - x3)  (dot2 with a or b as accumulator)
+// Products of bf16 values by +-1 are exact, so each output is rounded at most
+// twice, as with fp32 adds of the widened values: six dot2 per four outputs.
+__device__ __forceinline__ void first_stages_bf16(const uint32_t (&d)[16], float (&v)[RUN]) {
+  const uint32_t pp = 0x3F803F80u;  // (+1, +1)
+  const uint32_t pm = 0xBF803F80u;  // (+1, -1)
+  const uint32_t mm = 0xBF80BF80u;  // (-1, -1)
+  const uint32_t mp = 0x3F80BF80u;  // (-1, +1)
+#pragma unroll
+  for (int i = 0; i < RUN / 4; ++i) {
+    const uint32_t d0 = d[2 * i], d1 = d[2 * i + 1];
+    const float a = dot2_bf16(d0, pp);
+    const float b = dot2_bf16(d0, pm);
+    v[4 * i + 0] = dot2_bf16(d1, pp, a);
+    v[4 * i + 2] = dot2_bf16(d1, mm, a);
+    v[4 * i + 1] = dot2_bf16(d1, pm, b);
+    v[4 * i + 3] = dot2_bf16(d1, mp, b);
+  }
+}
+
+// Sum of squares of the 32 inputs, lo^2 + hi^2 per packed pair (products of
+// bf16 values are exact in fp32), four accumulation chains.
+__device__ __forceinline__ float sum_squares_bf16(const uint32_t (&d)[16]) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RUN / 2; ++i) {
+    const bf16x2_t x = __builtin_bit_cast(bf16x2_t, d[i]);
+    a[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(x, x, a[i & 3], false);
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+__device__ __forceinline__ float sum_squares(const float (&v)[RUN]) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) a[i & 3] = __builtin_fmaf(v[i], v[i], a[i & 3]);
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
 // Masked loads for the backward pass: element j is kept when bit j of `m`
@@ -128,10 +334,11 @@ __device__ __forceinline__ void store_run(float* __restrict__ p, const float (&v
 // Unnormalised Walsh-Hadamard butterflies (Sylvester order).
 // ----------------------------------------------------------------------------
 
-// In-lane stages: pairs 1, 2, 4, 8, 16 apart.
+// In-lane stages: pairs FIRST, 2 FIRST, ..., 16 apart (FIRST = 1 does all five).
+template <int FIRST = 1>
 __device__ __forceinline__ void fwht_in_lane(float (&v)[RUN]) {
 #pragma unroll
-  for (int s = 1; s < RUN; s <<= 1) {
+  for (int s = FIRST; s < RUN; s <<= 1) {
 #pragma unroll
     for (int i = 0; i < RUN; ++i) {
       if ((i & s) == 0) {
@@ -187,10 +394,10 @@ __device__ __forceinline__ void fwht_lane_xor4(float (&v)[RUN], float sigma) {
 
 // Full unnormalised transform of a block of 2^LOGN entries spread over
 // 2^(LOGN-5) lanes.  Returns tau, the sign every value of this lane carries.
+// Cross-lane stages only (the in-lane ones done by the caller).
 template <int LOGN>
-__device__ __forceinline__ float fwht_block(float (&v)[RUN], int lane) {
+__device__ __forceinline__ float fwht_cross_lanes(float (&v)[RUN], int lane) {
   static_assert(LOGN >= 6 && LOGN <= 8, "block sizes 64, 128 and 256");
-  fwht_in_lane(v);
   const float s1 = (lane & 1) ? -1.0f : 1.0f;
   fwht_lane_xor1(v, s1);
   float tau = s1;
@@ -205,6 +412,104 @@ __device__ __forceinline__ float fwht_block(float (&v)[RUN], int lane) {
     tau *= s4;
   }
   return tau;
+}
+
+template <int LOGN>
+__device__ __forceinline__ float fwht_block(float (&v)[RUN], int lane) {
+  fwht_in_lane<1>(v);
+  return fwht_cross_lanes<LOGN>(v, lane);
+}
+
+// ----------------------------------------------------------------------------
+// One bit per element, gathered LSB-first into a dword: a comparison writes a
+// lane mask and v_addc doubles the word and adds the carry, two VALU
+// operations per element.  Elements are pushed from the last to the first, so
+// element j ends in bit j once all 32 have been pushed.
+//
+// gfx950 needs two wait states between a VALU write of an SGPR and a VALU read
+// of it.  Each block of 16 pushes therefore rotates three SGPR pairs: every
+// v_addc reads a carry written at least two instructions earlier, with no
+// s_nop in between.
+// ----------------------------------------------------------------------------
+
+// w = (w << 16) | bits, bit j = [ |v[j]| <= thr ], j = 0..15.
+__device__ __forceinline__ void push16_abs_le(uint32_t& w, const float* v, float thr) {
+  uint64_t p0, p1, p2;
+  asm(
+      "v_cmp_ge_f32_e64 %1, %20, |%19|\n\t"
+      "v_cmp_ge_f32_e64 %2, %20, |%18|\n\t"
+      "v_cmp_ge_f32_e64 %3, %20, |%17|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %20, |%16|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %20, |%15|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_ge_f32_e64 %3, %20, |%14|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %20, |%13|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %20, |%12|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_ge_f32_e64 %3, %20, |%11|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %20, |%10|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %20, |%9|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_ge_f32_e64 %3, %20, |%8|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %20, |%7|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %20, |%6|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_ge_f32_e64 %3, %20, |%5|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %20, |%4|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      : "+v"(w), "=&s"(p0), "=&s"(p1), "=&s"(p2)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]), "v"(thr));
+}
+
+// w = (w << 16) | bits, bit j = [ v[j] >= 0 ] (true for -0), j = 0..15.
+__device__ __forceinline__ void push16_nonneg(uint32_t& w, const float* v) {
+  uint64_t p0, p1, p2;
+  asm(
+      "v_cmp_le_f32_e64 %1, 0, %19\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %18\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %17\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %16\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %15\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %14\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %13\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %12\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %11\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %10\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %9\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %8\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %7\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %6\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %5\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %4\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      : "+v"(w), "=&s"(p0), "=&s"(p1), "=&s"(p2)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
 }
 
 // ----------------------------------------------------------------------------

@@ -42,32 +42,101 @@ struct BlockConst {
 // Lanes past the last row load row 0 and compute like the others (DPP needs
 // every lane of a quad), but store nothing.
 // ----------------------------------------------------------------------------
+// Quantise 32 transformed values v (= tau * sqrt(n) * y) into b-bit codes.
+// kk = tau * (L - 1) / (2 s sqrt(n)), so v * kk = y / Delta.
+template <int B>
+__device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], float kk) {
+  constexpr float L = static_cast<float>(1 << B);
+  CodeWords<B> cw;
+  if constexpr (B == 1) {
+    // u = [y >= 0]
+    float p[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) p[j] = v[j] * kk;
+    uint32_t w = 0u;
+    push16_nonneg(w, p + 16);
+    push16_nonneg(w, p);
+    cw.w[0] = w;
+  } else if constexpr (B == 2 || B == 4) {
+    // u = clamp(floor(y / Delta + L/2), 0, L-1) = RNE(min(y / Delta + (L-1)/2, L-1)), saturated
+    // at 0 by v_cvt_pk_u8_f32; the two differ only when y / Delta is exactly an integer
+    // (y exactly on a decision threshold), where round-to-even may pick the upper code.
+    // Byte k of accumulator j collects code (per-word index) k * (8/B) + j; the accumulators
+    // are then interleaved into B-bit fields.
+    constexpr int PER_BYTE = 8 / B;
+    constexpr int PER_WORD = 32 / B;
+    const float off = 0.5f * (L - 1.f);
+#pragma unroll
+    for (int w = 0; w < B; ++w) {
+      uint32_t acc[PER_BYTE];
+#pragma unroll
+      for (int j = 0; j < PER_BYTE; ++j) acc[j] = 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int j = 0; j < PER_BYTE; ++j) {
+          const float t = __builtin_fminf(__builtin_fmaf(v[w * PER_WORD + k * PER_BYTE + j], kk, off), L - 1.f);
+          acc[j] = __builtin_amdgcn_cvt_pk_u8_f32(t, k, acc[j]);
+        }
+      }
+      uint32_t word = acc[0];
+#pragma unroll
+      for (int j = 1; j < PER_BYTE; ++j) word |= acc[j] << (B * j);
+      cw.w[w] = word;
+    }
+  } else {
+    // b = 3: codes straddle dword boundaries; clamp(floor(t), 0, L-1) = trunc(clamp(t, 0, L-1)).
+#pragma unroll
+    for (int i = 0; i < B; ++i) cw.w[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[j], kk, 0.5f * L), 0.f, L - 1.f);
+      put_code<B>(cw, j, static_cast<uint32_t>(t));
+    }
+  }
+  return cw;
+}
+
 template <typename In, int LOGN, int B, bool WAVE_LOCAL>
 __global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
     quest_fwd_kernel(const In* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg, int group,
-                     float alpha, float inv_count, uint8_t* __restrict__ codes, float* __restrict__ scale,
+                     float alpha, float inv_cols, uint8_t* __restrict__ codes, float* __restrict__ scale,
                      uint32_t* __restrict__ mask) {
+  constexpr int U = sizeof(In) * 2;  // 16-byte pieces per run
+  constexpr int WAVES = (WAVE_LOCAL ? 256 : 1024) / 64;
+  __shared__ u32x4 stage_all[WAVES][64 * U];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int lrow = tid / runs_per_row;
   const int run_in_row = tid - lrow * runs_per_row;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * rows_per_wg + lrow;
   const bool valid = (lrow < rows_per_wg) && (row < rows);
-  const int64_t run = (valid ? row : 0) * runs_per_row + run_in_row;
+  // Lane t of the workgroup holds run (first run of the workgroup) + t; runs of
+  // lanes past the workgroup's rows belong to the next workgroup or lie past
+  // the tensor, and are loaded (or stood in for) but never stored.
+  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * rows_per_wg * runs_per_row;
+  const int64_t run = wg_first_run + tid;
+  const int64_t total_pieces = rows * runs_per_row * U;
 
+  uint32_t raw[4 * U];
+  wave_load_runs<U>(reinterpret_cast<const u32x4*>(x), (wg_first_run + (tid & ~63)) * U, total_pieces, lane,
+                    stage_all[tid >> 6], raw);
+
+  // The row's RMS is taken from the inputs: the orthonormal transform keeps the
+  // sum of squares (Parseval), so it equals the RMS of the transformed row.
   float v[RUN];
-  load_run(x + run * RUN, v);
-  const float tau = fwht_block<LOGN>(v, tid);
-
-  // Sum of squares of the unnormalised transform (n * y^2), four chains.
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-  for (int i = 0; i < RUN; i += 4) {
-    a0 = __builtin_fmaf(v[i + 0], v[i + 0], a0);
-    a1 = __builtin_fmaf(v[i + 1], v[i + 1], a1);
-    a2 = __builtin_fmaf(v[i + 2], v[i + 2], a2);
-    a3 = __builtin_fmaf(v[i + 3], v[i + 3], a3);
+  float ss;
+  if constexpr (sizeof(In) == 2) {
+    ss = sum_squares_bf16(raw);
+    first_stages_bf16(raw, v);
+    fwht_in_lane<4>(v);
+  } else {
+    widen_run(raw, v);
+    ss = sum_squares(v);
+    fwht_in_lane<1>(v);
   }
-  float ss = (a0 + a1) + (a2 + a3);
+  const float tau = fwht_cross_lanes<LOGN>(v, tid);
+
   if constexpr (WAVE_LOCAL) {
     for (int off = 1; off < runs_per_row; off <<= 1) ss += __shfl_xor(ss, off);
   } else {
@@ -83,12 +152,12 @@ __global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
     }
   }
 
-  // s = alpha * RMS, RMS^2 = sum(n y^2) / (n cols).
-  const float s = alpha * sqrtf(ss * inv_count);
+  // s = alpha * RMS, RMS^2 = sum(x^2) / cols.
+  const float s = alpha * sqrtf(ss * inv_cols);
   if (valid && run_in_row == 0) scale[row] = s;
 
   constexpr float L = static_cast<float>(1 << B);
-  // t = y / Delta + L/2 = v * kk + L/2 with v = tau * sqrt(n) * y;
+  // With v = tau * sqrt(n) * y:  y / Delta = v * kk,  and
   // trusted <=> |y| <= s L / (L - 1) <=> |v| <= thr.
   float kk = 0.f, thr = 0.f;
   if (s > 0.f) {
@@ -96,17 +165,10 @@ __global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
     thr = s * (L / (L - 1.f)) * BlockConst<LOGN>::sqrt_n;
   }
 
-  CodeWords<B> cw;
-#pragma unroll
-  for (int i = 0; i < B; ++i) cw.w[i] = 0u;
+  const CodeWords<B> cw = quantise_run<B>(v, kk);
   uint32_t mw = 0u;
-#pragma unroll
-  for (int j = 0; j < RUN; ++j) {
-    // clamp(floor(t), 0, L-1) == trunc(clamp(t, 0, L-1)).
-    const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[j], kk, 0.5f * L), 0.f, L - 1.f);
-    put_code<B>(cw, j, static_cast<uint32_t>(t));
-    mw |= (__builtin_fabsf(v[j]) <= thr ? 1u : 0u) << j;
-  }
+  push16_abs_le(mw, v + 16, thr);
+  push16_abs_le(mw, v, thr);
   if (valid) {
     store_codes<B>(codes, run, cw);
     mask[run] = mw;
@@ -121,17 +183,23 @@ __global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
 template <typename G, int LOGN>
 __global__ void __launch_bounds__(256)
     quest_bwd_kernel(const G* grad, const uint32_t* mask, int64_t total_runs, G* grad_out) {
+  constexpr int U = sizeof(G) * 2;
+  __shared__ u32x4 stage_all[4][64 * U];
+  const int lane = threadIdx.x & 63;
+  u32x4* stage = stage_all[threadIdx.x >> 6];
   const int64_t run0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const bool valid = run0 < total_runs;
-  const int64_t run = valid ? run0 : 0;
-  const uint32_t m = mask[run];
+  const int64_t first_piece = (run0 - lane) * U;
+  const uint32_t m = __builtin_nontemporal_load(mask + (run0 < total_runs ? run0 : 0));
+  uint32_t raw[4 * U];
+  wave_load_runs<U>(reinterpret_cast<const u32x4*>(grad), first_piece, total_runs * U, lane, stage, raw);
   float v[RUN];
-  load_run_masked(grad + run * RUN, m, v);
+  widen_run_masked(raw, m, v);
   const float tau = fwht_block<LOGN>(v, threadIdx.x);
   const float k = tau * BlockConst<LOGN>::rsqrt_n;
 #pragma unroll
   for (int j = 0; j < RUN; ++j) v[j] *= k;
-  if (valid) store_run(grad_out + run * RUN, v);
+  narrow_run(v, raw);
+  wave_store_runs<U>(reinterpret_cast<u32x4*>(grad_out), first_piece, total_runs * U, lane, stage, raw);
 }
 
 // ----------------------------------------------------------------------------
@@ -141,9 +209,11 @@ template <typename Out, int B>
 __global__ void __launch_bounds__(256)
     quest_dequant_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale, uint32_t total_runs,
                          uint32_t runs_per_row, Out* __restrict__ out) {
+  constexpr int U = sizeof(Out) * 2;
+  __shared__ u32x4 stage_all[4][64 * U];
+  const int lane = threadIdx.x & 63;
   const uint32_t run0 = blockIdx.x * 256u + threadIdx.x;
-  const bool valid = run0 < total_runs;
-  const uint32_t run = valid ? run0 : 0u;
+  const uint32_t run = run0 < total_runs ? run0 : 0u;
   const uint32_t row = run / runs_per_row;
   const float c = scale[row] / static_cast<float>((1 << B) - 1);
   const CodeWords<B> cw = load_codes<B>(codes, run);
@@ -153,7 +223,10 @@ __global__ void __launch_bounds__(256)
     const int u = static_cast<int>(get_code<B>(cw, j));
     v[j] = static_cast<float>(2 * u - (1 << B) + 1) * c;
   }
-  if (valid) store_run(out + static_cast<int64_t>(run) * RUN, v);
+  uint32_t raw[4 * U];
+  narrow_run(v, raw);
+  wave_store_runs<U>(reinterpret_cast<u32x4*>(out), (static_cast<int64_t>(run0) - lane) * U,
+                     static_cast<int64_t>(total_runs) * U, lane, stage_all[threadIdx.x >> 6], raw);
 }
 
 // ----------------------------------------------------------------------------
@@ -174,13 +247,13 @@ template <typename In, int LOGN, int B>
 hipError_t fwd_dispatch_wave(const In* x, int64_t rows, int64_t cols, float alpha, uint8_t* codes, float* scale,
                              uint8_t* mask, hipStream_t stream) {
   const int runs_per_row = static_cast<int>(cols / RUN);
-  const float inv_count = static_cast<float>(1.0 / (double(1 << LOGN) * double(cols)));
+  const float inv_cols = static_cast<float>(1.0 / double(cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
   if (runs_per_row <= 64 && (runs_per_row & (runs_per_row - 1)) == 0) {
     const int rows_per_wg = 256 / runs_per_row;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     hipLaunchKernelGGL((quest_fwd_kernel<In, LOGN, B, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
-                       x, rows, runs_per_row, rows_per_wg, 0, alpha, inv_count, codes, scale, mask32);
+                       x, rows, runs_per_row, rows_per_wg, 0, alpha, inv_cols, codes, scale, mask32);
   } else {
     int group = runs_per_row & -runs_per_row;
     if (group > 64) group = 64;
@@ -190,7 +263,7 @@ hipError_t fwd_dispatch_wave(const In* x, int64_t rows, int64_t cols, float alph
     const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     hipLaunchKernelGGL((quest_fwd_kernel<In, LOGN, B, false>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
-                       stream, x, rows, runs_per_row, rows_per_wg, group, alpha, inv_count, codes, scale, mask32);
+                       stream, x, rows, runs_per_row, rows_per_wg, group, alpha, inv_cols, codes, scale, mask32);
   }
   return hipGetLastError();
 }
