@@ -159,7 +159,7 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
   if (overlaps(x, nx, codes, nc) || overlaps(x, nx, scale, ns) || overlaps(x, nx, mask, nm) ||
       overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm))
     return QUEST_EINVAL;
-  const float alpha = static_cast<float>(quest_fit_alpha(b));
+  const double alpha = quest_fit_alpha(b);
   return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, codes, scale, mask,
                                              static_cast<hipStream_t>(stream)));
 }

@@ -29,7 +29,37 @@ namespace quest {
 constexpr int RUN = 32;
 
 // ----------------------------------------------------------------------------
-// Coalesced global traffic through a wave-private LDS stage.
+// Global memory goes through buffer instructions.  A buffer resource covers a
+// window of at most 4 GB; accesses at or past its end read zero and write
+// nothing.  Kernels build a resource per chunk of work (a few scalar
+// instructions) and pass 32-bit per-lane offsets, so there is no per-lane
+// bounds test and no divergent branch around a store: the code between waits
+// is straight-line and the wait counts stay exact (loads and stores share one
+// counter on gfx950, and a guarded store makes every later wait conservative).
+// ----------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kNonTemporal = 2;             // cache policy bit "nt"
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Bytes of the window [start, start + window) that lie inside [0, size).
+__device__ __forceinline__ uint32_t window_bytes(int64_t start, int64_t size, uint32_t window) {
+  const int64_t rem = size - start;
+  return rem <= 0 ? 0u : (rem >= static_cast<int64_t>(window) ? window : static_cast<uint32_t>(rem));
+}
+
+// Resource for the window starting `start` bytes into an array of `size` bytes at p.
+__device__ __forceinline__ rsrc_t window_at(const void* p, int64_t start, int64_t size, uint32_t window) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(start);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a), static_cast<short>(0),
+                                           static_cast<int>(window_bytes(start, size, window)), kRawBufferWord3);
+}
+
+// ----------------------------------------------------------------------------
+// Coalesced traffic through a wave-private LDS stage.
 //
 // Lanes compute on runs of 32 consecutive elements, but a wave reading its 64
 // runs run-by-run (64 or 128 B per lane, lanes 64 or 128 B apart) only
@@ -43,7 +73,6 @@ constexpr int RUN = 32;
 // LDS instructions of one wave complete in order, so no barrier is needed
 // between a wave's writes and its reads of its own stage.
 // ----------------------------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // h[c] for U = 4 is {0, 10, 4, 14} and for U = 8 {0, 2, 4, 6, 9, 11, 13, 15};
 // both are linear in the bits of c, which keeps them arithmetic (no table).
@@ -56,21 +85,23 @@ __device__ __forceinline__ constexpr int stage_xor(int c) {
   }
 }
 
-// Load the 64 runs of a wave: lane l receives the 4U dwords of run
-// first_piece / U + l.  Pieces at or past `total` (the tensor's piece count)
-// are read from the tensor's first piece instead; those lanes compute on
-// stand-in data and must not store.
+// Issue the coalesced loads of a wave's chunk: piece first_piece + 64 k + lane
+// into t[k].  Pieces at or past total_pieces read as zero.
+template <int U>
+__device__ __forceinline__ void wave_fetch(const void* base, int64_t first_piece, int64_t total_pieces, int lane,
+                                           u32x4 (&t)[U]) {
+  const rsrc_t r = window_at(base, first_piece * 16, total_pieces * 16, 64 * U * 16);
+#pragma unroll
+  for (int k = 0; k < U; ++k) t[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64 * k) * 16, 0, kNonTemporal);
+}
+
+// Transpose fetched pieces through the wave's LDS stage: lane l receives the
+// 4U dwords of run l of the chunk.
 // (Runs are handed out as plain dword arrays: element access on
 // ext_vector_type values inside unrolled loops has been seen to miscompile.)
 template <int U>
-__device__ __forceinline__ void wave_load_runs(const u32x4* __restrict__ base, int64_t first_piece, int64_t total,
-                                               int lane, u32x4* stage, uint32_t (&out)[4 * U]) {
-  u32x4 t[U];
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int64_t idx = first_piece + 64 * k + lane;
-    t[k] = __builtin_nontemporal_load(base + (idx < total ? idx : 0));
-  }
+__device__ __forceinline__ void wave_stage(const u32x4 (&t)[U], int lane, u32x4* stage, uint32_t (&out)[4 * U]) {
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int k = 0; k < U; ++k) {
     const int q = 64 * k + lane;
@@ -88,10 +119,20 @@ __device__ __forceinline__ void wave_load_runs(const u32x4* __restrict__ base, i
   }
 }
 
-// Store the 64 runs of a wave (lane l holds the 4U dwords of run
-// first_piece / U + l); pieces at or past `total` are dropped.
+// Load the 64 runs of a wave: lane l receives the 4U dwords of run
+// first_piece / U + l (zeros past the tensor).
 template <int U>
-__device__ __forceinline__ void wave_store_runs(u32x4* __restrict__ base, int64_t first_piece, int64_t total, int lane,
+__device__ __forceinline__ void wave_load_runs(const void* base, int64_t first_piece, int64_t total_pieces, int lane,
+                                               u32x4* stage, uint32_t (&out)[4 * U]) {
+  u32x4 t[U];
+  wave_fetch<U>(base, first_piece, total_pieces, lane, t);
+  wave_stage<U>(t, lane, stage, out);
+}
+
+// Store the 64 runs of a wave (lane l holds the 4U dwords of run
+// first_piece / U + l); pieces at or past total_pieces are dropped.
+template <int U>
+__device__ __forceinline__ void wave_store_runs(void* base, int64_t first_piece, int64_t total_pieces, int lane,
                                                 u32x4* stage, const uint32_t (&in)[4 * U]) {
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -104,13 +145,13 @@ __device__ __forceinline__ void wave_store_runs(u32x4* __restrict__ base, int64_
     stage[64 * c + (lane ^ stage_xor<U>(c))] = w;
   }
   __builtin_amdgcn_wave_barrier();
+  const rsrc_t r = window_at(base, first_piece * 16, total_pieces * 16, 64 * U * 16);
 #pragma unroll
   for (int k = 0; k < U; ++k) {
     const int q = 64 * k + lane;
-    const int r = q / U, c = q % U;
-    const u32x4 t = stage[64 * c + (r ^ stage_xor<U>(c))];
-    const int64_t idx = first_piece + q;
-    if (idx < total) __builtin_nontemporal_store(t, base + idx);
+    const int rr = q / U, c = q % U;
+    const u32x4 t = stage[64 * c + (rr ^ stage_xor<U>(c))];
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, q * 16, 0, kNonTemporal);
   }
 }
 
@@ -162,49 +203,30 @@ __device__ __forceinline__ void narrow_run(const float (&v)[RUN], uint32_t (&d)[
 }
 
 // ----------------------------------------------------------------------------
-// Loads: one run of 32 elements, widened exactly to fp32.
+// Sum over aligned groups of 2^log_g lanes (log_g <= 6, wave-uniform); every
+// lane of a group ends with the group's sum, added in the same order.  After
+// the two quad steps all lanes of a quad agree, so the half-row mirror (lane
+// i with 7 - i) and the row mirror (i with 15 - i) pair whole quads and whole
+// half-rows; lanes 16 apart meet through ds_swizzle, the two halves of the
+// wave through v_readlane.
 // ----------------------------------------------------------------------------
-
-__device__ __forceinline__ void load_run(const uint16_t* __restrict__ p, float (&v)[RUN]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = q[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t d[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // bf16 is the upper half of an fp32: widening is a shift or a mask.
-      v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-      v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-    }
-  }
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ void load_run(const float* __restrict__ p, float (&v)[RUN]) {
-  const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 t = q[i];
-    v[4 * i] = t.x;
-    v[4 * i + 1] = t.y;
-    v[4 * i + 2] = t.z;
-    v[4 * i + 3] = t.w;
+__device__ __forceinline__ float group_sum(float x, int log_g) {
+  if (log_g > 0) x += dpp_read<0xB1>(x);   // quad_perm [1,0,3,2]
+  if (log_g > 1) x += dpp_read<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (log_g > 2) x += dpp_read<0x141>(x);  // row_half_mirror
+  if (log_g > 3) x += dpp_read<0x140>(x);  // row_mirror
+  if (log_g > 4) x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // lane ^ 16
+  if (log_g > 5) {
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    x = lo + hi;
   }
-}
-
-// Raw bf16 pairs of one run: d[i] holds elements 2i (low half) and 2i+1.
-__device__ __forceinline__ void load_raw_bf16(const uint16_t* __restrict__ p, uint32_t (&d)[RUN / 2]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 t = q[i];
-    d[4 * i] = t.x;
-    d[4 * i + 1] = t.y;
-    d[4 * i + 2] = t.z;
-    d[4 * i + 3] = t.w;
-  }
+  return x;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -267,39 +289,8 @@ __device__ __forceinline__ float sum_squares(const float (&v)[RUN]) {
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// Masked loads for the backward pass: element j is kept when bit j of `m`
-// is set, otherwise it becomes +0.  The bit is sign-extended to an all-ones
-// or all-zeros dword and ANDed onto the fp32 bit pattern.
-__device__ __forceinline__ void load_run_masked(const uint16_t* __restrict__ p, uint32_t m, float (&v)[RUN]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = q[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t d[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 8 * i + 2 * j;
-      const uint32_t keep_lo = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), e, 1));
-      const uint32_t keep_hi = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), e + 1, 1));
-      v[e] = __uint_as_float((d[j] << 16) & keep_lo);
-      v[e + 1] = __uint_as_float(d[j] & 0xFFFF0000u & keep_hi);
-    }
-  }
-}
-
-__device__ __forceinline__ void load_run_masked(const float* __restrict__ p, uint32_t m, float (&v)[RUN]) {
-  load_run(p, v);
-#pragma unroll
-  for (int e = 0; e < RUN; ++e) {
-    const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(m), e, 1));
-    v[e] = __uint_as_float(__float_as_uint(v[e]) & keep);
-  }
-}
-
 // ----------------------------------------------------------------------------
-// Stores of a run of fp32 results, rounded to the output type.
+// fp32 to bf16, two at a time.
 // ----------------------------------------------------------------------------
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -309,25 +300,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 f = {lo, hi};
   const bf16x2 h = __builtin_convertvector(f, bf16x2);
   return __builtin_bit_cast(uint32_t, h);
-}
-
-__device__ __forceinline__ void store_run(uint16_t* __restrict__ p, const float (&v)[RUN]) {
-  uint4* q = reinterpret_cast<uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 t;
-    t.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
-    t.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
-    t.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
-    t.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
-    q[i] = t;
-  }
-}
-
-__device__ __forceinline__ void store_run(float* __restrict__ p, const float (&v)[RUN]) {
-  float4* q = reinterpret_cast<float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
 // ----------------------------------------------------------------------------
@@ -530,19 +502,18 @@ __device__ __forceinline__ void put_code(CodeWords<B>& cw, int j, uint32_t code)
   if (off + B > 32) cw.w[wi + 1] |= code >> (32 - off);
 }
 
+// Store the codes of run `lane` of a window (4 B bytes per run).
 template <int B>
-__device__ __forceinline__ void store_codes(uint8_t* __restrict__ codes, int64_t run, const CodeWords<B>& cw) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(codes) + run * B;
+__device__ __forceinline__ void store_codes(rsrc_t r, int lane, const CodeWords<B>& cw) {
+  const int off = lane * 4 * B;
   if constexpr (B == 1) {
-    p[0] = cw.w[0];
+    __builtin_amdgcn_raw_buffer_store_b32(cw.w[0], r, off, 0, kNonTemporal);
   } else if constexpr (B == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(cw.w[0], cw.w[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[0], cw.w[1]}, r, off, 0, kNonTemporal);
   } else if constexpr (B == 3) {
-    p[0] = cw.w[0];
-    p[1] = cw.w[1];
-    p[2] = cw.w[2];
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[0], cw.w[1], cw.w[2]}, r, off, 0, kNonTemporal);
   } else {
-    *reinterpret_cast<uint4*>(p) = make_uint4(cw.w[0], cw.w[1], cw.w[2], cw.w[3]);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[0], cw.w[1], cw.w[2], cw.w[3]}, r, off, 0, kNonTemporal);
   }
 }
 
@@ -556,22 +527,24 @@ __device__ __forceinline__ uint32_t get_code(const CodeWords<B>& cw, int j) {
   return c & ((1u << B) - 1u);
 }
 
+// Load the codes of run `lane` of a window (zeros past its end).
 template <int B>
-__device__ __forceinline__ CodeWords<B> load_codes(const uint8_t* __restrict__ codes, int64_t run) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(codes) + run * B;
+__device__ __forceinline__ CodeWords<B> load_codes(rsrc_t r, int lane) {
+  const int off = lane * 4 * B;
   CodeWords<B> cw;
   if constexpr (B == 1) {
-    cw.w[0] = p[0];
+    cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else if constexpr (B == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     cw.w[0] = t.x;
     cw.w[1] = t.y;
   } else if constexpr (B == 3) {
-    cw.w[0] = p[0];
-    cw.w[1] = p[1];
-    cw.w[2] = p[2];
+    const u32x3 t = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    cw.w[0] = t.x;
+    cw.w[1] = t.y;
+    cw.w[2] = t.z;
   } else {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     cw.w[0] = t.x;
     cw.w[1] = t.y;
     cw.w[2] = t.z;

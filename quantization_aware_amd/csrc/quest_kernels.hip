@@ -10,10 +10,12 @@
 //
 // All three stream through HBM once.  The forward transform is computed
 // unnormalised (entries scaled by sqrt(n)); codes and mask only depend on
-// y / Delta, so the factor is folded into the per-row constants instead of
+// y / Delta, so the factor is folded into per-row constants instead of
 // costing a multiply per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cmath>
 
 #include "quest_device.h"
 #include "quest_launch.h"
@@ -22,28 +24,32 @@ namespace quest {
 
 template <int LOGN>
 struct BlockConst {
-  // 1/sqrt(n) and sqrt(n) for n = 2^LOGN, exact to fp32 rounding.
+  // 1/sqrt(n) for n = 2^LOGN, rounded once to fp32.
   static constexpr double kRsqrt2 = 0.70710678118654752440084436210485;
   static constexpr float rsqrt_n =
       static_cast<float>((LOGN & 1) ? kRsqrt2 / double(1 << (LOGN / 2)) : 1.0 / double(1 << (LOGN / 2)));
-  static constexpr float sqrt_n =
-      static_cast<float>((LOGN & 1) ? double(1 << (LOGN / 2)) / kRsqrt2 : double(1 << (LOGN / 2)));
 };
 
+// Byte offset that lies past every window: a buffer store there is dropped.
+constexpr int kNowhere = 0x7FFFFFF0;
+
 // ----------------------------------------------------------------------------
-// Forward quantisation.
-//
-// Workgroup = rows_per_wg rows; a row is runs_per_row = cols/32 consecutive
-// lanes.  WAVE_LOCAL: runs_per_row is a power of two <= 64, so a row lives
-// inside one wavefront and its sum of squares is a butterfly over lanes.
-// Otherwise a row spans several wavefronts: lanes reduce in aligned groups of
-// `group` lanes (a power of two dividing runs_per_row), group sums go through
-// LDS and every lane adds up the groups of its row in the same order.
-// Lanes past the last row load row 0 and compute like the others (DPP needs
-// every lane of a quad), but store nothing.
+// Forward quantisation
 // ----------------------------------------------------------------------------
-// Quantise 32 transformed values v (= tau * sqrt(n) * y) into b-bit codes.
-// kk = tau * (L - 1) / (2 s sqrt(n)), so v * kk = y / Delta.
+
+// Per-bit-width constants computed on the host in float64 and rounded once:
+//   alpha = alpha_b,  kk = (L - 1) / (2 alpha_b sqrt(n)),  thr = alpha_b L sqrt(n) / (L - 1).
+// With m = mean of x^2 over the row (RMS^2) and v = tau * sqrt(n) * y:
+//   s = alpha * sqrt(m),  y / Delta = v * tau * kk / sqrt(m),  trusted <=> |v| <= thr * sqrt(m).
+struct FwdConsts {
+  float alpha;
+  float kk;
+  float thr;
+  float inv_cols;
+};
+
+// Quantise 32 transformed values v (= tau * sqrt(n) * y) into b-bit codes,
+// given kk = y / (Delta v).
 template <int B>
 __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], float kk) {
   constexpr float L = static_cast<float>(1 << B);
@@ -97,35 +103,13 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
   return cw;
 }
 
-template <typename In, int LOGN, int B, bool WAVE_LOCAL>
-__global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
-    quest_fwd_kernel(const In* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg, int group,
-                     float alpha, float inv_cols, uint8_t* __restrict__ codes, float* __restrict__ scale,
-                     uint32_t* __restrict__ mask) {
-  constexpr int U = sizeof(In) * 2;  // 16-byte pieces per run
-  constexpr int WAVES = (WAVE_LOCAL ? 256 : 1024) / 64;
-  __shared__ u32x4 stage_all[WAVES][64 * U];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int lrow = tid / runs_per_row;
-  const int run_in_row = tid - lrow * runs_per_row;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * rows_per_wg + lrow;
-  const bool valid = (lrow < rows_per_wg) && (row < rows);
-  // Lane t of the workgroup holds run (first run of the workgroup) + t; runs of
-  // lanes past the workgroup's rows belong to the next workgroup or lie past
-  // the tensor, and are loaded (or stood in for) but never stored.
-  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * rows_per_wg * runs_per_row;
-  const int64_t run = wg_first_run + tid;
-  const int64_t total_pieces = rows * runs_per_row * U;
-
-  uint32_t raw[4 * U];
-  wave_load_runs<U>(reinterpret_cast<const u32x4*>(x), (wg_first_run + (tid & ~63)) * U, total_pieces, lane,
-                    stage_all[tid >> 6], raw);
-
-  // The row's RMS is taken from the inputs: the orthonormal transform keeps the
-  // sum of squares (Parseval), so it equals the RMS of the transformed row.
-  float v[RUN];
-  float ss;
+// Transform one run per lane: returns tau and the lane's share of the row's
+// sum of squares.  The row's RMS is taken from the inputs: the orthonormal
+// transform keeps the sum of squares (Parseval), so it equals the RMS of the
+// transformed row.
+template <typename In, int LOGN>
+__device__ __forceinline__ float fwd_transform(const uint32_t (&raw)[8 * sizeof(In)], float (&v)[RUN], float& ss,
+                                               int lane_bits) {
   if constexpr (sizeof(In) == 2) {
     ss = sum_squares_bf16(raw);
     first_stages_bf16(raw, v);
@@ -135,50 +119,142 @@ __global__ void __launch_bounds__(WAVE_LOCAL ? 256 : 1024)
     ss = sum_squares(v);
     fwht_in_lane<1>(v);
   }
-  const float tau = fwht_cross_lanes<LOGN>(v, tid);
+  return fwht_cross_lanes<LOGN>(v, lane_bits);
+}
 
-  if constexpr (WAVE_LOCAL) {
-    for (int off = 1; off < runs_per_row; off <<= 1) ss += __shfl_xor(ss, off);
-  } else {
-    __shared__ float part[1024];
-    for (int off = 1; off < group; off <<= 1) ss += __shfl_xor(ss, off);
-    if ((tid & (group - 1)) == 0) part[tid / group] = ss;
-    __syncthreads();
-    const int per_row = runs_per_row / group;
-    ss = 0.f;
-    if (lrow < rows_per_wg) {
-      const float* pr = part + lrow * per_row;
-      for (int i = 0; i < per_row; ++i) ss += pr[i];
-    }
-  }
-
-  // s = alpha * RMS, RMS^2 = sum(x^2) / cols.
-  const float s = alpha * sqrtf(ss * inv_cols);
-  if (valid && run_in_row == 0) scale[row] = s;
-
-  constexpr float L = static_cast<float>(1 << B);
-  // With v = tau * sqrt(n) * y:  y / Delta = v * kk,  and
-  // trusted <=> |y| <= s L / (L - 1) <=> |v| <= thr.
-  float kk = 0.f, thr = 0.f;
-  if (s > 0.f) {
-    kk = tau * ((L - 1.f) / (2.f * s)) * BlockConst<LOGN>::rsqrt_n;
-    thr = s * (L / (L - 1.f)) * BlockConst<LOGN>::sqrt_n;
-  }
-
+// Codes, mask and scale of one run per lane, once its row's sum of squares is
+// known.  The lane's codes go to offset 4 B lane of `codes_r`, its mask word to
+// 4 lane of `mask_r`, and the row scale to `scale_off` of `scale_r` (kNowhere
+// for all lanes but one per row).
+template <int B>
+__device__ __forceinline__ void fwd_quantise_store(const float (&v)[RUN], float tau, float ss, const FwdConsts& k,
+                                                   int lane, rsrc_t codes_r, rsrc_t mask_r, rsrc_t scale_r,
+                                                   int scale_off) {
+  const float ms = ss * k.inv_cols;
+  const float rms = __builtin_amdgcn_sqrtf(ms);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(k.alpha * rms), scale_r, scale_off, 0, 0);
+  // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
+  const float kk = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
+  const float thr = k.thr * rms;
   const CodeWords<B> cw = quantise_run<B>(v, kk);
   uint32_t mw = 0u;
   push16_abs_le(mw, v + 16, thr);
   push16_abs_le(mw, v, thr);
-  if (valid) {
-    store_codes<B>(codes, run, cw);
-    mask[run] = mw;
+  store_codes<B>(codes_r, lane, cw);
+  __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, kNonTemporal);
+}
+
+// Rows of at most 64 runs (cols <= 2048) with a power-of-two run count: a
+// wave's 64 lanes hold 64 consecutive runs ("a tile", 64 / runs_per_row
+// whole rows), so the row reduction stays inside the wave.  Each wave walks
+// tiles tile0, tile0 + stride, ... with its loads running two tiles ahead of
+// the arithmetic.
+template <typename In, int LOGN, int B>
+__global__ void __launch_bounds__(256)
+    quest_fwd_tiles_kernel(const In* __restrict__ x, int64_t total_runs, int log_runs_per_row, FwdConsts k,
+                           uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask) {
+  constexpr int U = sizeof(In) * 2;  // 16-byte pieces per run
+  __shared__ u32x4 stage_all[4][64 * U];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  u32x4* stage = stage_all[wave];
+  const int64_t total_pieces = total_runs * U;
+  const int64_t rows = total_runs >> log_runs_per_row;
+  const int64_t tiles = (total_runs + 63) >> 6;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (tile >= tiles) return;
+  const int rows_per_tile = 64 >> log_runs_per_row;
+  const int scale_off = (lane & ((1 << log_runs_per_row) - 1)) == 0 ? (lane >> log_runs_per_row) * 4 : kNowhere;
+
+  auto process = [&](int64_t t, const u32x4 (&pieces)[U]) {
+    uint32_t raw[4 * U];
+    wave_stage<U>(pieces, lane, stage, raw);
+    float v[RUN];
+    float ss;
+    const float tau = fwd_transform<In, LOGN>(raw, v, ss, lane);
+    ss = group_sum(ss, log_runs_per_row);
+    const int64_t run0 = t * 64;
+    const rsrc_t codes_r = window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B);
+    const rsrc_t mask_r = window_at(mask, run0 * 4, total_runs * 4, 64 * 4);
+    const rsrc_t scale_r = window_at(scale, t * rows_per_tile * 4, rows * 4, rows_per_tile * 4);
+    fwd_quantise_store<B>(v, tau, ss, k, lane, codes_r, mask_r, scale_r, scale_off);
+  };
+
+  // Three tile buffers, fetched two tiles ahead.  Every fetch is issued (past
+  // the last tile it reads zeros), so each wait only has to cover loads
+  // issued two tiles earlier: the stores of the previous tile and the newer
+  // fetches stay in flight (loads and stores share one counter).
+  u32x4 a[U], b[U], c[U];
+  wave_fetch<U>(x, tile * 64 * U, total_pieces, lane, a);
+  wave_fetch<U>(x, (tile + stride) * 64 * U, total_pieces, lane, b);
+  for (;;) {
+    wave_fetch<U>(x, (tile + 2 * stride) * 64 * U, total_pieces, lane, c);
+    process(tile, a);
+    tile += stride;
+    if (tile >= tiles) break;
+    wave_fetch<U>(x, (tile + 2 * stride) * 64 * U, total_pieces, lane, a);
+    process(tile, b);
+    tile += stride;
+    if (tile >= tiles) break;
+    wave_fetch<U>(x, (tile + 2 * stride) * 64 * U, total_pieces, lane, b);
+    process(tile, c);
+    tile += stride;
+    if (tile >= tiles) break;
   }
+}
+
+// Rows that span several wavefronts (or whose run count is not a power of
+// two): a workgroup holds rows_per_wg whole rows, lane t holding run
+// (first run of the workgroup) + t.  Lanes reduce in aligned groups of
+// 2^log_group lanes (a power of two dividing runs_per_row), group sums go
+// through LDS and every lane adds up the groups of its row in the same order.
+// Lanes past the workgroup's rows compute on whatever they loaded (DPP needs
+// whole quads) and their stores fall outside the workgroup's windows.
+template <typename In, int LOGN, int B>
+__global__ void __launch_bounds__(1024)
+    quest_fwd_rows_kernel(const In* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg, int log_group,
+                          FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
+                          uint32_t* __restrict__ mask) {
+  constexpr int U = sizeof(In) * 2;
+  __shared__ u32x4 stage_all[16][64 * U];
+  __shared__ float part[1024];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lrow = tid / runs_per_row;
+  const int run_in_row = tid - lrow * runs_per_row;
+  const int64_t total_runs = rows * runs_per_row;
+  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * rows_per_wg * runs_per_row;
+  const int wave_tid0 = __builtin_amdgcn_readfirstlane(tid) & ~63;
+
+  uint32_t raw[4 * U];
+  wave_load_runs<U>(x, (wg_first_run + wave_tid0) * U, total_runs * U, lane, stage_all[wave_tid0 >> 6], raw);
+  float v[RUN];
+  float ss;
+  const float tau = fwd_transform<In, LOGN>(raw, v, ss, tid);
+
+  ss = group_sum(ss, log_group);
+  if ((tid & ((1 << log_group) - 1)) == 0) part[tid >> log_group] = ss;
+  __syncthreads();
+  const int per_row = runs_per_row >> log_group;
+  ss = 0.f;
+  if (lrow < rows_per_wg) {
+    const float* pr = part + lrow * per_row;
+    for (int i = 0; i < per_row; ++i) ss += pr[i];
+  }
+  const uint32_t wg_runs = static_cast<uint32_t>(rows_per_wg * runs_per_row);
+  const rsrc_t codes_r = window_at(codes, wg_first_run * 4 * B, total_runs * 4 * B, wg_runs * 4 * B);
+  const rsrc_t mask_r = window_at(mask, wg_first_run * 4, total_runs * 4, wg_runs * 4);
+  const rsrc_t scale_r =
+      window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
+  const int scale_off = (run_in_row == 0 && lrow < rows_per_wg) ? lrow * 4 : kNowhere;
+  fwd_quantise_store<B>(v, tau, ss, k, tid, codes_r, mask_r, scale_r, scale_off);
 }
 
 // ----------------------------------------------------------------------------
 // Trust-masked backward: one lane per run, no cross-row work.
-// grad and grad_out may be the same buffer: every run is read and written by
-// the same lane only, and its loads come before its stores.
+// grad and grad_out may be the same buffer: every chunk is read and written
+// by the same wave only, and its loads come before its stores.
 // ----------------------------------------------------------------------------
 template <typename G, int LOGN>
 __global__ void __launch_bounds__(256)
@@ -186,20 +262,21 @@ __global__ void __launch_bounds__(256)
   constexpr int U = sizeof(G) * 2;
   __shared__ u32x4 stage_all[4][64 * U];
   const int lane = threadIdx.x & 63;
-  u32x4* stage = stage_all[threadIdx.x >> 6];
-  const int64_t run0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t first_piece = (run0 - lane) * U;
-  const uint32_t m = __builtin_nontemporal_load(mask + (run0 < total_runs ? run0 : 0));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  u32x4* stage = stage_all[wave];
+  const int64_t run0 = static_cast<int64_t>(blockIdx.x) * 256 + wave * 64;  // first run of the wave
+  const rsrc_t mask_r = window_at(mask, run0 * 4, total_runs * 4, 64 * 4);
+  const uint32_t m = __builtin_amdgcn_raw_buffer_load_b32(mask_r, lane * 4, 0, kNonTemporal);
   uint32_t raw[4 * U];
-  wave_load_runs<U>(reinterpret_cast<const u32x4*>(grad), first_piece, total_runs * U, lane, stage, raw);
+  wave_load_runs<U>(grad, run0 * U, total_runs * U, lane, stage, raw);
   float v[RUN];
   widen_run_masked(raw, m, v);
-  const float tau = fwht_block<LOGN>(v, threadIdx.x);
+  const float tau = fwht_block<LOGN>(v, lane);
   const float k = tau * BlockConst<LOGN>::rsqrt_n;
 #pragma unroll
   for (int j = 0; j < RUN; ++j) v[j] *= k;
   narrow_run(v, raw);
-  wave_store_runs<U>(reinterpret_cast<u32x4*>(grad_out), first_piece, total_runs * U, lane, stage, raw);
+  wave_store_runs<U>(grad_out, run0 * U, total_runs * U, lane, stage, raw);
 }
 
 // ----------------------------------------------------------------------------
@@ -207,16 +284,20 @@ __global__ void __launch_bounds__(256)
 // ----------------------------------------------------------------------------
 template <typename Out, int B>
 __global__ void __launch_bounds__(256)
-    quest_dequant_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale, uint32_t total_runs,
+    quest_dequant_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale, int64_t total_runs,
                          uint32_t runs_per_row, Out* __restrict__ out) {
   constexpr int U = sizeof(Out) * 2;
   __shared__ u32x4 stage_all[4][64 * U];
   const int lane = threadIdx.x & 63;
-  const uint32_t run0 = blockIdx.x * 256u + threadIdx.x;
-  const uint32_t run = run0 < total_runs ? run0 : 0u;
-  const uint32_t row = run / runs_per_row;
-  const float c = scale[row] / static_cast<float>((1 << B) - 1);
-  const CodeWords<B> cw = load_codes<B>(codes, run);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t run0 = static_cast<int64_t>(blockIdx.x) * 256 + wave * 64;
+  // rows * 4 bytes stay below 2^32 (rows * cols < 2^36, cols >= 64).
+  const uint32_t row = static_cast<uint32_t>((run0 + lane) / runs_per_row);
+  const int64_t rows = total_runs / runs_per_row;
+  const rsrc_t scale_r = window_at(scale, 0, rows * 4, 0xFFFFFFF0u);
+  const float c = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scale_r, static_cast<int>(row * 4), 0, 0)) /
+                  static_cast<float>((1 << B) - 1);
+  const CodeWords<B> cw = load_codes<B>(window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B), lane);
   float v[RUN];
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
@@ -225,8 +306,7 @@ __global__ void __launch_bounds__(256)
   }
   uint32_t raw[4 * U];
   narrow_run(v, raw);
-  wave_store_runs<U>(reinterpret_cast<u32x4*>(out), (static_cast<int64_t>(run0) - lane) * U,
-                     static_cast<int64_t>(total_runs) * U, lane, stage_all[threadIdx.x >> 6], raw);
+  wave_store_runs<U>(out, run0 * U, total_runs * U, lane, stage_all[wave], raw);
 }
 
 // ----------------------------------------------------------------------------
@@ -243,17 +323,35 @@ int gcd_int(int a, int b) {
   return a;
 }
 
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+// Workgroups (of four waves) launched for the tiled forward kernel: two per
+// compute unit on the 256-CU MI355X, so each wave walks several tiles and its
+// loads run ahead of the arithmetic.
+constexpr int64_t kFwdTileWorkgroups = 512;
+
 template <typename In, int LOGN, int B>
-hipError_t fwd_dispatch_wave(const In* x, int64_t rows, int64_t cols, float alpha, uint8_t* codes, float* scale,
-                             uint8_t* mask, hipStream_t stream) {
+hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, uint8_t* codes, float* scale,
+                        uint8_t* mask, hipStream_t stream) {
   const int runs_per_row = static_cast<int>(cols / RUN);
-  const float inv_cols = static_cast<float>(1.0 / double(cols));
+  const double L = double(1 << B), sqrt_n = std::sqrt(double(1 << LOGN));
+  FwdConsts k;
+  k.alpha = static_cast<float>(alpha);
+  k.kk = static_cast<float>((L - 1.0) / (2.0 * alpha * sqrt_n));
+  k.thr = static_cast<float>(alpha * L * sqrt_n / (L - 1.0));
+  k.inv_cols = static_cast<float>(1.0 / double(cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
   if (runs_per_row <= 64 && (runs_per_row & (runs_per_row - 1)) == 0) {
-    const int rows_per_wg = 256 / runs_per_row;
-    const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((quest_fwd_kernel<In, LOGN, B, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
-                       x, rows, runs_per_row, rows_per_wg, 0, alpha, inv_cols, codes, scale, mask32);
+    const int64_t total_runs = rows * runs_per_row;
+    const int64_t tiles = (total_runs + 63) / 64;
+    int64_t wgs = (tiles + 3) / 4;
+    if (wgs > kFwdTileWorkgroups) wgs = kFwdTileWorkgroups;
+    hipLaunchKernelGGL((quest_fwd_tiles_kernel<In, LOGN, B>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream,
+                       x, total_runs, log2_exact(runs_per_row), k, codes, scale, mask32);
   } else {
     int group = runs_per_row & -runs_per_row;
     if (group > 64) group = 64;
@@ -262,25 +360,25 @@ hipError_t fwd_dispatch_wave(const In* x, int64_t rows, int64_t cols, float alph
     if (rows_per_wg < 1) rows_per_wg = 1;
     const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((quest_fwd_kernel<In, LOGN, B, false>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
-                       stream, x, rows, runs_per_row, rows_per_wg, group, alpha, inv_cols, codes, scale, mask32);
+    hipLaunchKernelGGL((quest_fwd_rows_kernel<In, LOGN, B>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
+                       stream, x, rows, runs_per_row, rows_per_wg, log2_exact(group), k, codes, scale, mask32);
   }
   return hipGetLastError();
 }
 
 template <typename In, int LOGN>
-hipError_t fwd_dispatch_bits(const In* x, int64_t rows, int64_t cols, int bits, float alpha, uint8_t* codes,
+hipError_t fwd_dispatch_bits(const In* x, int64_t rows, int64_t cols, int bits, double alpha, uint8_t* codes,
                              float* scale, uint8_t* mask, hipStream_t stream) {
   switch (bits) {
-    case 1: return fwd_dispatch_wave<In, LOGN, 1>(x, rows, cols, alpha, codes, scale, mask, stream);
-    case 2: return fwd_dispatch_wave<In, LOGN, 2>(x, rows, cols, alpha, codes, scale, mask, stream);
-    case 3: return fwd_dispatch_wave<In, LOGN, 3>(x, rows, cols, alpha, codes, scale, mask, stream);
-    default: return fwd_dispatch_wave<In, LOGN, 4>(x, rows, cols, alpha, codes, scale, mask, stream);
+    case 1: return fwd_dispatch<In, LOGN, 1>(x, rows, cols, alpha, codes, scale, mask, stream);
+    case 2: return fwd_dispatch<In, LOGN, 2>(x, rows, cols, alpha, codes, scale, mask, stream);
+    case 3: return fwd_dispatch<In, LOGN, 3>(x, rows, cols, alpha, codes, scale, mask, stream);
+    default: return fwd_dispatch<In, LOGN, 4>(x, rows, cols, alpha, codes, scale, mask, stream);
   }
 }
 
 template <typename In>
-hipError_t fwd_dispatch_block(const In* x, int64_t rows, int64_t cols, int log_block, int bits, float alpha,
+hipError_t fwd_dispatch_block(const In* x, int64_t rows, int64_t cols, int log_block, int bits, double alpha,
                               uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
   switch (log_block) {
     case 6: return fwd_dispatch_bits<In, 6>(x, rows, cols, bits, alpha, codes, scale, mask, stream);
@@ -316,8 +414,8 @@ template <typename Out>
 hipError_t dequant_dispatch(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits, Out* out,
                             hipStream_t stream) {
   const uint32_t runs_per_row = static_cast<uint32_t>(cols / RUN);
-  const uint32_t total_runs = static_cast<uint32_t>(rows) * runs_per_row;
-  const uint32_t grid = (total_runs + 255u) / 256u;
+  const int64_t total_runs = rows * runs_per_row;
+  const uint32_t grid = static_cast<uint32_t>((total_runs + 255) / 256);
   switch (bits) {
     case 1:
       hipLaunchKernelGGL((quest_dequant_kernel<Out, 1>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
@@ -342,7 +440,7 @@ hipError_t dequant_dispatch(const uint8_t* codes, const float* scale, int64_t ro
 }  // namespace
 
 hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
-                               float alpha, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
+                               double alpha, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
   if (x_is_bf16)
     return fwd_dispatch_block(static_cast<const uint16_t*>(x), rows, cols, log_block, bits, alpha, codes, scale, mask,
                               stream);
