@@ -37,6 +37,9 @@ def build_command(out_path: str = LIB_PATH) -> list[str]:
         "-target-feature",
         "-Xclang",
         "-packed-fp32-ops",
+        # Matrix-core results go straight to VGPRs (no accumulator-register copies).
+        "-mllvm",
+        "-amdgpu-mfma-vgpr-form",
         "-I",
         os.path.join(ROOT, "include"),
         "-o",

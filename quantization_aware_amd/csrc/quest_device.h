@@ -327,9 +327,17 @@ __device__ __forceinline__ void fwht_in_lane(float (&v)[RUN]) {
 // quad permutation.  The leading s_nop 1 gives the two wait states gfx9
 // requires between a VALU write of a VGPR and a DPP read of it; inside the
 // block every DPP source is a different register, untouched by the block.
-#define QUEST_FMAC_DPP8(PERM)                                                                              \
+#define QUEST_FMAC_DPP8(PERM) QUEST_FMAC_DPP8_AFTER(PERM, "s_nop 1\n\t")
+
+// The same block preceded by a given wait.  The compiler counts wait states
+// only for instructions it can see, not for reads inside inline asm, so a
+// block whose inputs come straight from a matrix-core instruction supplies
+// the VALU-read-after-MFMA-write wait itself: 8 wait states for
+// v_mfma_f32_16x16x32_bf16 on gfx950 (the count the compiler inserts before
+// its own reads), given here as 10.
+#define QUEST_FMAC_DPP8_AFTER(PERM, WAIT)                                                                  \
   asm volatile(                                                                                            \
-      "s_nop 1\n\t"                                                                                        \
+      WAIT                                                                                                 \
       "v_fmac_f32_dpp %0, %0, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
       "v_fmac_f32_dpp %1, %1, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
       "v_fmac_f32_dpp %2, %2, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
@@ -346,6 +354,12 @@ __device__ __forceinline__ void fwht_in_lane(float (&v)[RUN]) {
 __device__ __forceinline__ void fwht_lane_xor1(float (&v)[RUN], float sigma) {
 #pragma unroll
   for (int k = 0; k < RUN; k += 8) QUEST_FMAC_DPP8("[1,0,3,2]");
+}
+
+// The same on values just written by v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ void fwht_lane_xor1_after_mfma(float (&v)[RUN], float sigma) {
+#pragma unroll
+  for (int k = 0; k < RUN; k += 8) QUEST_FMAC_DPP8_AFTER("[1,0,3,2]", "s_nop 7\n\ts_nop 1\n\t");
 }
 
 // Butterfly between lanes l and l ^ 2.
@@ -367,11 +381,15 @@ __device__ __forceinline__ void fwht_lane_xor4(float (&v)[RUN], float sigma) {
 // Full unnormalised transform of a block of 2^LOGN entries spread over
 // 2^(LOGN-5) lanes.  Returns tau, the sign every value of this lane carries.
 // Cross-lane stages only (the in-lane ones done by the caller).
-template <int LOGN>
+template <int LOGN, bool AFTER_MFMA = false>
 __device__ __forceinline__ float fwht_cross_lanes(float (&v)[RUN], int lane) {
   static_assert(LOGN >= 6 && LOGN <= 8, "block sizes 64, 128 and 256");
   const float s1 = (lane & 1) ? -1.0f : 1.0f;
-  fwht_lane_xor1(v, s1);
+  if constexpr (AFTER_MFMA) {
+    fwht_lane_xor1_after_mfma(v, s1);
+  } else {
+    fwht_lane_xor1(v, s1);
+  }
   float tau = s1;
   if constexpr (LOGN >= 7) {
     const float s2 = (lane & 2) ? -1.0f : 1.0f;
@@ -482,6 +500,133 @@ __device__ __forceinline__ void push16_nonneg(uint32_t& w, const float* v) {
       "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
       : "+v"(w), "=&s"(p0), "=&s"(p1), "=&s"(p2)
       : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+}
+
+// w = (w << 8) | bits, bit j = [ |v[j]| <= thr ], j = 0..7 (same scheme, 8 elements).
+__device__ __forceinline__ void push8_abs_le(uint32_t& w, const float* v, float thr) {
+  uint64_t p0, p1, p2;
+  asm(
+      "v_cmp_ge_f32_e64 %1, %12, |%11|\n\t"
+      "v_cmp_ge_f32_e64 %2, %12, |%10|\n\t"
+      "v_cmp_ge_f32_e64 %3, %12, |%9|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %12, |%8|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %12, |%7|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_ge_f32_e64 %3, %12, |%6|\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_ge_f32_e64 %1, %12, |%5|\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_ge_f32_e64 %2, %12, |%4|\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      : "+v"(w), "=&s"(p0), "=&s"(p1), "=&s"(p2)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(thr));
+}
+
+// w = (w << 8) | bits, bit j = [ v[j] >= 0 ] (true for -0), j = 0..7.
+__device__ __forceinline__ void push8_nonneg(uint32_t& w, const float* v) {
+  uint64_t p0, p1, p2;
+  asm(
+      "v_cmp_le_f32_e64 %1, 0, %11\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %10\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %9\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %8\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %7\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_cmp_le_f32_e64 %3, 0, %6\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_cmp_le_f32_e64 %1, 0, %5\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_cmp_le_f32_e64 %2, 0, %4\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %3\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      : "+v"(w), "=&s"(p0), "=&s"(p1), "=&s"(p2)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+}
+
+// ----------------------------------------------------------------------------
+// Matrix-core transform of 32-element runs (bf16 input).
+//
+// v_mfma_f32_16x16x32_bf16 computes D = A B for a 16 x 32 A, a 32 x 16 B and
+// a 16 x 16 fp32 D.  Lane l = 16 g + n holds B[8 g + e][n] (e = 0..7, eight
+// consecutive bf16 of one 16-byte load), A[n][8 g + e] and D[4 g + i][n]
+// (i = 0..3).  Taking column n of B to be run n of a group of 16 runs and A
+// to be 16 rows of the +-1 Sylvester matrix H_32, one instruction applies
+// half of H_32 to 16 runs; two (row sets m = 0, 1) give all 32 outputs.  The
+// rows are permuted so that lane (g, n) ends with outputs 8 g .. 8 g + 7 of
+// run n, in order: row 4 g + i of row set m is Hadamard row 8 g + 4 m + i.
+// Loads of the group (lane (g, n) reads 16 bytes at 64 n + 16 g) cover one
+// contiguous kilobyte per instruction.  Products of bf16 values by +-1 are
+// exact; the sums are accumulated in fp32.
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The A operand of row set m for this lane: entries (-1)^popcount(r & k) of
+// Hadamard row r = 8 (n / 4) + 4 m + n % 4, columns k = 8 g .. 8 g + 7.
+__device__ __forceinline__ bf16x8_t hadamard_fragment(int lane, int m) {
+  const int n = lane & 15, g = lane >> 4;
+  const int r = 8 * (n >> 2) + 4 * m + (n & 3);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const uint32_t lo = 0x3F80u | ((static_cast<uint32_t>(__builtin_popcount(r & (8 * g + e))) & 1u) << 15);
+    const uint32_t hi = 0x3F80u | ((static_cast<uint32_t>(__builtin_popcount(r & (8 * g + e + 1))) & 1u) << 15);
+    w[e / 2] = lo | (hi << 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+// Outputs 8 g .. 8 g + 7 of the lane's run of a 16-run group held in `f`
+// (the lane's 16-byte B fragment), written to v[0..7].
+__device__ __forceinline__ void mfma_run_outputs(const bf16x8_t& h0, const bf16x8_t& h1, const u32x4& f, float* v) {
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, f);
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, b, zero, 0, 0, 0);
+  const f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, b, zero, 0, 0, 0);
+  v[0] = d0.x;
+  v[1] = d0.y;
+  v[2] = d0.z;
+  v[3] = d0.w;
+  v[4] = d1.x;
+  v[5] = d1.y;
+  v[6] = d1.z;
+  v[7] = d1.w;
+}
+
+// Sum of squares of the eight bf16 values of a fragment.  The dwords are
+// copied out before the bit casts: __builtin_bit_cast applied directly to an
+// element of an ext_vector_type value has been seen to read element 0 for
+// every element.
+__device__ __forceinline__ float sum_squares_fragment(const u32x4& f) {
+  const uint32_t fx = f.x, fy = f.y, fz = f.z, fw = f.w;
+  const bf16x2_t a = __builtin_bit_cast(bf16x2_t, fx), b = __builtin_bit_cast(bf16x2_t, fy);
+  const bf16x2_t c = __builtin_bit_cast(bf16x2_t, fz), d = __builtin_bit_cast(bf16x2_t, fw);
+  const float s0 = __builtin_amdgcn_fdot2_f32_bf16(b, b, __builtin_amdgcn_fdot2_f32_bf16(a, a, 0.f, false), false);
+  const float s1 = __builtin_amdgcn_fdot2_f32_bf16(d, d, __builtin_amdgcn_fdot2_f32_bf16(c, c, 0.f, false), false);
+  return s0 + s1;
+}
+
+// 4 x 4 transpose between lane quarters (g = lane / 16) and slots: afterwards
+// slot j of quarter g holds what slot g of quarter j held (same lane within
+// the quarter).  v_permlane32_swap exchanges the upper half-wave of its first
+// operand with the lower half-wave of its second; v_permlane16_swap the odd
+// 16-lane rows of its first operand with the even rows of its second.
+__device__ __forceinline__ void transpose_quarters(uint32_t (&x)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x[0] = c[0];
+  x[1] = c[1];
+  x[2] = d[0];
+  x[3] = d[1];
 }
 
 // ----------------------------------------------------------------------------

@@ -103,6 +103,48 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
   return cw;
 }
 
+// Quantise 8 transformed values (a quarter run) into b-bit codes packed
+// LSB-first into the low 8 b bits of the result: the same arithmetic as
+// quantise_run, on 8 entries.
+template <int B>
+__device__ __forceinline__ uint32_t quantise8(const float* v, float kk) {
+  constexpr float L = static_cast<float>(1 << B);
+  if constexpr (B == 1) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = v[j] * kk;
+    uint32_t w = 0u;
+    push8_nonneg(w, p);
+    return w;
+  } else if constexpr (B == 2 || B == 4) {
+    constexpr int PER_BYTE = 8 / B;
+    const float off = 0.5f * (L - 1.f);
+    uint32_t acc[PER_BYTE];
+#pragma unroll
+    for (int j = 0; j < PER_BYTE; ++j) acc[j] = 0u;
+#pragma unroll
+    for (int k = 0; k < 8 / PER_BYTE; ++k) {
+#pragma unroll
+      for (int j = 0; j < PER_BYTE; ++j) {
+        const float t = __builtin_fminf(__builtin_fmaf(v[k * PER_BYTE + j], kk, off), L - 1.f);
+        acc[j] = __builtin_amdgcn_cvt_pk_u8_f32(t, k, acc[j]);
+      }
+    }
+    uint32_t w = acc[0];
+#pragma unroll
+    for (int j = 1; j < PER_BYTE; ++j) w |= acc[j] << (B * j);
+    return w;
+  } else {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[j], kk, 0.5f * L), 0.f, L - 1.f);
+      w |= static_cast<uint32_t>(t) << (3 * j);
+    }
+    return w;
+  }
+}
+
 // Transform one run per lane: returns tau and the lane's share of the row's
 // sum of squares.  The row's RMS is taken from the inputs: the orthonormal
 // transform keeps the sum of squares (Parseval), so it equals the RMS of the
@@ -198,6 +240,125 @@ __global__ void __launch_bounds__(256)
     tile += stride;
     if (tile >= tiles) break;
     wave_fetch<U>(x, (tile + 2 * stride) * 64 * U, total_pieces, lane, b);
+    process(tile, c);
+    tile += stride;
+    if (tile >= tiles) break;
+  }
+}
+
+// bf16 rows of 16, 32 or 64 runs (512, 1024 or 2048 columns) on the matrix
+// cores.  A wave's tile is 64 runs (64 / 2^LOGR whole rows) held as four
+// 16-run groups: slot j of lane (g, n) holds outputs 8 g .. 8 g + 7 of run
+// 16 j + n (H_32 applied by the MFMA), then the cross-lane stages finish the
+// block (runs of one block are neighbouring n).  Codes and mask bits are
+// packed per slot (8 entries) and a transpose between lane quarters and
+// slots hands lane l all four quarters of run l, which it stores as in the
+// run-per-lane kernels.  Loads run two tiles ahead of the arithmetic.
+template <int LOGN, int B, int LOGR>
+__global__ void __launch_bounds__(256)
+    quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
+                          uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask) {
+  static_assert(LOGR >= 4 && LOGR <= 6, "16, 32 or 64 runs per row");
+  constexpr int ROWS = 64 >> LOGR;  // rows per tile
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t rows = total_runs >> LOGR;
+  const int64_t tiles = (total_runs + 63) >> 6;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (tile >= tiles) return;
+  const bf16x8_t h0 = hadamard_fragment(lane, 0);
+  const bf16x8_t h1 = hadamard_fragment(lane, 1);
+  const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
+  const int scale_off = lane < ROWS ? lane * 4 : kNowhere;
+
+  auto fetch = [&](int64_t t, u32x4 (&f)[4]) {
+    const rsrc_t r = window_at(x, t * 4096, total_runs * 64, 4096);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(r, in_off + 1024 * j, 0, kNonTemporal);
+  };
+
+  auto process = [&](int64_t t, const u32x4 (&f)[4]) {
+    float v[RUN];
+    float part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mfma_run_outputs(h0, h1, f[j], v + 8 * j);
+      part[j] = sum_squares_fragment(f[j]);
+    }
+    // Row sums of squares: slot j belongs to row j / (4 / ROWS) of the tile.
+    float ss[ROWS];
+    if constexpr (ROWS == 1) {
+      ss[0] = group_sum((part[0] + part[1]) + (part[2] + part[3]), 6);
+    } else if constexpr (ROWS == 2) {
+      ss[0] = group_sum(part[0] + part[1], 6);
+      ss[1] = group_sum(part[2] + part[3], 6);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss[j] = group_sum(part[j], 6);
+    }
+    const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
+    float kk[ROWS], thr[ROWS], sc[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const float ms = ss[r] * k.inv_cols;
+      const float rms = __builtin_amdgcn_sqrtf(ms);
+      sc[r] = k.alpha * rms;
+      // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
+      kk[r] = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
+      thr[r] = k.thr * rms;
+    }
+    uint32_t cp[4], mp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      constexpr int SLOTS_PER_ROW = 4 / ROWS;
+      cp[j] = quantise8<B>(v + 8 * j, kk[j / SLOTS_PER_ROW]);
+      mp[j] = 0u;
+      push8_abs_le(mp[j], v + 8 * j, thr[j / SLOTS_PER_ROW]);
+    }
+    transpose_quarters(cp);
+    transpose_quarters(mp);
+    CodeWords<B> cw;
+    if constexpr (B == 1) {
+      cw.w[0] = cp[0] | (cp[1] << 8) | (cp[2] << 16) | (cp[3] << 24);
+    } else if constexpr (B == 2) {
+      cw.w[0] = cp[0] | (cp[1] << 16);
+      cw.w[1] = cp[2] | (cp[3] << 16);
+    } else if constexpr (B == 3) {
+      cw.w[0] = cp[0] | (cp[1] << 24);
+      cw.w[1] = (cp[1] >> 8) | (cp[2] << 16);
+      cw.w[2] = (cp[2] >> 16) | (cp[3] << 8);
+    } else {
+      cw.w[0] = cp[0];
+      cw.w[1] = cp[1];
+      cw.w[2] = cp[2];
+      cw.w[3] = cp[3];
+    }
+    const uint32_t mw = mp[0] | (mp[1] << 8) | (mp[2] << 16) | (mp[3] << 24);
+    float my_scale = sc[0];
+#pragma unroll
+    for (int r = 1; r < ROWS; ++r) my_scale = lane == r ? sc[r] : my_scale;
+    const int64_t run0 = t * 64;
+    store_codes<B>(window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B), lane, cw);
+    __builtin_amdgcn_raw_buffer_store_b32(mw, window_at(mask, run0 * 4, total_runs * 4, 64 * 4), lane * 4, 0,
+                                          kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale),
+                                          window_at(scale, t * ROWS * 4, rows * 4, ROWS * 4), scale_off, 0, 0);
+  };
+
+  u32x4 a[4], b[4], c[4];
+  fetch(tile, a);
+  fetch(tile + stride, b);
+  for (;;) {
+    fetch(tile + 2 * stride, c);
+    process(tile, a);
+    tile += stride;
+    if (tile >= tiles) break;
+    fetch(tile + 2 * stride, a);
+    process(tile, b);
+    tile += stride;
+    if (tile >= tiles) break;
+    fetch(tile + 2 * stride, b);
     process(tile, c);
     tile += stride;
     if (tile >= tiles) break;
@@ -345,6 +506,25 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, u
   k.thr = static_cast<float>(alpha * L * sqrt_n / (L - 1.0));
   k.inv_cols = static_cast<float>(1.0 / double(cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
+  if constexpr (sizeof(In) == 2) {
+    if (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64) {
+      const int64_t total_runs = rows * runs_per_row;
+      const int64_t tiles = (total_runs + 63) / 64;
+      int64_t wgs = (tiles + 3) / 4;
+      if (wgs > kFwdTileWorkgroups) wgs = kFwdTileWorkgroups;
+      const dim3 grid(static_cast<uint32_t>(wgs));
+      if (runs_per_row == 16)
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 4>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
+                           scale, mask32);
+      else if (runs_per_row == 32)
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 5>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
+                           scale, mask32);
+      else
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 6>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
+                           scale, mask32);
+      return hipGetLastError();
+    }
+  }
   if (runs_per_row <= 64 && (runs_per_row & (runs_per_row - 1)) == 0) {
     const int64_t total_runs = rows * runs_per_row;
     const int64_t tiles = (total_runs + 63) / 64;
