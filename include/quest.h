@@ -102,9 +102,13 @@ double quest_fit_alpha(int b);
  *   scale   device output, rows floats (s_r)
  *   mask    device output, quest_mask_bytes(rows, cols) bytes
  * Pointers must be 16-byte aligned.  No output may overlap x or another
- * output (QUEST_EINVAL).  The transform and the reduction run in fp32; an
+ * output (QUEST_EINVAL).  rows * cols must stay below 2^36
+ * (QUEST_EUNSUPPORTED).  The transform and the reduction run in fp32; an
  * entry within about 1e-6 * s_r of a decision or trust threshold may round
  * to the neighbouring outcome of the exact (fp64) definition.
+ * bf16 rows of 512, 1024 or 2048 columns take the 32-point transforms on the
+ * matrix cores; setting the environment variable QUEST_FWD_KERNEL=valu
+ * before the first call keeps them on the vector ALUs (timing comparisons).
  */
 quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
                                 int b, uint8_t* codes, float* scale, uint8_t* mask, void* stream);

@@ -2,6 +2,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <cstdint>
 #include <limits>
 #include <mutex>
@@ -70,6 +72,17 @@ std::once_flag g_alpha_once;
 
 void fill_alpha_table() {
   for (int b = 1; b <= kMaxBits; ++b) g_alpha[b] = solve_alpha(b);
+}
+
+// Forward kernel selection, read once per process: QUEST_FWD_KERNEL=valu keeps
+// bf16 rows of 512..2048 columns on the vector-ALU transform instead of the
+// matrix cores (same results up to fp32 rounding order; for A/B timing).
+std::once_flag g_env_once;
+bool g_allow_mfma = true;
+
+void read_env() {
+  const char* v = std::getenv("QUEST_FWD_KERNEL");
+  g_allow_mfma = !(v && std::strcmp(v, "valu") == 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -160,8 +173,9 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
       overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm))
     return QUEST_EINVAL;
   const double alpha = quest_fit_alpha(b);
-  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, codes, scale, mask,
-                                             static_cast<hipStream_t>(stream)));
+  std::call_once(g_env_once, read_env);
+  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, g_allow_mfma, codes,
+                                             scale, mask, static_cast<hipStream_t>(stream)));
 }
 
 quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,

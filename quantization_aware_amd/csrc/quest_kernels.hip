@@ -496,8 +496,8 @@ int log2_exact(int v) {
 constexpr int64_t kFwdTileWorkgroups = 512;
 
 template <typename In, int LOGN, int B>
-hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, uint8_t* codes, float* scale,
-                        uint8_t* mask, hipStream_t stream) {
+hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, bool allow_mfma, uint8_t* codes,
+                        float* scale, uint8_t* mask, hipStream_t stream) {
   const int runs_per_row = static_cast<int>(cols / RUN);
   const double L = double(1 << B), sqrt_n = std::sqrt(double(1 << LOGN));
   FwdConsts k;
@@ -507,7 +507,7 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, u
   k.inv_cols = static_cast<float>(1.0 / double(cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
   if constexpr (sizeof(In) == 2) {
-    if (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64) {
+    if (allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
       const int64_t total_runs = rows * runs_per_row;
       const int64_t tiles = (total_runs + 63) / 64;
       int64_t wgs = (tiles + 3) / 4;
@@ -547,23 +547,23 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, u
 }
 
 template <typename In, int LOGN>
-hipError_t fwd_dispatch_bits(const In* x, int64_t rows, int64_t cols, int bits, double alpha, uint8_t* codes,
-                             float* scale, uint8_t* mask, hipStream_t stream) {
+hipError_t fwd_dispatch_bits(const In* x, int64_t rows, int64_t cols, int bits, double alpha, bool allow_mfma,
+                             uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
   switch (bits) {
-    case 1: return fwd_dispatch<In, LOGN, 1>(x, rows, cols, alpha, codes, scale, mask, stream);
-    case 2: return fwd_dispatch<In, LOGN, 2>(x, rows, cols, alpha, codes, scale, mask, stream);
-    case 3: return fwd_dispatch<In, LOGN, 3>(x, rows, cols, alpha, codes, scale, mask, stream);
-    default: return fwd_dispatch<In, LOGN, 4>(x, rows, cols, alpha, codes, scale, mask, stream);
+    case 1: return fwd_dispatch<In, LOGN, 1>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
+    case 2: return fwd_dispatch<In, LOGN, 2>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
+    case 3: return fwd_dispatch<In, LOGN, 3>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
+    default: return fwd_dispatch<In, LOGN, 4>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
   }
 }
 
 template <typename In>
 hipError_t fwd_dispatch_block(const In* x, int64_t rows, int64_t cols, int log_block, int bits, double alpha,
-                              uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
+                              bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
   switch (log_block) {
-    case 6: return fwd_dispatch_bits<In, 6>(x, rows, cols, bits, alpha, codes, scale, mask, stream);
-    case 7: return fwd_dispatch_bits<In, 7>(x, rows, cols, bits, alpha, codes, scale, mask, stream);
-    default: return fwd_dispatch_bits<In, 8>(x, rows, cols, bits, alpha, codes, scale, mask, stream);
+    case 6: return fwd_dispatch_bits<In, 6>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
+    case 7: return fwd_dispatch_bits<In, 7>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
+    default: return fwd_dispatch_bits<In, 8>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
   }
 }
 
@@ -620,12 +620,13 @@ hipError_t dequant_dispatch(const uint8_t* codes, const float* scale, int64_t ro
 }  // namespace
 
 hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
-                               double alpha, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
+                               double alpha, bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask,
+                               hipStream_t stream) {
   if (x_is_bf16)
-    return fwd_dispatch_block(static_cast<const uint16_t*>(x), rows, cols, log_block, bits, alpha, codes, scale, mask,
-                              stream);
-  return fwd_dispatch_block(static_cast<const float*>(x), rows, cols, log_block, bits, alpha, codes, scale, mask,
-                            stream);
+    return fwd_dispatch_block(static_cast<const uint16_t*>(x), rows, cols, log_block, bits, alpha, allow_mfma, codes,
+                              scale, mask, stream);
+  return fwd_dispatch_block(static_cast<const float*>(x), rows, cols, log_block, bits, alpha, allow_mfma, codes, scale,
+                            mask, stream);
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,

@@ -197,11 +197,19 @@ SHAPES = [
     (257, 2048, 64, "bf16"),
     (70, 2048, 256, "f32"),
     (300, 768, 256, "bf16"),  # 24 runs per row
+    # bf16 rows of 16, 32 and 64 runs go to the matrix-core transform: every
+    # block size, ragged last tiles (tiles hold 2048 elements).
+    (5, 512, 64, "bf16"),
+    (3, 512, 256, "bf16"),
+    (77, 1024, 128, "bf16"),
+    (2, 1024, 64, "bf16"),
+    (1, 2048, 128, "bf16"),
+    (31, 2048, 256, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("rows,cols,block,dt", SHAPES)
-@pytest.mark.parametrize("b", [1, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
 def test_shapes_fwd(dev, rows, cols, block, dt, b):
     spec = TensorSpec(f"shape{rows}x{cols}", rows, cols, dt, "student_t", 4, 7000 + rows + cols + block,
                       outlier_cols=max(1, cols // 100), outlier_scale=20.0)
@@ -353,3 +361,49 @@ def test_binding_rejects_misaligned_view(dev):
         qa.quantize_fwd(y, 128, 4)
     assert e.value.status == qa.QUEST_EALIGN
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# The vector-ALU transform on the shapes the matrix cores normally take
+# (QUEST_FWD_KERNEL=valu is read once per process, so it runs in a child).
+# ---------------------------------------------------------------------------
+_VALU_CHILD = r"""
+import sys
+import numpy as np
+import torch
+sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
+import quantization_aware_amd as qa
+from quest_inputs import TensorSpec, make_tensor
+dev = torch.device("cuda", 0)
+spec = TensorSpec("valu", 96, int(sys.argv[2]), "bf16", "student_t", 4, 8100, outlier_cols=20, outlier_scale=20.0)
+x = make_tensor(spec, dev)
+codes, scale, mask = qa.quantize_fwd(x, int(sys.argv[3]), int(sys.argv[4]))
+torch.cuda.synchronize()
+np.savez(sys.argv[5], codes=codes.cpu().numpy(), scale=scale.cpu().numpy(), mask=mask.cpu().numpy())
+"""
+
+
+@pytest.mark.parametrize("cols,block,b", [(2048, 128, 4), (512, 64, 1)])
+def test_valu_switch_matches_oracle_and_mfma(dev, tmp_path, cols, block, b):
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = tmp_path / "valu.npz"
+    env = dict(os.environ, QUEST_FWD_KERNEL="valu")
+    log(f"vector-ALU forward in a child process, 96x{cols} bf16 block {block} b={b}")
+    subprocess.run([sys.executable, "-c", _VALU_CHILD, root, str(cols), str(block), str(b), str(out)],
+                   env=env, check=True, timeout=300)
+    got = np.load(out)
+    spec = TensorSpec("valu", 96, cols, "bf16", "student_t", 4, 8100, outlier_cols=20, outlier_scale=20.0)
+    x = make_tensor(spec, dev)
+    x64 = to_float64(x)
+    ref = qo.quantize_fwd(x64, block, b)
+    check_fwd(x64, block, b, got["codes"], got["scale"], got["mask"], ref=ref)
+    codes, scale, mask = fwd_gpu(x, block, b)
+    check_fwd(x64, block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), ref=ref)
+    ex = exempt_entries(ref["y"], ref["scale"], b)
+    u_valu = qo.unpack_lsb_first(got["codes"], b, cols)
+    u_mfma = qo.unpack_lsb_first(codes.cpu().numpy(), b, cols)
+    assert np.array_equal(u_valu[~ex], u_mfma[~ex])
