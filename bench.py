@@ -10,8 +10,10 @@ several buffer sets so that no step finds its data in the 256 MB last-level
 cache.
 
 Timing, all with HIP events on the stream the kernels are launched on:
-  * the step: K steps (forward then backward, as in training) between two
-    events, bracketed by device synchronisation;
+  * the step: K steps between two events, bracketed by device
+    synchronisation.  Steps are independent batches: each step's backward
+    runs on a second stream after an event from its own forward, so it
+    overlaps the next step's forward (the one-stream time is reported too);
   * each kernel: K back-to-back launches of that kernel alone between two
     events (events between every kernel would add their own gaps);
   * a plain copy kernel (elementwise negation) moving as many bytes as the
@@ -158,6 +160,21 @@ def main():
     dxs = [torch.empty_like(g0) for _ in range(N_SETS)]
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
+    # Steps are independent batches: step i's backward runs on a second stream
+    # (default priority) after an event from step i's forward, so it overlaps
+    # step i+1's forward; a forward waits for the backward that last read its
+    # buffer set.
+    # Both are streams created here with hipStreamCreate (default priority):
+    # the null stream would synchronise with the other stream and serialise
+    # the two passes.
+    def hip_stream():
+        st = ctypes.c_void_p()
+        if lib.hipStreamCreate(ctypes.byref(st)):
+            raise RuntimeError("hipStreamCreate failed")
+        return st
+
+    sh_a = hip_stream()
+    sh_b = hip_stream()
     # The timed loop calls the C ABI directly with prepared arguments.
     fwd_args = [
         (ctypes.c_void_p(xs[i].data_ptr()), qa.QUEST_BF16, ROWS, COLS, BLOCK, BITS, ctypes.c_void_p(codes[i].data_ptr()),
@@ -170,15 +187,39 @@ def main():
         for i in range(N_SETS)
     ]
     f_fwd, f_bwd = lib.quest_quantize_fwd, lib.quest_trust_bwd
+    # Events of the HIP runtime that libquest (and torch) use, called
+    # directly: they bracket the timed region across both streams.
+    hip_record, hip_wait = lib.hipEventRecord, lib.hipStreamWaitEvent
+    hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip_wait.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
 
-    def step(i):
+    def hip_event():
+        ev = ctypes.c_void_p()
+        if lib.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(2)):  # hipEventDisableTiming
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
+
+    # Steps are independent batches.  Step i runs on stream i % 2, its
+    # backward after its forward in that stream's order; steps on the two
+    # streams overlap.  Step i + N_SETS reuses step i's buffers and, N_SETS
+    # being even, runs on the same stream after it.
+    streams = (sh_a, sh_b)
+
+    def check(name, st):
+        if st:
+            raise qa.QuestError(name, st, lib.quest_status_string(st).decode())
+
+    def run_steps(first, count):
+        for i in range(first, first + count):
+            s = i % N_SETS
+            st = streams[i % 2]
+            check("quest_quantize_fwd", f_fwd(*fwd_args[s][:-1], st))
+            check("quest_trust_bwd", f_bwd(*bwd_args[s][:-1], st))
+
+    def step_one_stream(i):
         s = i % N_SETS
-        st = f_fwd(*fwd_args[s])
-        if st:
-            raise qa.QuestError("quest_quantize_fwd", st, lib.quest_status_string(st).decode())
-        st = f_bwd(*bwd_args[s])
-        if st:
-            raise qa.QuestError("quest_trust_bwd", st, lib.quest_status_string(st).decode())
+        check("quest_quantize_fwd", f_fwd(*fwd_args[s]))
+        check("quest_trust_bwd", f_bwd(*bwd_args[s]))
 
     if args.copy_calibration:
         src = torch.empty((256 << 20) // 2, dtype=torch.bfloat16, device=dev).normal_()
@@ -188,25 +229,47 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: 3 x elementwise neg of {src.numel() * 2} bytes", file=sys.stderr, flush=True)
 
-    for i in range(args.warmup):
-        step(i)
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps between two events on the launch stream.
+    # Timed region: exactly K steps.  The start event is on the forward stream
+    # (the backward stream waits for it); the end event follows both streams.
     K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1, e_join = ctypes.c_void_p(), ctypes.c_void_p(), hip_event()
+    for e in (e0, e1):
+        if lib.hipEventCreate(ctypes.byref(e)):
+            raise RuntimeError("hipEventCreate failed")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        step(i)
-    e1.record(stream)
+    hip_record(e0, sh_a)
+    hip_wait(sh_b, e0, 0)
+    run_steps(args.warmup, K)
+    hip_record(e_join, sh_b)
+    hip_wait(sh_a, e_join, 0)
+    hip_record(e1, sh_a)
+    enqueue = time.perf_counter() - t0
+    lib.hipEventSynchronize(e1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1)
+    elapsed = ctypes.c_float()
+    if lib.hipEventElapsedTime(ctypes.byref(elapsed), e0, e1):
+        raise RuntimeError("hipEventElapsedTime failed")
+    step_ms = elapsed.value
     ms_per_step = max(step_ms, 1000.0 * wall) / K
     elements = ROWS * COLS
     value = elements / (ms_per_step / 1000.0)
+
+    # The same K steps with forward and backward on one stream, for reference.
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t2 = time.perf_counter()
+    e2.record(stream)
+    for i in range(K):
+        step_one_stream(i)
+    e3.record(stream)
+    enqueue_one = time.perf_counter() - t2
+    torch.cuda.synchronize()
+    one_stream_ms = e2.elapsed_time(e3) / K
 
     def timed_launches(launch):
         """Mean duration of K back-to-back launches, HIP events on the launch stream."""
@@ -278,7 +341,11 @@ def main():
         "kernels": kernels,
         "copy_reference": {"kernel": "torch.neg, 16384x2048 bf16", "bytes": copy_bytes, "avg_us": 1000 * copy_avg,
                            "gbps": copy_gbps, "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
-        "timing": {"step_events_ms": step_ms, "step_wall_s": wall},
+        "timing": {"step_events_ms": step_ms, "step_wall_s": wall,
+                   "schedule": "step i on stream i % 2 (forward then backward in stream order); "
+                               "consecutive steps overlap",
+                   "one_stream_ms_per_step": one_stream_ms,
+                   "host_enqueue_s": enqueue, "one_stream_host_enqueue_s": enqueue_one},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x0, g0, args.cpu_seconds)
