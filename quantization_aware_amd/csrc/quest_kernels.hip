@@ -246,6 +246,63 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Codes and mask of a wave's four 16-run groups after the matrix-core
+// transform: v[8 j .. 8 j + 7] of lane (g, n) are outputs 8 g .. 8 g + 7 of
+// run 16 j + n, quantised with kk[j] and tested against thr[j].  Codes and
+// mask bits are packed per slot (8 entries); a transpose between lane
+// quarters and slots then hands lane l all four quarters of run l, stored at
+// run l of the windows `codes_r` (4 B bytes per run) and `mask_r` (a dword
+// per run).
+template <int B>
+__device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const float (&kk)[4],
+                                                    const float (&thr)[4], int lane, rsrc_t codes_r, rsrc_t mask_r) {
+  uint32_t cp[4], mp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cp[j] = quantise8<B>(v + 8 * j, kk[j]);
+    mp[j] = 0u;
+    push8_abs_le(mp[j], v + 8 * j, thr[j]);
+  }
+  transpose_quarters(cp);
+  transpose_quarters(mp);
+  CodeWords<B> cw;
+  if constexpr (B == 1) {
+    cw.w[0] = cp[0] | (cp[1] << 8) | (cp[2] << 16) | (cp[3] << 24);
+  } else if constexpr (B == 2) {
+    cw.w[0] = cp[0] | (cp[1] << 16);
+    cw.w[1] = cp[2] | (cp[3] << 16);
+  } else if constexpr (B == 3) {
+    cw.w[0] = cp[0] | (cp[1] << 24);
+    cw.w[1] = (cp[1] >> 8) | (cp[2] << 16);
+    cw.w[2] = (cp[2] >> 16) | (cp[3] << 8);
+  } else {
+    cw.w[0] = cp[0];
+    cw.w[1] = cp[1];
+    cw.w[2] = cp[2];
+    cw.w[3] = cp[3];
+  }
+  const uint32_t mw = mp[0] | (mp[1] << 8) | (mp[2] << 16) | (mp[3] << 24);
+  store_codes<B>(codes_r, lane, cw);
+  __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, kNonTemporal);
+}
+
+// Per-row constants from a row's sum of squares: the scale s = alpha RMS, the
+// code factor kk (times this lane's sign tau) and the trust threshold on v.
+struct RowConsts {
+  float scale, kk, thr;
+};
+
+__device__ __forceinline__ RowConsts row_consts(float ss, float tau, const FwdConsts& k) {
+  const float ms = ss * k.inv_cols;
+  const float rms = __builtin_amdgcn_sqrtf(ms);
+  RowConsts c;
+  c.scale = k.alpha * rms;
+  // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
+  c.kk = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
+  c.thr = k.thr * rms;
+  return c;
+}
+
 // bf16 rows of 16, 32 or 64 runs (512, 1024 or 2048 columns) on the matrix
 // cores.  A wave's tile is 64 runs (64 / 2^LOGR whole rows) held as four
 // 16-run groups: slot j of lane (g, n) holds outputs 8 g .. 8 g + 7 of run
@@ -298,50 +355,23 @@ __global__ void __launch_bounds__(256)
       for (int j = 0; j < 4; ++j) ss[j] = group_sum(part[j], 6);
     }
     const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
-    float kk[ROWS], thr[ROWS], sc[ROWS];
+    float kk[4], thr[4], sc[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      const float ms = ss[r] * k.inv_cols;
-      const float rms = __builtin_amdgcn_sqrtf(ms);
-      sc[r] = k.alpha * rms;
-      // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
-      kk[r] = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
-      thr[r] = k.thr * rms;
-    }
-    uint32_t cp[4], mp[4];
+      const RowConsts c = row_consts(ss[r], tau, k);
+      sc[r] = c.scale;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      constexpr int SLOTS_PER_ROW = 4 / ROWS;
-      cp[j] = quantise8<B>(v + 8 * j, kk[j / SLOTS_PER_ROW]);
-      mp[j] = 0u;
-      push8_abs_le(mp[j], v + 8 * j, thr[j / SLOTS_PER_ROW]);
+      for (int j = r * (4 / ROWS); j < (r + 1) * (4 / ROWS); ++j) {
+        kk[j] = c.kk;
+        thr[j] = c.thr;
+      }
     }
-    transpose_quarters(cp);
-    transpose_quarters(mp);
-    CodeWords<B> cw;
-    if constexpr (B == 1) {
-      cw.w[0] = cp[0] | (cp[1] << 8) | (cp[2] << 16) | (cp[3] << 24);
-    } else if constexpr (B == 2) {
-      cw.w[0] = cp[0] | (cp[1] << 16);
-      cw.w[1] = cp[2] | (cp[3] << 16);
-    } else if constexpr (B == 3) {
-      cw.w[0] = cp[0] | (cp[1] << 24);
-      cw.w[1] = (cp[1] >> 8) | (cp[2] << 16);
-      cw.w[2] = (cp[2] >> 16) | (cp[3] << 8);
-    } else {
-      cw.w[0] = cp[0];
-      cw.w[1] = cp[1];
-      cw.w[2] = cp[2];
-      cw.w[3] = cp[3];
-    }
-    const uint32_t mw = mp[0] | (mp[1] << 8) | (mp[2] << 16) | (mp[3] << 24);
+    const int64_t run0 = t * 64;
+    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B),
+                           window_at(mask, run0 * 4, total_runs * 4, 64 * 4));
     float my_scale = sc[0];
 #pragma unroll
     for (int r = 1; r < ROWS; ++r) my_scale = lane == r ? sc[r] : my_scale;
-    const int64_t run0 = t * 64;
-    store_codes<B>(window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B), lane, cw);
-    __builtin_amdgcn_raw_buffer_store_b32(mw, window_at(mask, run0 * 4, total_runs * 4, 64 * 4), lane * 4, 0,
-                                          kNonTemporal);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale),
                                           window_at(scale, t * ROWS * 4, rows * 4, ROWS * 4), scale_off, 0, 0);
   };
@@ -363,6 +393,88 @@ __global__ void __launch_bounds__(256)
     tile += stride;
     if (tile >= tiles) break;
   }
+}
+
+// bf16 rows of 16 m runs (m > 4: more than 2048 columns, a multiple of 512)
+// on the matrix cores.  A workgroup holds rows_per_wg whole rows; wave w
+// takes runs 64 w .. 64 w + 63 of the workgroup as four 16-run groups, each
+// inside one row, transformed and quantised as in quest_fwd_mfma_kernel.
+// Each group's sum of squares goes to LDS; after a barrier every wave adds
+// up the groups of its rows in a fixed order.  Groups past the workgroup's
+// rows (when rows_per_wg * runs_per_row is not a multiple of 64) read zeros
+// and their stores fall outside the workgroup's windows.  One workgroup per
+// block of rows (no grid-stride loop): with a barrier per block, letting the
+// hardware refill compute units as workgroups finish hides latency better
+// than a resident loop.
+template <int LOGN, int B>
+__global__ void __launch_bounds__(1024)
+    quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
+                               FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
+                               uint32_t* __restrict__ mask) {
+  __shared__ float group_ss[64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t total_runs = rows * runs_per_row;
+  const uint32_t wg_runs = static_cast<uint32_t>(rows_per_wg * runs_per_row);
+  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * wg_runs;
+  const int groups_per_row = runs_per_row >> 4;
+  const bf16x8_t h0 = hadamard_fragment(lane, 0);
+  const bf16x8_t h1 = hadamard_fragment(lane, 1);
+
+  const rsrc_t in_r = window_at(x, wg_first_run * 64, total_runs * 64, wg_runs * 64);
+  const int in_off = wave * 4096 + 64 * (lane & 15) + 16 * (lane >> 4);
+  u32x4 f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(in_r, in_off + 1024 * j, 0, kNonTemporal);
+
+  float v[RUN];
+  float part[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mfma_run_outputs(h0, h1, f[j], v + 8 * j);
+    part[j] = group_sum(sum_squares_fragment(f[j]), 6);
+  }
+  if (lane < 4) group_ss[4 * wave + lane] = lane == 0 ? part[0] : lane == 1 ? part[1] : lane == 2 ? part[2] : part[3];
+  const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
+  __syncthreads();
+
+  // Row of each slot (wave-uniform); a wave's 64 runs touch at most two rows.
+  const int row_a = (4 * wave) / groups_per_row;
+  const int row_b = (4 * wave + 3) / groups_per_row;
+  float ss_a = 0.f, ss_b = 0.f;
+  if (row_a < rows_per_wg) {
+    const float* g = group_ss + row_a * groups_per_row;
+    for (int i = 0; i < groups_per_row; ++i) ss_a += g[i];
+  }
+  if (row_b != row_a && row_b < rows_per_wg) {
+    const float* g = group_ss + row_b * groups_per_row;
+    for (int i = 0; i < groups_per_row; ++i) ss_b += g[i];
+  } else {
+    ss_b = ss_a;
+  }
+  const RowConsts ca = row_consts(ss_a, tau, k);
+  const RowConsts cb = row_consts(ss_b, tau, k);
+  float kk[4], thr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool in_a = (4 * wave + j) / groups_per_row == row_a;
+    kk[j] = in_a ? ca.kk : cb.kk;
+    thr[j] = in_a ? ca.thr : cb.thr;
+  }
+  // The wave's windows end where the workgroup's rows end: runs past them
+  // belong to the next workgroup.
+  const int64_t run0 = wg_first_run + 64 * wave;
+  const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
+  mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, run_end * 4 * B, 64 * 4 * B),
+                         window_at(mask, run0 * 4, run_end * 4, 64 * 4));
+  // Slot j stores its row's scale when it holds the row's first group.
+  const int my_group = 4 * wave + (lane & 3);
+  const int my_row = my_group / groups_per_row;
+  const bool first = lane < 4 && my_group % groups_per_row == 0 && my_row < rows_per_wg;
+  const float my_scale = my_row == row_a ? ca.scale : cb.scale;
+  const rsrc_t scale_r =
+      window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), scale_r, first ? my_row * 4 : kNowhere, 0, 0);
 }
 
 // Rows that span several wavefronts (or whose run count is not a power of
@@ -507,6 +619,16 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, b
   k.inv_cols = static_cast<float>(1.0 / double(cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
   if constexpr (sizeof(In) == 2) {
+    if (allow_mfma && runs_per_row > 64 && runs_per_row % 16 == 0) {
+      int rows_per_wg = 64 / gcd_int(runs_per_row, 64);
+      if (rows_per_wg * runs_per_row > 1024) rows_per_wg = 1024 / runs_per_row;
+      if (rows_per_wg < 1) rows_per_wg = 1;
+      const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
+      const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+      hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
+                         stream, x, rows, runs_per_row, rows_per_wg, k, codes, scale, mask32);
+      return hipGetLastError();
+    }
     if (allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
       const int64_t total_runs = rows * runs_per_row;
       const int64_t tiles = (total_runs + 63) / 64;

@@ -205,6 +205,12 @@ SHAPES = [
     (2, 1024, 64, "bf16"),
     (1, 2048, 128, "bf16"),
     (31, 2048, 256, "bf16"),
+    # Wider bf16 rows of 16 m runs take the matrix-core row kernel: one row per
+    # workgroup (4096), row boundaries inside a wave (2560), three rows per
+    # workgroup with a partial last wave (10752).
+    (3, 4096, 64, "bf16"),
+    (9, 2560, 256, "bf16"),
+    (7, 10752, 128, "bf16"),
 ]
 
 
@@ -383,7 +389,7 @@ np.savez(sys.argv[5], codes=codes.cpu().numpy(), scale=scale.cpu().numpy(), mask
 """
 
 
-@pytest.mark.parametrize("cols,block,b", [(2048, 128, 4), (512, 64, 1)])
+@pytest.mark.parametrize("cols,block,b", [(2048, 128, 4), (512, 64, 1), (5632, 128, 1)])
 def test_valu_switch_matches_oracle_and_mfma(dev, tmp_path, cols, block, b):
     import os
     import subprocess
