@@ -158,6 +158,7 @@ def main():
     scales = [torch.empty((ROWS,), dtype=torch.float32, device=dev) for _ in range(N_SETS)]
     masks = [torch.empty((ROWS, COLS // 8), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
     dxs = [torch.empty_like(g0) for _ in range(N_SETS)]
+    dqs = [torch.empty_like(x0) for _ in range(N_SETS)]  # fake-quantised outputs of the fused forward
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     # Steps are independent batches: step i's backward runs on a second stream
@@ -287,6 +288,15 @@ def main():
     fwd_avg = timed_launches(lambda s_: f_fwd(*fwd_args[s_]))
     bwd_avg = timed_launches(lambda s_: f_bwd(*bwd_args[s_]))
     copy_avg = timed_launches(lambda s_: torch.neg(gs[s_], out=dxs[s_]))
+    f_fwd_dq = lib.quest_quantize_fwd_dq
+    fwd_dq_args = [
+        (ctypes.c_void_p(xs[i].data_ptr()), qa.QUEST_BF16, ROWS, COLS, BLOCK, BITS, None,
+         ctypes.c_void_p(scales[i].data_ptr()), ctypes.c_void_p(masks[i].data_ptr()),
+         ctypes.c_void_p(dqs[i].data_ptr()), qa.QUEST_BF16, sh)
+        for i in range(N_SETS)
+    ]
+    fwd_dq_avg = timed_launches(lambda s_: check("quest_quantize_fwd_dq", f_fwd_dq(*fwd_dq_args[s_])))
+    fwd_dq_bytes = ROWS * COLS * 2 + ROWS * COLS * 2 + ROWS * COLS // 8 + 4 * ROWS
     fwd_bytes = alg_bytes_fwd(ROWS, COLS, 2, BITS)
     bwd_bytes = alg_bytes_bwd(ROWS, COLS, 2)
     copy_bytes = 2 * ROWS * COLS * 2
@@ -339,6 +349,12 @@ def main():
         "step_hbm_gbps": step_bytes / (ms_per_step * 1e6),
         "step_roofline_frac": step_bytes / (ms_per_step * 1e6) / HBM_PEAK_GBPS,
         "kernels": kernels,
+        "other_kernels": {
+            "quest_quantize_fwd_dq (no codes, bf16 dequantised output; QAT training forward)": {
+                "avg_us": 1000 * fwd_dq_avg, "alg_bytes": fwd_dq_bytes,
+                "gbps": fwd_dq_bytes / (fwd_dq_avg * 1e6),
+                "frac_of_peak": round(fwd_dq_bytes / (fwd_dq_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+        },
         "copy_reference": {"kernel": "torch.neg, 16384x2048 bf16", "bytes": copy_bytes, "avg_us": 1000 * copy_avg,
                            "gbps": copy_gbps, "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "timing": {"step_events_ms": step_ms, "step_wall_s": wall,

@@ -114,6 +114,31 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
                                 int b, uint8_t* codes, float* scale, uint8_t* mask, void* stream);
 
 /*
+ * Forward quantisation that also writes the dequantised ("fake-quantised")
+ * tensor, in one pass over x: everything quest_quantize_fwd computes, plus
+ *   dq[r, c] = (2 u[r, c] - L + 1) * s_r / (L - 1)   (Hadamard domain),
+ * the grid value of each entry's code, rounded to dq_dtype (bf16: round to
+ * nearest even).  The values are those quest_dequantize returns for the
+ * same codes and scale, bit for bit.  This is the tensor a quantisation-
+ * aware training step multiplies with: both operands of a product are
+ * transformed and quantised, and their product in the Hadamard domain equals
+ * the product of the originals' reconstructions (pith.science review of
+ * QuEST, "Assumptions & free parameters"; "What carries the argument").
+ *
+ *   x, x_dtype, rows, cols, block, b, scale, mask, stream: as for
+ *           quest_quantize_fwd
+ *   codes   device output as for quest_quantize_fwd, or NULL: codes are then
+ *           not written (a training step that keeps only dq, scale and mask)
+ *   dq      device output, rows*cols elements of dq_dtype (QUEST_BF16 or
+ *           QUEST_F32), 16-byte aligned, overlapping no other argument
+ * Errors as for quest_quantize_fwd; a NULL dq with rows > 0 or an unknown
+ * dq_dtype is QUEST_EINVAL.
+ */
+quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                   int b, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                                   quest_dtype dq_dtype, void* stream);
+
+/*
  * Dequantise codes to their grid values, in the Hadamard domain:
  *   out[r, c] = (2 u[r, c] - L + 1) * s_r / (L - 1),  L = 2^b,
  * rounded to out_dtype (bf16: round to nearest even).  The Hadamard domain

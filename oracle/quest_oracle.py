@@ -64,6 +64,8 @@ __all__ = [
     "quantize_fwd",
     "dequantize",
     "trust_bwd",
+    "qat_linear_fwd",
+    "qat_linear_bwd",
 ]
 
 
@@ -411,3 +413,39 @@ def trust_bwd(grad: np.ndarray, mask: np.ndarray, block: int) -> np.ndarray:
     grad = np.asarray(grad, dtype=np.float64)
     m = unpack_lsb_first(mask, 1, grad.shape[1]).astype(np.float64)
     return blockwise_hadamard(m * grad, block)
+
+
+# ---------------------------------------------------------------------------
+# A quantisation-aware linear layer built from the pieces above.
+# pith.science review of QuEST, "Assumptions & free parameters" (the
+# orthogonal transform is applied to both operands of a product, so their
+# product can be taken in the transformed domain), "What carries the
+# argument" and the Figure 2 caption (the backward pass masks the
+# Hadamard-domain gradient with the trust mask and transforms it back).
+# ---------------------------------------------------------------------------
+def qat_linear_fwd(x: np.ndarray, w: np.ndarray, block: int, bits_x: int, bits_w: int) -> dict:
+    """y = Q(x) Q(w)^T with both operands quantised along their last axis.
+
+    x is N x K (activations), w is M x K (weights); the Hadamard blocks run
+    along K, the contraction axis.  Q(.) is the dequantised grid value in the
+    Hadamard domain, so y = (x~ H)(w~ H)^T = x~ w~^T, where x~ and w~ are the
+    original-domain reconstructions.
+    """
+    fx = quantize_fwd(np.asarray(x, dtype=np.float64), block, bits_x)
+    fw = quantize_fwd(np.asarray(w, dtype=np.float64), block, bits_w)
+    qx = fx["q"]
+    qw = fw["q"]
+    return {"y": qx @ qw.T, "qx": qx, "qw": qw, "mask_x": fx["mask"], "mask_w": fw["mask"], "fx": fx, "fw": fw}
+
+
+def qat_linear_bwd(dy: np.ndarray, fwd: dict, block: int) -> tuple:
+    """Gradients of the layer with the trust estimator on both operands.
+
+    The gradient reaching Q(x) is dy Q(w), the one reaching Q(w) is
+    dy^T Q(x); each is masked by its operand's trust mask and transformed
+    back (trust_bwd).  Returns (dx, dw).
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    dx = trust_bwd(dy @ fwd["qw"], fwd["mask_x"], block)
+    dw = trust_bwd(dy.T @ fwd["qx"], fwd["mask_w"], block)
+    return dx, dw

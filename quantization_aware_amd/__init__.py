@@ -21,6 +21,7 @@ __all__ = [
     "codes_bytes",
     "mask_bytes",
     "quantize_fwd",
+    "quantize_fwd_dq",
     "dequantize",
     "trust_bwd",
     "EXPORTED_SYMBOLS",
@@ -34,6 +35,7 @@ QUEST_F32, QUEST_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "quest_fit_alpha",
     "quest_quantize_fwd",
+    "quest_quantize_fwd_dq",
     "quest_dequantize",
     "quest_trust_bwd",
     "quest_codes_bytes",
@@ -69,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_fit_alpha.restype = ctypes.c_double
     lib.quest_quantize_fwd.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp]
     lib.quest_quantize_fwd.restype = c_int
+    lib.quest_quantize_fwd_dq.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp, c_int, vp]
+    lib.quest_quantize_fwd_dq.restype = c_int
     lib.quest_dequantize.argtypes = [vp, vp, i64, i64, c_int, vp, c_int, vp]
     lib.quest_dequantize.restype = c_int
     lib.quest_trust_bwd.argtypes = [vp, c_int, vp, i64, i64, c_int, vp, vp]
@@ -155,6 +159,50 @@ def quantize_fwd(x: torch.Tensor, block: int, b: int, codes=None, scale=None, ma
     )
     _check("quest_quantize_fwd", st)
     return codes, scale, mask
+
+
+def quantize_fwd_dq(x: torch.Tensor, block: int, b: int, dq_dtype=torch.bfloat16, with_codes: bool = True,
+                    codes=None, scale=None, mask=None, dq=None, stream=None):
+    """Forward quantisation that also returns the dequantised tensor, in one pass.
+
+    Returns (codes, scale, mask, dq); codes is None when with_codes is False
+    (they are then not written).  dq holds the grid value of every entry's
+    code in the Hadamard domain, rows x cols of dq_dtype (bfloat16 or float32).
+    """
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    if with_codes and codes is None:
+        codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev)
+    if not with_codes:
+        codes = None
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if mask is None:
+        mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
+    if dq is None:
+        dq = torch.empty((rows, cols), dtype=dq_dtype, device=dev)
+    checks = [("scale", scale, torch.float32), ("mask", mask, torch.uint8)]
+    if codes is not None:
+        checks.append(("codes", codes, torch.uint8))
+    for name, t, dt in checks:
+        _device_tensor(name, t)
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}")
+    _device_tensor("dq", dq)
+    if (codes is not None and codes.numel() < codes_bytes(rows, cols, b)) or scale.numel() < rows \
+            or mask.numel() < mask_bytes(rows, cols) or dq.numel() < rows * cols:
+        raise ValueError("output buffer too small")
+    st = lib.quest_quantize_fwd_dq(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b),
+        codes.data_ptr() if codes is not None else None, scale.data_ptr(), mask.data_ptr(),
+        dq.data_ptr(), _dtype_code(dq), _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd_dq", st)
+    return codes, scale, mask, dq
 
 
 def dequantize(codes: torch.Tensor, scale: torch.Tensor, rows: int, cols: int, b: int,

@@ -122,6 +122,13 @@ quest_status check_shape(int64_t rows, int64_t cols, int multiple_of) {
 
 quest_status from_hip(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_EHIP; }
 
+// Forward with codes (null allowed unless codes_required) and an optional
+// dequantised output (dq null = none; required when dq_dtype is given by
+// quest_quantize_fwd_dq).  Checks every argument before launching.
+quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                 uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, void* dq,
+                                 quest_dtype dq_dtype, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -157,25 +164,14 @@ const char* quest_status_string(quest_status s) {
 
 quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                 uint8_t* codes, float* scale, uint8_t* mask, void* stream) {
-  const int lb = log2_block(block);
-  if (lb < 0 || b < 1 || b > 4) return QUEST_EUNSUPPORTED;
-  if (!dtype_ok(x_dtype)) return QUEST_EINVAL;
-  const quest_status sh = check_shape(rows, cols, block);
-  if (sh != QUEST_OK) return sh;
-  if (rows == 0) return QUEST_OK;
-  if (!x || !codes || !scale || !mask) return QUEST_EINVAL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(mask)) return QUEST_EALIGN;
-  const size_t nx = static_cast<size_t>(rows * cols) * dtype_size(x_dtype);
-  const size_t nc = quest_codes_bytes(rows, cols, b);
-  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
-  const size_t nm = quest_mask_bytes(rows, cols);
-  if (overlaps(x, nx, codes, nc) || overlaps(x, nx, scale, ns) || overlaps(x, nx, mask, nm) ||
-      overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm))
-    return QUEST_EINVAL;
-  const double alpha = quest_fit_alpha(b);
-  std::call_once(g_env_once, read_env);
-  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, g_allow_mfma, codes,
-                                             scale, mask, static_cast<hipStream_t>(stream)));
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, codes, true, scale, mask, nullptr, QUEST_BF16, stream);
+}
+
+quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                   uint8_t* codes, float* scale, uint8_t* mask, void* dq, quest_dtype dq_dtype,
+                                   void* stream) {
+  if (!dtype_ok(dq_dtype)) return QUEST_EINVAL;
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, codes, false, scale, mask, dq, dq_dtype, stream);
 }
 
 quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,
@@ -214,3 +210,37 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
 }
 
 }  // extern "C"
+
+namespace {
+
+quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                 uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, void* dq,
+                                 quest_dtype dq_dtype, void* stream) {
+  const int lb = log2_block(block);
+  if (lb < 0 || b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(x_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, block);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!x || !scale || !mask || (codes_required && !codes) || (!codes_required && !dq)) return QUEST_EINVAL;
+  if (!aligned16(x) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(mask) ||
+      (dq && !aligned16(dq)))
+    return QUEST_EALIGN;
+  const size_t nx = static_cast<size_t>(rows * cols) * dtype_size(x_dtype);
+  const size_t nc = codes ? quest_codes_bytes(rows, cols, b) : 0;
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t nm = quest_mask_bytes(rows, cols);
+  const size_t nd = dq ? static_cast<size_t>(rows * cols) * dtype_size(dq_dtype) : 0;
+  if (overlaps(x, nx, codes, nc) || overlaps(x, nx, scale, ns) || overlaps(x, nx, mask, nm) ||
+      overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm) ||
+      overlaps(dq, nd, x, nx) || overlaps(dq, nd, codes, nc) || overlaps(dq, nd, scale, ns) ||
+      overlaps(dq, nd, mask, nm))
+    return QUEST_EINVAL;
+  const double alpha = quest_fit_alpha(b);
+  std::call_once(g_env_once, read_env);
+  const int dq_kind = dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
+  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, g_allow_mfma, codes,
+                                             scale, mask, dq, dq_kind, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace

@@ -164,26 +164,98 @@ __device__ __forceinline__ float fwd_transform(const uint32_t (&raw)[8 * sizeof(
   return fwht_cross_lanes<LOGN>(v, lane_bits);
 }
 
+// Per-row constants from a row's sum of squares: the scale s = alpha RMS, the
+// code factor kk (times this lane's sign tau) and the trust threshold on v.
+struct RowConsts {
+  float scale, kk, thr;
+};
+
+__device__ __forceinline__ RowConsts row_consts(float ss, float tau, const FwdConsts& k) {
+  const float ms = ss * k.inv_cols;
+  const float rms = __builtin_amdgcn_sqrtf(ms);
+  RowConsts c;
+  c.scale = k.alpha * rms;
+  // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
+  c.kk = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
+  c.thr = k.thr * rms;
+  return c;
+}
+
+// Optional dequantised output of the forward pass: Dq = void (none),
+// uint16_t (bf16) or float.  U is the number of 16-byte pieces per run.
+template <typename Dq>
+struct DqOut {
+  static constexpr bool kOn = true;
+  static constexpr int U = static_cast<int>(sizeof(Dq)) * 2;
+};
+template <>
+struct DqOut<void> {
+  static constexpr bool kOn = false;
+  static constexpr int U = 1;
+};
+
+// Grid values (2u - L + 1) s / (L - 1) of N entries whose codes are computed
+// from v with factor kk by quantise_run / quantise8 (the same arithmetic, so
+// each value is the grid value of the stored code).  c = s / (L - 1),
+// rounded as by quest_dequantize, and the product is rounded once, so the
+// values equal quest_dequantize's on the same codes and scale.
+template <int B, int N>
+__device__ __forceinline__ void grid_values(const float* v, float kk, float c, float* q) {
+  constexpr float L = static_cast<float>(1 << B);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float u;
+    if constexpr (B == 1) {
+      u = v[i] * kk >= 0.f ? 1.f : 0.f;
+    } else if constexpr (B == 2 || B == 4) {
+      const float t = __builtin_fminf(__builtin_fmaf(v[i], kk, 0.5f * (L - 1.f)), L - 1.f);
+      u = __builtin_fmaxf(__builtin_rintf(t), 0.f);
+    } else {
+      u = __builtin_truncf(__builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], kk, 0.5f * L), 0.f, L - 1.f));
+    }
+    q[i] = __builtin_fmaf(u, 2.f, 1.f - L) * c;
+  }
+}
+
+// c = s / (L - 1) for the grid values (a correctly rounded fp32 division, as
+// in quest_dequantize).
+template <int B>
+__device__ __forceinline__ float grid_step_half(float s) {
+  return s / static_cast<float>((1 << B) - 1);
+}
+
 // Codes, mask and scale of one run per lane, once its row's sum of squares is
 // known.  The lane's codes go to offset 4 B lane of `codes_r`, its mask word to
 // 4 lane of `mask_r`, and the row scale to `scale_off` of `scale_r` (kNowhere
 // for all lanes but one per row).
 template <int B>
-__device__ __forceinline__ void fwd_quantise_store(const float (&v)[RUN], float tau, float ss, const FwdConsts& k,
-                                                   int lane, rsrc_t codes_r, rsrc_t mask_r, rsrc_t scale_r,
-                                                   int scale_off) {
-  const float ms = ss * k.inv_cols;
-  const float rms = __builtin_amdgcn_sqrtf(ms);
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(k.alpha * rms), scale_r, scale_off, 0, 0);
-  // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
-  const float kk = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
-  const float thr = k.thr * rms;
-  const CodeWords<B> cw = quantise_run<B>(v, kk);
+__device__ __forceinline__ RowConsts fwd_quantise_store(const float (&v)[RUN], float tau, float ss,
+                                                        const FwdConsts& k, int lane, rsrc_t codes_r, rsrc_t mask_r,
+                                                        rsrc_t scale_r, int scale_off) {
+  const RowConsts c = row_consts(ss, tau, k);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c.scale), scale_r, scale_off, 0, 0);
+  const CodeWords<B> cw = quantise_run<B>(v, c.kk);
   uint32_t mw = 0u;
-  push16_abs_le(mw, v + 16, thr);
-  push16_abs_le(mw, v, thr);
+  push16_abs_le(mw, v + 16, c.thr);
+  push16_abs_le(mw, v, c.thr);
   store_codes<B>(codes_r, lane, cw);
   __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, kNonTemporal);
+  return c;
+}
+
+// Dequantised values of the lane's run, stored through the wave's LDS stage
+// as run first_run + lane of `dq` (runs at or past end_run dropped).
+template <int B, typename Dq>
+__device__ __forceinline__ void fwd_store_dq(const float (&v)[RUN], const RowConsts& c, Dq* dq, int64_t first_run,
+                                             int64_t end_run, int lane, u32x4* stage) {
+  if constexpr (DqOut<Dq>::kOn) {
+    constexpr int UD = DqOut<Dq>::U;
+    float q[RUN];
+    grid_values<B, RUN>(v, c.kk, grid_step_half<B>(c.scale), q);
+    uint32_t raw[4 * UD];
+    narrow_run(q, raw);
+    wave_store_runs<UD>(dq, first_run * UD, end_run * UD, lane, stage, raw);
+  }
 }
 
 // Rows of at most 64 runs (cols <= 2048) with a power-of-two run count: a
@@ -191,12 +263,14 @@ __device__ __forceinline__ void fwd_quantise_store(const float (&v)[RUN], float 
 // whole rows), so the row reduction stays inside the wave.  Each wave walks
 // tiles tile0, tile0 + stride, ... with its loads running two tiles ahead of
 // the arithmetic.
-template <typename In, int LOGN, int B>
+template <typename In, int LOGN, int B, typename Dq>
 __global__ void __launch_bounds__(256)
     quest_fwd_tiles_kernel(const In* __restrict__ x, int64_t total_runs, int log_runs_per_row, FwdConsts k,
-                           uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask) {
+                           uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask,
+                           Dq* __restrict__ dq) {
   constexpr int U = sizeof(In) * 2;  // 16-byte pieces per run
-  __shared__ u32x4 stage_all[4][64 * U];
+  constexpr int US = U > DqOut<Dq>::U ? U : DqOut<Dq>::U;
+  __shared__ u32x4 stage_all[4][64 * US];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   u32x4* stage = stage_all[wave];
@@ -208,6 +282,7 @@ __global__ void __launch_bounds__(256)
   if (tile >= tiles) return;
   const int rows_per_tile = 64 >> log_runs_per_row;
   const int scale_off = (lane & ((1 << log_runs_per_row) - 1)) == 0 ? (lane >> log_runs_per_row) * 4 : kNowhere;
+  const int64_t codes_total = codes ? total_runs * 4 * B : 0;  // no codes: every code store is dropped
 
   auto process = [&](int64_t t, const u32x4 (&pieces)[U]) {
     uint32_t raw[4 * U];
@@ -217,10 +292,11 @@ __global__ void __launch_bounds__(256)
     const float tau = fwd_transform<In, LOGN>(raw, v, ss, lane);
     ss = group_sum(ss, log_runs_per_row);
     const int64_t run0 = t * 64;
-    const rsrc_t codes_r = window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B);
+    const rsrc_t codes_r = window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B);
     const rsrc_t mask_r = window_at(mask, run0 * 4, total_runs * 4, 64 * 4);
     const rsrc_t scale_r = window_at(scale, t * rows_per_tile * 4, rows * 4, rows_per_tile * 4);
-    fwd_quantise_store<B>(v, tau, ss, k, lane, codes_r, mask_r, scale_r, scale_off);
+    const RowConsts c = fwd_quantise_store<B>(v, tau, ss, k, lane, codes_r, mask_r, scale_r, scale_off);
+    fwd_store_dq<B>(v, c, dq, run0, total_runs, lane, stage);
   };
 
   // Three tile buffers, fetched two tiles ahead.  Every fetch is issued (past
@@ -286,21 +362,32 @@ __device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const
   __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, kNonTemporal);
 }
 
-// Per-row constants from a row's sum of squares: the scale s = alpha RMS, the
-// code factor kk (times this lane's sign tau) and the trust threshold on v.
-struct RowConsts {
-  float scale, kk, thr;
-};
-
-__device__ __forceinline__ RowConsts row_consts(float ss, float tau, const FwdConsts& k) {
-  const float ms = ss * k.inv_cols;
-  const float rms = __builtin_amdgcn_sqrtf(ms);
-  RowConsts c;
-  c.scale = k.alpha * rms;
-  // A zero row (ms = 0) keeps kk = 0: every code is the middle one, every entry trusted.
-  c.kk = ms > 0.f ? tau * k.kk * __builtin_amdgcn_rsqf(ms) : 0.f;
-  c.thr = k.thr * rms;
-  return c;
+// Dequantised values of the wave's four 16-run groups (layout of
+// mfma_quantise_store's inputs) into the window `dq_r` of the wave's 64 runs:
+// lane (g, n) holds entries 8 g .. 8 g + 7 of run 16 j + n in slot j, which
+// it stores as 16 (bf16) or 32 (fp32) contiguous bytes; each store
+// instruction covers one contiguous stretch, as the loads do.
+template <int B, typename Dq>
+__device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float (&kk)[4], const float (&c)[4],
+                                              int lane, rsrc_t dq_r) {
+  if constexpr (DqOut<Dq>::kOn) {
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float q[8];
+      grid_values<B, 8>(v + 8 * j, kk[j], c[j], q);
+      if constexpr (sizeof(Dq) == 2) {
+        const u32x4 w = {pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]), pack_bf16x2(q[4], q[5]),
+                         pack_bf16x2(q[6], q[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, dq_r, 64 * (16 * j + n) + 16 * g, 0, kNonTemporal);
+      } else {
+        const u32x4 w0 = {__float_as_uint(q[0]), __float_as_uint(q[1]), __float_as_uint(q[2]), __float_as_uint(q[3])};
+        const u32x4 w1 = {__float_as_uint(q[4]), __float_as_uint(q[5]), __float_as_uint(q[6]), __float_as_uint(q[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w0, dq_r, 128 * (16 * j + n) + 32 * g, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, dq_r, 128 * (16 * j + n) + 32 * g + 16, 0, kNonTemporal);
+      }
+    }
+  }
 }
 
 // bf16 rows of 16, 32 or 64 runs (512, 1024 or 2048 columns) on the matrix
@@ -311,10 +398,11 @@ __device__ __forceinline__ RowConsts row_consts(float ss, float tau, const FwdCo
 // packed per slot (8 entries) and a transpose between lane quarters and
 // slots hands lane l all four quarters of run l, which it stores as in the
 // run-per-lane kernels.  Loads run two tiles ahead of the arithmetic.
-template <int LOGN, int B, int LOGR>
+template <int LOGN, int B, int LOGR, typename Dq>
 __global__ void __launch_bounds__(256)
     quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
-                          uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask) {
+                          uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask,
+                          Dq* __restrict__ dq) {
   static_assert(LOGR >= 4 && LOGR <= 6, "16, 32 or 64 runs per row");
   constexpr int ROWS = 64 >> LOGR;  // rows per tile
   const int lane = threadIdx.x & 63;
@@ -328,6 +416,7 @@ __global__ void __launch_bounds__(256)
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
   const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
   const int scale_off = lane < ROWS ? lane * 4 : kNowhere;
+  const int64_t codes_total = codes ? total_runs * 4 * B : 0;  // no codes: every code store is dropped
 
   auto fetch = [&](int64_t t, u32x4 (&f)[4]) {
     const rsrc_t r = window_at(x, t * 4096, total_runs * 64, 4096);
@@ -355,7 +444,7 @@ __global__ void __launch_bounds__(256)
       for (int j = 0; j < 4; ++j) ss[j] = group_sum(part[j], 6);
     }
     const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
-    float kk[4], thr[4], sc[ROWS];
+    float kk[4], thr[4], ch[4], sc[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const RowConsts c = row_consts(ss[r], tau, k);
@@ -364,11 +453,16 @@ __global__ void __launch_bounds__(256)
       for (int j = r * (4 / ROWS); j < (r + 1) * (4 / ROWS); ++j) {
         kk[j] = c.kk;
         thr[j] = c.thr;
+        ch[j] = grid_step_half<B>(c.scale);
       }
     }
     const int64_t run0 = t * 64;
-    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, total_runs * 4 * B, 64 * 4 * B),
+    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
                            window_at(mask, run0 * 4, total_runs * 4, 64 * 4));
+    if constexpr (DqOut<Dq>::kOn) {
+      constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
+      mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, total_runs * RB, 64 * RB));
+    }
     float my_scale = sc[0];
 #pragma unroll
     for (int r = 1; r < ROWS; ++r) my_scale = lane == r ? sc[r] : my_scale;
@@ -406,11 +500,11 @@ __global__ void __launch_bounds__(256)
 // block of rows (no grid-stride loop): with a barrier per block, letting the
 // hardware refill compute units as workgroups finish hides latency better
 // than a resident loop.
-template <int LOGN, int B>
+template <int LOGN, int B, typename Dq>
 __global__ void __launch_bounds__(1024)
     quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
                                FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
-                               uint32_t* __restrict__ mask) {
+                               uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
   __shared__ float group_ss[64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
@@ -454,19 +548,24 @@ __global__ void __launch_bounds__(1024)
   }
   const RowConsts ca = row_consts(ss_a, tau, k);
   const RowConsts cb = row_consts(ss_b, tau, k);
-  float kk[4], thr[4];
+  float kk[4], thr[4], ch[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bool in_a = (4 * wave + j) / groups_per_row == row_a;
     kk[j] = in_a ? ca.kk : cb.kk;
     thr[j] = in_a ? ca.thr : cb.thr;
+    ch[j] = grid_step_half<B>(in_a ? ca.scale : cb.scale);
   }
   // The wave's windows end where the workgroup's rows end: runs past them
   // belong to the next workgroup.
   const int64_t run0 = wg_first_run + 64 * wave;
   const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
-  mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, run_end * 4 * B, 64 * 4 * B),
+  mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
                          window_at(mask, run0 * 4, run_end * 4, 64 * 4));
+  if constexpr (DqOut<Dq>::kOn) {
+    constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
+    mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, run_end * RB, 64 * RB));
+  }
   // Slot j stores its row's scale when it holds the row's first group.
   const int my_group = 4 * wave + (lane & 3);
   const int my_row = my_group / groups_per_row;
@@ -484,13 +583,14 @@ __global__ void __launch_bounds__(1024)
 // through LDS and every lane adds up the groups of its row in the same order.
 // Lanes past the workgroup's rows compute on whatever they loaded (DPP needs
 // whole quads) and their stores fall outside the workgroup's windows.
-template <typename In, int LOGN, int B>
+template <typename In, int LOGN, int B, typename Dq>
 __global__ void __launch_bounds__(1024)
     quest_fwd_rows_kernel(const In* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg, int log_group,
                           FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
-                          uint32_t* __restrict__ mask) {
+                          uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
   constexpr int U = sizeof(In) * 2;
-  __shared__ u32x4 stage_all[16][64 * U];
+  constexpr int US = U > DqOut<Dq>::U ? U : DqOut<Dq>::U;
+  __shared__ u32x4 stage_all[16][64 * US];
   __shared__ float part[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -516,12 +616,15 @@ __global__ void __launch_bounds__(1024)
     for (int i = 0; i < per_row; ++i) ss += pr[i];
   }
   const uint32_t wg_runs = static_cast<uint32_t>(rows_per_wg * runs_per_row);
-  const rsrc_t codes_r = window_at(codes, wg_first_run * 4 * B, total_runs * 4 * B, wg_runs * 4 * B);
+  const rsrc_t codes_r = window_at(codes, wg_first_run * 4 * B, codes ? total_runs * 4 * B : 0, wg_runs * 4 * B);
   const rsrc_t mask_r = window_at(mask, wg_first_run * 4, total_runs * 4, wg_runs * 4);
   const rsrc_t scale_r =
       window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
   const int scale_off = (run_in_row == 0 && lrow < rows_per_wg) ? lrow * 4 : kNowhere;
-  fwd_quantise_store<B>(v, tau, ss, k, tid, codes_r, mask_r, scale_r, scale_off);
+  const RowConsts c = fwd_quantise_store<B>(v, tau, ss, k, tid, codes_r, mask_r, scale_r, scale_off);
+  // Lanes past the workgroup's rows must not write the next workgroup's runs.
+  const int64_t wg_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
+  fwd_store_dq<B>(v, c, dq, wg_first_run + wave_tid0, wg_end, lane, stage_all[wave_tid0 >> 6]);
 }
 
 // ----------------------------------------------------------------------------
@@ -607,43 +710,57 @@ int log2_exact(int v) {
 // loads run ahead of the arithmetic.
 constexpr int64_t kFwdTileWorkgroups = 512;
 
-template <typename In, int LOGN, int B>
-hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, bool allow_mfma, uint8_t* codes,
-                        float* scale, uint8_t* mask, hipStream_t stream) {
-  const int runs_per_row = static_cast<int>(cols / RUN);
+// Arguments of one forward launch, already validated.
+struct FwdLaunch {
+  int64_t rows, cols;
+  double alpha;
+  bool allow_mfma;
+  uint8_t* codes;  // may be null: codes are not written
+  float* scale;
+  uint8_t* mask;
+  void* dq;  // dequantised output (type chosen by the caller), or null
+  hipStream_t stream;
+};
+
+template <typename In, int LOGN, int B, typename Dq>
+hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
+  const int64_t rows = a.rows;
+  const int runs_per_row = static_cast<int>(a.cols / RUN);
   const double L = double(1 << B), sqrt_n = std::sqrt(double(1 << LOGN));
   FwdConsts k;
-  k.alpha = static_cast<float>(alpha);
-  k.kk = static_cast<float>((L - 1.0) / (2.0 * alpha * sqrt_n));
-  k.thr = static_cast<float>(alpha * L * sqrt_n / (L - 1.0));
-  k.inv_cols = static_cast<float>(1.0 / double(cols));
-  uint32_t* mask32 = reinterpret_cast<uint32_t*>(mask);
+  k.alpha = static_cast<float>(a.alpha);
+  k.kk = static_cast<float>((L - 1.0) / (2.0 * a.alpha * sqrt_n));
+  k.thr = static_cast<float>(a.alpha * L * sqrt_n / (L - 1.0));
+  k.inv_cols = static_cast<float>(1.0 / double(a.cols));
+  uint32_t* mask32 = reinterpret_cast<uint32_t*>(a.mask);
+  Dq* dq = static_cast<Dq*>(a.dq);
+  hipStream_t stream = a.stream;
   if constexpr (sizeof(In) == 2) {
-    if (allow_mfma && runs_per_row > 64 && runs_per_row % 16 == 0) {
+    if (a.allow_mfma && runs_per_row > 64 && runs_per_row % 16 == 0) {
       int rows_per_wg = 64 / gcd_int(runs_per_row, 64);
       if (rows_per_wg * runs_per_row > 1024) rows_per_wg = 1024 / runs_per_row;
       if (rows_per_wg < 1) rows_per_wg = 1;
       const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
       const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-      hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
-                         stream, x, rows, runs_per_row, rows_per_wg, k, codes, scale, mask32);
+      hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads),
+                         0, stream, x, rows, runs_per_row, rows_per_wg, k, a.codes, a.scale, mask32, dq);
       return hipGetLastError();
     }
-    if (allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
+    if (a.allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
       const int64_t total_runs = rows * runs_per_row;
       const int64_t tiles = (total_runs + 63) / 64;
       int64_t wgs = (tiles + 3) / 4;
       if (wgs > kFwdTileWorkgroups) wgs = kFwdTileWorkgroups;
       const dim3 grid(static_cast<uint32_t>(wgs));
       if (runs_per_row == 16)
-        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 4>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
-                           scale, mask32);
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 4, Dq>), grid, dim3(256), 0, stream, x, total_runs, k,
+                           a.codes, a.scale, mask32, dq);
       else if (runs_per_row == 32)
-        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 5>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
-                           scale, mask32);
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 5, Dq>), grid, dim3(256), 0, stream, x, total_runs, k,
+                           a.codes, a.scale, mask32, dq);
       else
-        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 6>), grid, dim3(256), 0, stream, x, total_runs, k, codes,
-                           scale, mask32);
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, 6, Dq>), grid, dim3(256), 0, stream, x, total_runs, k,
+                           a.codes, a.scale, mask32, dq);
       return hipGetLastError();
     }
   }
@@ -652,8 +769,8 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, b
     const int64_t tiles = (total_runs + 63) / 64;
     int64_t wgs = (tiles + 3) / 4;
     if (wgs > kFwdTileWorkgroups) wgs = kFwdTileWorkgroups;
-    hipLaunchKernelGGL((quest_fwd_tiles_kernel<In, LOGN, B>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream,
-                       x, total_runs, log2_exact(runs_per_row), k, codes, scale, mask32);
+    hipLaunchKernelGGL((quest_fwd_tiles_kernel<In, LOGN, B, Dq>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+                       stream, x, total_runs, log2_exact(runs_per_row), k, a.codes, a.scale, mask32, dq);
   } else {
     int group = runs_per_row & -runs_per_row;
     if (group > 64) group = 64;
@@ -662,30 +779,38 @@ hipError_t fwd_dispatch(const In* x, int64_t rows, int64_t cols, double alpha, b
     if (rows_per_wg < 1) rows_per_wg = 1;
     const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((quest_fwd_rows_kernel<In, LOGN, B>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
-                       stream, x, rows, runs_per_row, rows_per_wg, log2_exact(group), k, codes, scale, mask32);
+    hipLaunchKernelGGL((quest_fwd_rows_kernel<In, LOGN, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
+                       stream, x, rows, runs_per_row, rows_per_wg, log2_exact(group), k, a.codes, a.scale, mask32,
+                       dq);
   }
   return hipGetLastError();
 }
 
-template <typename In, int LOGN>
-hipError_t fwd_dispatch_bits(const In* x, int64_t rows, int64_t cols, int bits, double alpha, bool allow_mfma,
-                             uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
+template <typename In, int LOGN, typename Dq>
+hipError_t fwd_dispatch_bits(const In* x, int bits, const FwdLaunch& a) {
   switch (bits) {
-    case 1: return fwd_dispatch<In, LOGN, 1>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
-    case 2: return fwd_dispatch<In, LOGN, 2>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
-    case 3: return fwd_dispatch<In, LOGN, 3>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
-    default: return fwd_dispatch<In, LOGN, 4>(x, rows, cols, alpha, allow_mfma, codes, scale, mask, stream);
+    case 1: return fwd_dispatch<In, LOGN, 1, Dq>(x, a);
+    case 2: return fwd_dispatch<In, LOGN, 2, Dq>(x, a);
+    case 3: return fwd_dispatch<In, LOGN, 3, Dq>(x, a);
+    default: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
+  }
+}
+
+template <typename In, typename Dq>
+hipError_t fwd_dispatch_block(const In* x, int log_block, int bits, const FwdLaunch& a) {
+  switch (log_block) {
+    case 6: return fwd_dispatch_bits<In, 6, Dq>(x, bits, a);
+    case 7: return fwd_dispatch_bits<In, 7, Dq>(x, bits, a);
+    default: return fwd_dispatch_bits<In, 8, Dq>(x, bits, a);
   }
 }
 
 template <typename In>
-hipError_t fwd_dispatch_block(const In* x, int64_t rows, int64_t cols, int log_block, int bits, double alpha,
-                              bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask, hipStream_t stream) {
-  switch (log_block) {
-    case 6: return fwd_dispatch_bits<In, 6>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
-    case 7: return fwd_dispatch_bits<In, 7>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
-    default: return fwd_dispatch_bits<In, 8>(x, rows, cols, bits, alpha, allow_mfma, codes, scale, mask, stream);
+hipError_t fwd_dispatch_dq(const In* x, int log_block, int bits, int dq_kind, const FwdLaunch& a) {
+  switch (dq_kind) {
+    case 1: return fwd_dispatch_block<In, uint16_t>(x, log_block, bits, a);
+    case 2: return fwd_dispatch_block<In, float>(x, log_block, bits, a);
+    default: return fwd_dispatch_block<In, void>(x, log_block, bits, a);
   }
 }
 
@@ -742,13 +867,11 @@ hipError_t dequant_dispatch(const uint8_t* codes, const float* scale, int64_t ro
 }  // namespace
 
 hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
-                               double alpha, bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask,
-                               hipStream_t stream) {
-  if (x_is_bf16)
-    return fwd_dispatch_block(static_cast<const uint16_t*>(x), rows, cols, log_block, bits, alpha, allow_mfma, codes,
-                              scale, mask, stream);
-  return fwd_dispatch_block(static_cast<const float*>(x), rows, cols, log_block, bits, alpha, allow_mfma, codes, scale,
-                            mask, stream);
+                               double alpha, bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                               int dq_kind, hipStream_t stream) {
+  const FwdLaunch a{rows, cols, alpha, allow_mfma, codes, scale, mask, dq, stream};
+  if (x_is_bf16) return fwd_dispatch_dq(static_cast<const uint16_t*>(x), log_block, bits, dq_kind, a);
+  return fwd_dispatch_dq(static_cast<const float*>(x), log_block, bits, dq_kind, a);
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,

@@ -1,0 +1,81 @@
+"""QuEST quantisation-aware linear layer on libquest.
+
+y = Q(x) Q(w)^T + bias, where Q(.) quantises each operand along the
+contraction axis (blockwise Hadamard transform, RMS clip scale, b-bit grid)
+and returns the grid values in the Hadamard domain.  The transform is
+orthogonal and applied to both operands, so the product of the transformed
+operands equals the product of their original-domain reconstructions
+(pith.science review of QuEST, "Assumptions & free parameters").  The
+backward pass uses the trust estimator on both operands: the gradient
+reaching Q(x) is dy Q(w), the one reaching Q(w) is dy^T Q(x); each is masked
+by its operand's trust mask and transformed back (pith.science review,
+"What carries the argument" and the Figure 2 caption).
+
+Quantisation, masking and both transforms run in libquest's kernels
+(quest_quantize_fwd_dq, quest_trust_bwd).  The two matrix products are plain
+library GEMMs through torch.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import quantize_fwd_dq, trust_bwd
+
+__all__ = ["QuestLinearFunction", "quest_linear", "QuestLinear"]
+
+
+class QuestLinearFunction(torch.autograd.Function):
+    """y = Q(x) Q(w)^T for 2-D x (N x K) and w (M x K), K a multiple of `block`."""
+
+    @staticmethod
+    def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype):
+        _, _, mask_x, qx = quantize_fwd_dq(x, block, bits_x, dq_dtype=compute_dtype, with_codes=False)
+        _, _, mask_w, qw = quantize_fwd_dq(w, block, bits_w, dq_dtype=compute_dtype, with_codes=False)
+        y = torch.nn.functional.linear(qx, qw)
+        ctx.save_for_backward(qx, qw, mask_x, mask_w)
+        ctx.block = block
+        ctx.x_dtype, ctx.w_dtype = x.dtype, w.dtype
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        qx, qw, mask_x, mask_w = ctx.saved_tensors
+        dy = dy.to(qx.dtype).contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            g = torch.mm(dy, qw)  # gradient reaching Q(x), Hadamard domain
+            dx = trust_bwd(g, mask_x, ctx.block, out=g).to(ctx.x_dtype)
+        if ctx.needs_input_grad[1]:
+            # gradient reaching Q(w), Hadamard domain (dy^T made contiguous: bf16
+            # products with a transposed operand view are avoided)
+            g = torch.mm(dy.t().contiguous(), qx)
+            dw = trust_bwd(g, mask_w, ctx.block, out=g).to(ctx.w_dtype)
+        return dx, dw, None, None, None, None
+
+
+def quest_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None, block: int = 128,
+                 bits_x: int = 4, bits_w: int = 4, compute_dtype=torch.bfloat16) -> torch.Tensor:
+    """QuEST linear map of x (..., K) by w (M, K); leading axes of x are flattened."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    y = QuestLinearFunction.apply(x2, w.contiguous(), block, bits_x, bits_w, compute_dtype)
+    if bias is not None:
+        y = y + bias.to(y.dtype)
+    return y.reshape(*lead, w.shape[0])
+
+
+class QuestLinear(torch.nn.Module):
+    """Drop-in linear layer trained with QuEST quantisation of weights and activations."""
+
+    def __init__(self, in_features: int, out_features: int, bias: bool = True, block: int = 128, bits_x: int = 4,
+                 bits_w: int = 4, compute_dtype=torch.bfloat16, device=None, dtype=None):
+        super().__init__()
+        if in_features % block:
+            raise ValueError(f"in_features ({in_features}) must be a multiple of the Hadamard block ({block})")
+        self.block, self.bits_x, self.bits_w, self.compute_dtype = block, bits_x, bits_w, compute_dtype
+        self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
+        self.bias = torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=dtype)) if bias else None
+        torch.nn.init.kaiming_uniform_(self.weight, a=5 ** 0.5)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return quest_linear(x, self.weight, self.bias, self.block, self.bits_x, self.bits_w, self.compute_dtype)

@@ -187,6 +187,49 @@ def test_dequantize_rejects(lib, kw, status):
     assert deq(lib, **kw) == status
 
 
+E_ = 0x70000000
+
+
+def fwd_dq(lib, x=A, dt=qa.QUEST_BF16, rows=4, cols=256, block=128, b=4, codes=B_, scale=C_, mask=D_, dq=E_,
+           dq_dt=qa.QUEST_BF16):
+    return lib.quest_quantize_fwd_dq(x, dt, rows, cols, block, b, codes, scale, mask, dq, dq_dt, None)
+
+
+def test_fwd_dq_empty_call_is_a_noop(lib):
+    assert fwd_dq(lib, x=None, codes=None, scale=None, mask=None, dq=None, rows=0) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(block=32), qa.QUEST_EUNSUPPORTED),
+        (dict(b=5), qa.QUEST_EUNSUPPORTED),
+        (dict(dt=7), qa.QUEST_EINVAL),
+        (dict(dq_dt=3), qa.QUEST_EINVAL),
+        (dict(cols=320), qa.QUEST_EINVAL),
+        (dict(x=None), qa.QUEST_EINVAL),
+        (dict(dq=None), qa.QUEST_EINVAL),
+        (dict(scale=None), qa.QUEST_EINVAL),
+        (dict(mask=None), qa.QUEST_EINVAL),
+        (dict(dq=E_ + 8), qa.QUEST_EALIGN),
+        (dict(codes=B_ + 4), qa.QUEST_EALIGN),
+        (dict(codes=None, dq=E_ + 4), qa.QUEST_EALIGN),  # codes may be NULL; dq is still checked
+        (dict(dq=A + 1024), qa.QUEST_EINVAL),  # dq inside x
+        (dict(dq=B_), qa.QUEST_EINVAL),  # dq == codes
+        (dict(dq=C_ - 16), qa.QUEST_EINVAL),  # dq runs over scale
+        (dict(dq=D_), qa.QUEST_EINVAL),  # dq == mask
+        (dict(codes=None, dq=C_ - 16), qa.QUEST_EINVAL),
+        (dict(codes=A + 16), qa.QUEST_EINVAL),  # codes inside x
+    ],
+)
+def test_fwd_dq_rejects(lib, kw, status):
+    assert fwd_dq(lib, **kw) == status
+
+
+def test_fwd_still_requires_codes(lib):
+    assert fwd(lib, codes=None) == qa.QUEST_EINVAL
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
 

@@ -1,0 +1,147 @@
+"""QuEST linear layer (quest_quantize_fwd_dq + library GEMMs + quest_trust_bwd) vs the oracle.
+
+The oracle composes its pinned quantiser, a float64 matrix product and its
+trust backward (oracle.qat_linear_fwd / qat_linear_bwd).  The layer runs in
+a compute dtype:
+
+* float32: dequantised operands and GEMMs in fp32, so results agree with the
+  oracle to fp32 accumulation error (1e-4 relative);
+* bfloat16 (the training default): the dequantised operands are rounded to
+  bf16.  Within a row the rounding error of a grid value depends only on its
+  code, and with an outlier channel the codes of a block share the sign
+  pattern of one Hadamard row, so the errors correlate with that row and the
+  inverse transform gathers them onto the outlier's position: a few percent
+  of the gradient there.  Element-wise bound 1e-1 of max(|ref|, rms), norm-
+  wise 1e-2.
+
+The element-wise scale uses the RMS over the whole tensor for y and over the
+entry's row and Hadamard block for the gradients (which leave the kernel
+through an inverse transform).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import quantization_aware_amd as qa
+from oracle import quest_oracle as qo
+from quantization_aware_amd.linear import QuestLinear, quest_linear
+from quest_inputs import TensorSpec, make_tensor, to_float64
+from parity import exempt_entries
+
+pytestmark = pytest.mark.gpu
+
+TOLS = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (1e-1, 1e-2)}  # (element-wise, norm-wise)
+
+
+def log(msg: str) -> None:
+    print(f"[gpu-linear] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qa.load_library()
+    return torch.device("cuda", 0)
+
+
+def close(got: torch.Tensor, ref: np.ndarray, what: str, tols, skip=None, block=None) -> None:
+    """Element-wise and norm-wise agreement with the oracle, outside `skip`.
+
+    The element-wise scale is max(|ref|, rms), with rms taken over the whole
+    tensor, or per row and Hadamard block for the gradients (which leave the
+    kernel through an inverse transform: rounding of a large Hadamard-domain
+    entry spreads evenly over its block).
+    """
+    got = got.float().cpu().numpy().astype(np.float64)
+    if block is None:
+        rms = np.sqrt(np.mean(ref * ref))
+    else:
+        r, c = ref.shape
+        blk = ref.reshape(r, c // block, block)
+        rms = np.repeat(np.sqrt(np.mean(blk * blk, axis=2)), block, axis=1)
+    tol_elem, tol_norm = tols
+    err = np.abs(got - ref)
+    bad = err > tol_elem * np.maximum(np.abs(ref), rms)
+    if skip is not None:
+        bad &= ~skip
+    if bad.any():
+        r, c = np.argwhere(bad)[0]
+        log(f"{what}: relative Frobenius error {np.linalg.norm(got - ref) / np.linalg.norm(ref)!r}")
+        ratio = (err / np.maximum(np.abs(ref), rms))[bad]
+        raise AssertionError(f"{what}: {int(bad.sum())} entries off, first at ({r},{c}): got {got[r, c]!r} "
+                             f"ref {ref[r, c]!r}; worst error / max(|ref|, rms) {ratio.max()!r}")
+    keep = np.ones_like(bad) if skip is None else ~skip
+    rel = np.linalg.norm((got - ref)[keep]) / np.linalg.norm(ref[keep])
+    assert rel <= tol_norm, f"{what}: relative Frobenius error {rel} (outside the band's reach)"
+
+
+def band_reach(f: dict, bx: int, bw: int, block: int):
+    """Entries of y, dx and dw that an operand entry inside the threshold band can move.
+
+    A band entry (within 1e-6 s of a decision or trust threshold) may take the
+    neighbouring code or mask bit on the GPU, which is a correct outcome; it
+    shifts its row of y, dx or dw and, through the other operand's product,
+    the Hadamard block of its column.
+    """
+    bx_ = exempt_entries(f["fx"]["y"], f["fx"]["scale"], bx)
+    bw_ = exempt_entries(f["fw"]["y"], f["fw"]["scale"], bw)
+    rx, rw = bx_.any(axis=1), bw_.any(axis=1)
+    k = bx_.shape[1]
+    blk_x = np.repeat(bx_.reshape(bx_.shape[0], k // block, block).any(axis=(0, 2)), block)
+    blk_w = np.repeat(bw_.reshape(bw_.shape[0], k // block, block).any(axis=(0, 2)), block)
+    skip_y = rx[:, None] | rw[None, :]
+    skip_dx = rx[:, None] | blk_w[None, :] | blk_x[None, :] & rx[:, None]
+    skip_dw = rw[:, None] | blk_x[None, :] | blk_w[None, :] & rw[:, None]
+    return skip_y, skip_dx, skip_dw
+
+
+@pytest.mark.parametrize("compute_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,k,m,block,bx,bw", [(256, 1024, 384, 128, 4, 4), (96, 2048, 160, 64, 2, 3),
+                                              (130, 512, 64, 256, 4, 1)])
+def test_linear_matches_oracle(dev, n, k, m, block, bx, bw, compute_dtype):
+    log(f"linear {n}x{k} by {m}x{k}, block {block}, bits x{bx} w{bw}, compute {compute_dtype}")
+    tols = TOLS[compute_dtype]
+    x = make_tensor(TensorSpec("lin.x", n, k, "bf16", "student_t", 4, 9100 + n, outlier_cols=k // 100,
+                               outlier_scale=20.0), dev)
+    w = make_tensor(TensorSpec("lin.w", m, k, "bf16", "normal", 0.02, 9200 + m), dev)
+    dy = make_tensor(TensorSpec("lin.dy", n, m, "bf16", "normal", 1e-3, 9300 + n), dev)
+    # Inputs in the compute dtype (fp32 holds the same values exactly), so the
+    # gradients come back in it too.
+    xg = x.to(compute_dtype).requires_grad_(True)
+    wg = w.to(compute_dtype).requires_grad_(True)
+    y = quest_linear(xg, wg, block=block, bits_x=bx, bits_w=bw, compute_dtype=compute_dtype)
+    y.backward(dy.to(compute_dtype))
+    torch.cuda.synchronize()
+    f = qo.qat_linear_fwd(to_float64(x), to_float64(w), block, bx, bw)
+    dx_ref, dw_ref = qo.qat_linear_bwd(to_float64(dy), f, block)
+    skip_y, skip_dx, skip_dw = band_reach(f, bx, bw, block)
+    log(f"band reach: {int(skip_y.sum())} of y, {int(skip_dx.sum())} of dx, {int(skip_dw.sum())} of dw")
+    close(y.detach(), f["y"], "y", tols, skip_y)
+    close(xg.grad, dx_ref, "dx", tols, skip_dx, block)
+    close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
+
+
+def test_linear_module_autograd_3d_input(dev):
+    torch.manual_seed(0)
+    layer = QuestLinear(1024, 256, bias=True, block=128, device=dev, dtype=torch.bfloat16)
+    x = make_tensor(TensorSpec("mod.x", 2 * 64, 1024, "bf16", "student_t", 4, 9400), dev).reshape(2, 64, 1024)
+    x.requires_grad_(True)
+    log("module forward/backward, input 2x64x1024")
+    y = layer(x)
+    assert y.shape == (2, 64, 256) and y.dtype == torch.bfloat16
+    loss = (y.float() ** 2).mean()
+    loss.backward()
+    torch.cuda.synchronize()
+    # The same through the oracle (bias added after the product).
+    f = qo.qat_linear_fwd(to_float64(x.detach().reshape(128, 1024)), to_float64(layer.weight.detach()), 128, 4, 4)
+    y_ref = f["y"] + to_float64(layer.bias.detach())[None, :]
+    skip_y, skip_dx, skip_dw = band_reach(f, 4, 4, 128)
+    tols = TOLS[torch.bfloat16]
+    close(y.detach().reshape(128, 256), y_ref, "module y", tols, skip_y)
+    dy = (2.0 / y.numel()) * y.detach().float().reshape(128, 256).cpu().numpy().astype(np.float64)
+    dx_ref, dw_ref = qo.qat_linear_bwd(dy, f, 128)
+    close(x.grad.reshape(128, 1024), dx_ref, "module dx", tols, skip_dx, 128)
+    close(layer.weight.grad, dw_ref, "module dw", tols, skip_dw, 128)
+    assert np.allclose(layer.bias.grad.float().cpu().numpy(), dy.sum(axis=0), rtol=2e-2, atol=1e-6)

@@ -413,3 +413,47 @@ def test_valu_switch_matches_oracle_and_mfma(dev, tmp_path, cols, block, b):
     u_valu = qo.unpack_lsb_first(got["codes"], b, cols)
     u_mfma = qo.unpack_lsb_first(codes.cpu().numpy(), b, cols)
     assert np.array_equal(u_valu[~ex], u_mfma[~ex])
+
+
+# ---------------------------------------------------------------------------
+# Forward that also writes the dequantised tensor (quest_quantize_fwd_dq):
+# codes, scale and mask equal quest_quantize_fwd's bit for bit, dq equals
+# quest_dequantize of those codes bit for bit, and both match the oracle.
+# ---------------------------------------------------------------------------
+FWD_DQ_CASES = [
+    # rows, cols, block, x dtype, b, dq dtype, with codes
+    (96, 2048, 128, "bf16", 4, torch.bfloat16, True),  # matrix-core tiles
+    (77, 1024, 64, "bf16", 2, torch.float32, True),
+    (130, 512, 256, "bf16", 1, torch.bfloat16, False),
+    (9, 5632, 128, "bf16", 3, torch.bfloat16, True),  # matrix-core rows
+    (7, 10752, 128, "bf16", 4, torch.float32, False),
+    (33, 256, 128, "f32", 4, torch.bfloat16, True),  # vector-ALU tiles
+    (40, 2048, 64, "f32", 3, torch.float32, True),
+    (1000, 640, 64, "bf16", 1, torch.float32, True),  # vector-ALU rows
+    (17, 1536, 256, "f32", 2, torch.bfloat16, False),
+]
+
+
+@pytest.mark.parametrize("rows,cols,block,dt,b,dq_dtype,with_codes", FWD_DQ_CASES)
+def test_fwd_dq(dev, rows, cols, block, dt, b, dq_dtype, with_codes):
+    spec = TensorSpec(f"dq{rows}x{cols}", rows, cols, dt, "student_t", 4, 8300 + rows + cols + b,
+                      outlier_cols=max(1, cols // 100), outlier_scale=20.0)
+    log(f"fwd+dq {rows}x{cols} block {block} {dt} b={b} dq {dq_dtype} codes={with_codes}")
+    x = make_tensor(spec, dev)
+    codes, scale, mask, dq = qa.quantize_fwd_dq(x, block, b, dq_dtype=dq_dtype, with_codes=with_codes)
+    c_ref, s_ref, m_ref = qa.quantize_fwd(x, block, b)
+    deq = qa.dequantize(c_ref, s_ref, rows, cols, b, out_dtype=dq_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(scale, s_ref) and torch.equal(mask, m_ref)
+    if with_codes:
+        assert torch.equal(codes, c_ref)
+    else:
+        assert codes is None
+    assert torch.equal(dq.view(torch.int16 if dq_dtype == torch.bfloat16 else torch.int32),
+                       deq.view(torch.int16 if dq_dtype == torch.bfloat16 else torch.int32))
+    x64 = to_float64(x)
+    ref = qo.quantize_fwd(x64, block, b)
+    check_fwd(x64, block, b, c_ref.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), ref=ref)
+    ex = exempt_entries(ref["y"], ref["scale"], b)
+    check_values(dq.float().cpu().numpy(), qo.dequantize(ref["codes"], ref["scale"], cols, b),
+                 TOL_BF16 if dq_dtype == torch.bfloat16 else TOL_F32, skip=ex)

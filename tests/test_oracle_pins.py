@@ -454,3 +454,61 @@ def test_bwd_linear_and_norm_preserving():
             a = np.linalg.norm(out[r, 64 * k : 64 * (k + 1)])
             c = np.linalg.norm(masked[r, 64 * k : 64 * (k + 1)])
             assert abs(a - c) <= 1e-13 * max(c, 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# Quantisation-aware linear layer (oracle composition).
+# ---------------------------------------------------------------------------
+def _signs_through_hadamard(rng, rows, cols, block):
+    """Rows whose blockwise Hadamard transform is +-1 everywhere: every entry trusted."""
+    signs = rng.choice([-1.0, 1.0], size=(rows, cols))
+    return qo.blockwise_hadamard(signs, block)
+
+
+def test_qat_linear_product_equals_original_domain_product():
+    # Orthogonality: the Hadamard-domain product equals the product of the
+    # original-domain reconstructions (x~ = H Q(x) blockwise, H an involution).
+    rng = np.random.default_rng(71)
+    x = rng.standard_t(4, size=(24, 256))
+    w = 0.02 * rng.standard_normal((40, 256))
+    f = qo.qat_linear_fwd(x, w, 64, 4, 3)
+    x_rec = qo.blockwise_hadamard(f["qx"], 64)
+    w_rec = qo.blockwise_hadamard(f["qw"], 64)
+    assert np.allclose(f["y"], x_rec @ w_rec.T, rtol=1e-12, atol=1e-12)
+    # ... and not the product of reconstructions taken along the wrong axis
+    assert not np.allclose(f["y"], f["qx"] @ qo.blockwise_hadamard(f["qw"], 64).T, rtol=1e-3)
+
+
+@pytest.mark.parametrize("bx,bw", [(1, 1), (4, 2), (3, 4)])
+def test_qat_linear_all_trusted_gradients_are_straight_through(bx, bw):
+    # With every entry trusted the trust estimator is the straight-through
+    # gradient of y = x~ w~^T: dx = dy w~ and dw = dy^T x~ in the original domain.
+    rng = np.random.default_rng(72 + bx + bw)
+    x = _signs_through_hadamard(rng, 16, 256, 128)
+    w = 0.5 * _signs_through_hadamard(rng, 12, 256, 128)
+    f = qo.qat_linear_fwd(x, w, 128, bx, bw)
+    assert f["fx"]["m"].all() and f["fw"]["m"].all()
+    dy = rng.standard_normal((16, 12))
+    dx, dw = qo.qat_linear_bwd(dy, f, 128)
+    x_rec = qo.blockwise_hadamard(f["qx"], 128)
+    w_rec = qo.blockwise_hadamard(f["qw"], 128)
+    assert np.allclose(dx, dy @ w_rec, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dw, dy.T @ x_rec, rtol=1e-12, atol=1e-12)
+
+
+def test_qat_linear_untrusted_entries_get_no_gradient():
+    # In the Hadamard domain the gradient is zero exactly where an operand's
+    # entry is untrusted, and equals the unmasked gradient elsewhere.
+    rng = np.random.default_rng(73)
+    x = rng.standard_t(3, size=(32, 512))
+    w = rng.standard_t(3, size=(20, 512))
+    f = qo.qat_linear_fwd(x, w, 128, 2, 2)
+    assert (~f["fx"]["m"]).any() and (~f["fw"]["m"]).any()
+    dy = rng.standard_normal((32, 20))
+    dx, dw = qo.qat_linear_bwd(dy, f, 128)
+    gx = qo.blockwise_hadamard(dx, 128)  # H H = I up to fp64 rounding
+    gw = qo.blockwise_hadamard(dw, 128)
+    assert np.abs(gx[~f["fx"]["m"]]).max() <= 1e-12 * np.abs(gx).max()
+    assert np.abs(gw[~f["fw"]["m"]]).max() <= 1e-12 * np.abs(gw).max()
+    assert np.allclose(gx[f["fx"]["m"]], (dy @ f["qw"])[f["fx"]["m"]], rtol=1e-12, atol=1e-12)
+    assert np.allclose(gw[f["fw"]["m"]], (dy.T @ f["qx"])[f["fw"]["m"]], rtol=1e-12, atol=1e-12)
