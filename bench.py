@@ -41,7 +41,7 @@ HBM_PEAK_GBPS = 8000.0
 ROWS, COLS, BLOCK, BITS = 16384, 2048, 128, 4
 N_SETS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_16384x2048.txt")
-KERNEL_SOURCES = ["quest_device.h", "quest_kernels.hip"]
+KERNEL_SOURCES = ["quest_device.h", "quest_kernels.h"]
 
 
 def parse_args():

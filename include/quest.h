@@ -97,7 +97,7 @@ double quest_fit_alpha(int b);
  *   rows    >= 0
  *   cols    > 0, a multiple of `block`, at most QUEST_MAX_COLS
  *   block   Hadamard block size: 64, 128 or 256
- *   b       bits per code: 1, 2, 3 or 4
+ *   b       bits per code: 1 .. 8
  *   codes   device output, quest_codes_bytes(rows, cols, b) bytes
  *   scale   device output, rows floats (s_r)
  *   mask    device output, quest_mask_bytes(rows, cols) bytes
@@ -139,6 +139,27 @@ quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t r
                                    quest_dtype dq_dtype, void* stream);
 
 /*
+ * The general forward: quest_quantize_fwd_dq with an outer trust factor t.
+ * The trust mask keeps every entry inside the grid's range and, beyond the
+ * outermost levels, those within t half-steps of them:
+ *   mask = [ |q - y| <= Delta_r / 2 ]       for |y| <= s_r,
+ *          [ |q - y| <= t * Delta_r / 2 ]   for |y| >  s_r,
+ * i.e. trusted iff |y| <= s_r (1 + t / (L - 1)).  t = 1 is the plain rule of
+ * quest_quantize_fwd; the 1-bit runs of the pages use t = 1.30 (pith.science
+ * review of QuEST, "Assumptions & free parameters": the outer trust scaling
+ * factor s*; atlas.scime.ai summary, "Limitations").
+ *
+ *   trust   t, finite and >= 0 (QUEST_EINVAL otherwise)
+ *   codes   device output or NULL (not written)
+ *   dq      device output of dq_dtype or NULL (not written); dq_dtype is
+ *           checked only when dq is given
+ * Everything else as for quest_quantize_fwd_dq.
+ */
+quest_status quest_quantize_fwd_ex(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                   int b, double trust, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                                   quest_dtype dq_dtype, void* stream);
+
+/*
  * Dequantise codes to their grid values, in the Hadamard domain:
  *   out[r, c] = (2 u[r, c] - L + 1) * s_r / (L - 1),  L = 2^b,
  * rounded to out_dtype (bf16: round to nearest even).  The Hadamard domain
@@ -149,7 +170,7 @@ quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t r
  *   codes   device, quest_codes_bytes(rows, cols, b) bytes (layout above)
  *   scale   device, rows floats
  *   rows    >= 0;  cols > 0, a multiple of 64, at most QUEST_MAX_COLS
- *   b       1, 2, 3 or 4
+ *   b       1 .. 8
  *   out     device output, rows*cols elements of out_dtype; must not
  *           overlap codes or scale (QUEST_EINVAL)
  */

@@ -263,15 +263,23 @@ def fit_alpha(b: int) -> float:
 # Figure 7 caption (the mask M_alpha*).
 # ---------------------------------------------------------------------------
 
-def quantize_rows(y: np.ndarray, b: int, alpha: float):
+def quantize_rows(y: np.ndarray, b: int, alpha: float, trust: float = 1.0):
     """Quantise Hadamard-domain rows y (R x C).
 
     Returns (u, s, m, q):
       s[r]    = alpha * RMS_r with RMS_r = sqrt(mean_c y[r, c]^2)   (clip scale)
       u[r, c] = clamp(floor(y / Delta_r) + L/2, 0, L - 1), Delta_r = 2 s_r / (L - 1)
       q[r, c] = (2 u - L + 1) * Delta_r / 2                      (the grid value)
-      m[r, c] = |q - y| <= Delta_r / 2                            (trust mask)
+      m[r, c] = |q - y| <= Delta_r / 2             for |y| <= s_r  (trust mask)
+              = |q - y| <= trust * Delta_r / 2     for |y| >  s_r  (outer trust region)
     A row of zeros has s = 0; it takes the middle code L/2 and q = 0, m = 1.
+
+    The outer trust factor scales the trust region beyond the outermost
+    levels (pith.science review of QuEST, "Assumptions & free parameters":
+    the outer trust scaling factor, s* = 1.30 for 1-bit runs; atlas.scime.ai
+    summary, "Approach" and "Limitations").  Inside the grid the rounding
+    error never exceeds Delta / 2, so only clipped entries are affected; with
+    trust = 1 the mask is the plain |q - y| <= Delta / 2.
     """
     y = np.asarray(y, dtype=np.float64)
     big_l = 1 << b
@@ -285,11 +293,13 @@ def quantize_rows(y: np.ndarray, b: int, alpha: float):
     u[zero_row, :] = big_l // 2
     u = u.astype(np.int64)
     q = (2 * u - big_l + 1) * delta[:, None] / 2.0
-    m = np.abs(q - y) <= delta[:, None] / 2.0
+    err = np.abs(q - y)
+    inside = np.abs(y) <= s[:, None]
+    m = np.where(inside, err <= delta[:, None] / 2.0, err <= trust * delta[:, None] / 2.0)
     return u, s, m, q
 
 
-def quantize_rows_loop(y, b: int, alpha: float):
+def quantize_rows_loop(y, b: int, alpha: float, trust: float = 1.0):
     """The same quantiser as ``quantize_rows`` written as a scalar Python loop.
 
     Used on small inputs to cross-check the vectorised form.
@@ -318,7 +328,10 @@ def quantize_rows_loop(y, b: int, alpha: float):
             level = (2 * code - big_l + 1) * d_r / 2.0
             u[r, c] = code
             q[r, c] = level
-            m[r, c] = abs(level - v) <= d_r / 2.0
+            if abs(v) <= s_r:
+                m[r, c] = abs(level - v) <= d_r / 2.0
+            else:
+                m[r, c] = abs(level - v) <= trust * d_r / 2.0
     return u, s, m, q
 
 
@@ -362,7 +375,7 @@ def unpack_lsb_first(packed: np.ndarray, width: int, cols: int) -> np.ndarray:
 # The three calls of the path
 # ---------------------------------------------------------------------------
 
-def quantize_fwd(x: np.ndarray, block: int, b: int, alpha: float | None = None) -> dict:
+def quantize_fwd(x: np.ndarray, block: int, b: int, alpha: float | None = None, trust: float = 1.0) -> dict:
     """Forward QuEST quantisation of x (R x C): Hadamard -> RMS -> clip/round -> mask.
 
     QuEST abstract (codewithpapers.app record; Hadamard normalisation and
@@ -374,7 +387,7 @@ def quantize_fwd(x: np.ndarray, block: int, b: int, alpha: float | None = None) 
     if alpha is None:
         alpha = fit_alpha(b)
     y = blockwise_hadamard(x, block)
-    u, s, m, q = quantize_rows(y, b, alpha)
+    u, s, m, q = quantize_rows(y, b, alpha, trust)
     return {
         "codes": pack_lsb_first(u, b),
         "scale": s,
@@ -423,7 +436,8 @@ def trust_bwd(grad: np.ndarray, mask: np.ndarray, block: int) -> np.ndarray:
 # argument" and the Figure 2 caption (the backward pass masks the
 # Hadamard-domain gradient with the trust mask and transforms it back).
 # ---------------------------------------------------------------------------
-def qat_linear_fwd(x: np.ndarray, w: np.ndarray, block: int, bits_x: int, bits_w: int) -> dict:
+def qat_linear_fwd(x: np.ndarray, w: np.ndarray, block: int, bits_x: int, bits_w: int, trust_x: float = 1.0,
+                   trust_w: float = 1.0) -> dict:
     """y = Q(x) Q(w)^T with both operands quantised along their last axis.
 
     x is N x K (activations), w is M x K (weights); the Hadamard blocks run
@@ -431,8 +445,8 @@ def qat_linear_fwd(x: np.ndarray, w: np.ndarray, block: int, bits_x: int, bits_w
     Hadamard domain, so y = (x~ H)(w~ H)^T = x~ w~^T, where x~ and w~ are the
     original-domain reconstructions.
     """
-    fx = quantize_fwd(np.asarray(x, dtype=np.float64), block, bits_x)
-    fw = quantize_fwd(np.asarray(w, dtype=np.float64), block, bits_w)
+    fx = quantize_fwd(np.asarray(x, dtype=np.float64), block, bits_x, trust=trust_x)
+    fw = quantize_fwd(np.asarray(w, dtype=np.float64), block, bits_w, trust=trust_w)
     qx = fx["q"]
     qw = fw["q"]
     return {"y": qx @ qw.T, "qx": qx, "qw": qw, "mask_x": fx["mask"], "mask_w": fw["mask"], "fx": fx, "fw": fw}

@@ -22,6 +22,7 @@ __all__ = [
     "mask_bytes",
     "quantize_fwd",
     "quantize_fwd_dq",
+    "quantize_fwd_ex",
     "dequantize",
     "trust_bwd",
     "EXPORTED_SYMBOLS",
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "quest_fit_alpha",
     "quest_quantize_fwd",
     "quest_quantize_fwd_dq",
+    "quest_quantize_fwd_ex",
     "quest_dequantize",
     "quest_trust_bwd",
     "quest_codes_bytes",
@@ -73,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_quantize_fwd.restype = c_int
     lib.quest_quantize_fwd_dq.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp, c_int, vp]
     lib.quest_quantize_fwd_dq.restype = c_int
+    lib.quest_quantize_fwd_ex.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp, c_int, vp]
+    lib.quest_quantize_fwd_ex.restype = c_int
     lib.quest_dequantize.argtypes = [vp, vp, i64, i64, c_int, vp, c_int, vp]
     lib.quest_dequantize.restype = c_int
     lib.quest_trust_bwd.argtypes = [vp, c_int, vp, i64, i64, c_int, vp, vp]
@@ -202,6 +206,33 @@ def quantize_fwd_dq(x: torch.Tensor, block: int, b: int, dq_dtype=torch.bfloat16
         dq.data_ptr(), _dtype_code(dq), _stream_handle(dev, stream),
     )
     _check("quest_quantize_fwd_dq", st)
+    return codes, scale, mask, dq
+
+
+def quantize_fwd_ex(x: torch.Tensor, block: int, b: int, trust: float = 1.0, with_codes: bool = True,
+                    dq_dtype=None, stream=None):
+    """The general forward (quest_quantize_fwd_ex): outer trust factor, optional codes and dq.
+
+    Returns (codes or None, scale, mask, dq or None); dq_dtype None means no
+    dequantised output.
+    """
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev) if with_codes else None
+    scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
+    dq = torch.empty((rows, cols), dtype=dq_dtype, device=dev) if dq_dtype is not None else None
+    st = lib.quest_quantize_fwd_ex(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),
+        codes.data_ptr() if codes is not None else None, scale.data_ptr(), mask.data_ptr(),
+        dq.data_ptr() if dq is not None else None, _dtype_code(dq) if dq is not None else QUEST_BF16,
+        _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd_ex", st)
     return codes, scale, mask, dq
 
 

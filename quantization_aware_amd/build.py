@@ -1,5 +1,8 @@
 """Build libquest.so in-tree with hipcc for gfx950.
 
+Each translation unit is compiled by its own hipcc process (in parallel),
+then the objects are linked into the shared library.
+
 Usage: python -m quantization_aware_amd.build   (or build() from Python)
 """
 from __future__ import annotations
@@ -8,13 +11,22 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libquest.so")
-SOURCES = ["quest_api.hip", "quest_kernels.hip"]
+SOURCES = [
+    "quest_api.hip",
+    "quest_launch.hip",
+    "quest_fwd_nodq.hip",
+    "quest_fwd_dq_bf16.hip",
+    "quest_fwd_dq_f32.hip",
+]
 ARCH = "gfx950"
+NOISE = "is not a recognized feature for this target"  # the host pass does not know the GPU feature below
 
 
 def hipcc_path() -> str:
@@ -24,14 +36,12 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found; libquest needs ROCm's hipcc to build")
 
 
-def build_command(out_path: str = LIB_PATH) -> list[str]:
+def compile_flags() -> list[str]:
     return [
-        hipcc_path(),
         f"--offload-arch={ARCH}",
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         # Packed fp32 VALU forms are kept out of every kernel.
         "-Xclang",
         "-target-feature",
@@ -42,25 +52,36 @@ def build_command(out_path: str = LIB_PATH) -> list[str]:
         "-amdgpu-mfma-vgpr-form",
         "-I",
         os.path.join(ROOT, "include"),
-        "-o",
-        out_path,
-        *[os.path.join(CSRC, s) for s in SOURCES],
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libquest.so next to this file and return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = build_command(tmp)
+def compile_command(source: str, obj: str) -> list[str]:
+    return [hipcc_path(), *compile_flags(), "-c", os.path.join(CSRC, source), "-o", obj]
+
+
+def link_command(objs: list[str], out_path: str) -> list[str]:
+    return [hipcc_path(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_path, *objs]
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
+    text = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if NOISE not in line)
     if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose:
-        noise = "is not a recognized feature for this target"
-        for line in (res.stdout + res.stderr).splitlines():
-            if noise not in line:
-                print(line)
+        sys.stderr.write(text + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd)}")
+    if verbose and text.strip():
+        print(text)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile libquest.so next to this file (every time) and return its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        list(pool.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+    tmp = LIB_PATH + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -122,12 +122,13 @@ quest_status check_shape(int64_t rows, int64_t cols, int multiple_of) {
 
 quest_status from_hip(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_EHIP; }
 
-// Forward with codes (null allowed unless codes_required) and an optional
-// dequantised output (dq null = none; required when dq_dtype is given by
-// quest_quantize_fwd_dq).  Checks every argument before launching.
+// Forward with codes (null allowed unless codes_required), an optional
+// dequantised output (null allowed unless dq_required; dq_dtype is checked
+// only when dq is given) and the outer trust factor.  Checks every argument
+// before launching.
 quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
-                                 uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, void* dq,
-                                 quest_dtype dq_dtype, void* stream);
+                                 double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
+                                 void* dq, quest_dtype dq_dtype, bool dq_required, void* stream);
 
 }  // namespace
 
@@ -164,19 +165,27 @@ const char* quest_status_string(quest_status s) {
 
 quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                 uint8_t* codes, float* scale, uint8_t* mask, void* stream) {
-  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, codes, true, scale, mask, nullptr, QUEST_BF16, stream);
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, true, scale, mask, nullptr, QUEST_BF16,
+                             false, stream);
 }
 
 quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                    uint8_t* codes, float* scale, uint8_t* mask, void* dq, quest_dtype dq_dtype,
                                    void* stream) {
-  if (!dtype_ok(dq_dtype)) return QUEST_EINVAL;
-  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, codes, false, scale, mask, dq, dq_dtype, stream);
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, false, scale, mask, dq, dq_dtype, true,
+                             stream);
+}
+
+quest_status quest_quantize_fwd_ex(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                   double trust, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                                   quest_dtype dq_dtype, void* stream) {
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, trust, codes, false, scale, mask, dq, dq_dtype, false,
+                             stream);
 }
 
 quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,
                               quest_dtype out_dtype, void* stream) {
-  if (b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (b < 1 || b > kMaxBits) return QUEST_EUNSUPPORTED;
   if (!dtype_ok(out_dtype)) return QUEST_EINVAL;
   const quest_status sh = check_shape(rows, cols, 64);
   if (sh != QUEST_OK) return sh;
@@ -214,15 +223,17 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
 namespace {
 
 quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
-                                 uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, void* dq,
-                                 quest_dtype dq_dtype, void* stream) {
+                                 double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
+                                 void* dq, quest_dtype dq_dtype, bool dq_required, void* stream) {
   const int lb = log2_block(block);
-  if (lb < 0 || b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (lb < 0 || b < 1 || b > kMaxBits) return QUEST_EUNSUPPORTED;
   if (!dtype_ok(x_dtype)) return QUEST_EINVAL;
+  if ((dq || dq_required) && !dtype_ok(dq_dtype)) return QUEST_EINVAL;
+  if (!(trust >= 0.0) || !std::isfinite(trust)) return QUEST_EINVAL;
   const quest_status sh = check_shape(rows, cols, block);
   if (sh != QUEST_OK) return sh;
   if (rows == 0) return QUEST_OK;
-  if (!x || !scale || !mask || (codes_required && !codes) || (!codes_required && !dq)) return QUEST_EINVAL;
+  if (!x || !scale || !mask || (codes_required && !codes) || (dq_required && !dq)) return QUEST_EINVAL;
   if (!aligned16(x) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(mask) ||
       (dq && !aligned16(dq)))
     return QUEST_EALIGN;
@@ -236,11 +247,20 @@ quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t row
       overlaps(dq, nd, x, nx) || overlaps(dq, nd, codes, nc) || overlaps(dq, nd, scale, ns) ||
       overlaps(dq, nd, mask, nm))
     return QUEST_EINVAL;
-  const double alpha = quest_fit_alpha(b);
   std::call_once(g_env_once, read_env);
+  quest::FwdLaunch a;
+  a.rows = rows;
+  a.cols = cols;
+  a.alpha = quest_fit_alpha(b);
+  a.trust = trust;
+  a.allow_mfma = g_allow_mfma;
+  a.codes = codes;
+  a.scale = scale;
+  a.mask = mask;
+  a.dq = dq;
+  a.stream = static_cast<hipStream_t>(stream);
   const int dq_kind = dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
-  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, rows, cols, lb, b, alpha, g_allow_mfma, codes,
-                                             scale, mask, dq, dq_kind, static_cast<hipStream_t>(stream)));
+  return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, lb, b, dq_kind, a));
 }
 
 }  // namespace

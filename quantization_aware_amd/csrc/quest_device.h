@@ -647,7 +647,8 @@ __device__ __forceinline__ void put_code(CodeWords<B>& cw, int j, uint32_t code)
   if (off + B > 32) cw.w[wi + 1] |= code >> (32 - off);
 }
 
-// Store the codes of run `lane` of a window (4 B bytes per run).
+// Store the codes of run `lane` of a window (4 B bytes per run): one access
+// of 4..16 bytes for b <= 4, a 16-byte access plus one of 4..16 bytes above.
 template <int B>
 __device__ __forceinline__ void store_codes(rsrc_t r, int lane, const CodeWords<B>& cw) {
   const int off = lane * 4 * B;
@@ -659,6 +660,16 @@ __device__ __forceinline__ void store_codes(rsrc_t r, int lane, const CodeWords<
     __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[0], cw.w[1], cw.w[2]}, r, off, 0, kNonTemporal);
   } else {
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[0], cw.w[1], cw.w[2], cw.w[3]}, r, off, 0, kNonTemporal);
+    if constexpr (B == 5) {
+      __builtin_amdgcn_raw_buffer_store_b32(cw.w[4], r, off + 16, 0, kNonTemporal);
+    } else if constexpr (B == 6) {
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[4], cw.w[5]}, r, off + 16, 0, kNonTemporal);
+    } else if constexpr (B == 7) {
+      __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[4], cw.w[5], cw.w[6]}, r, off + 16, 0, kNonTemporal);
+    } else if constexpr (B == 8) {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[4], cw.w[5], cw.w[6], cw.w[7]}, r, off + 16, 0,
+                                             kNonTemporal);
+    }
   }
 }
 
@@ -694,6 +705,24 @@ __device__ __forceinline__ CodeWords<B> load_codes(rsrc_t r, int lane) {
     cw.w[1] = t.y;
     cw.w[2] = t.z;
     cw.w[3] = t.w;
+    if constexpr (B == 5) {
+      cw.w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16, 0, 0);
+    } else if constexpr (B == 6) {
+      const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, 0);
+      cw.w[4] = h.x;
+      cw.w[5] = h.y;
+    } else if constexpr (B == 7) {
+      const u32x3 h = __builtin_amdgcn_raw_buffer_load_b96(r, off + 16, 0, 0);
+      cw.w[4] = h.x;
+      cw.w[5] = h.y;
+      cw.w[6] = h.z;
+    } else if constexpr (B == 8) {
+      const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+      cw.w[4] = h.x;
+      cw.w[5] = h.y;
+      cw.w[6] = h.z;
+      cw.w[7] = h.w;
+    }
   }
   return cw;
 }

@@ -1,4 +1,7 @@
-// The three kernels of libquest and their launchers (gfx950).
+// The kernels of libquest (gfx950) and the templates that launch them.  The
+// translation units quest_fwd_*.hip instantiate the forward for one output
+// type each, quest_launch.hip the rest, so the build compiles them in
+// parallel.
 //
 // Forward (QuEST quantiser; atlas.scime.ai summary of QuEST, "Approach";
 // pith.science review of QuEST, "What carries the argument"):
@@ -12,6 +15,8 @@
 // unnormalised (entries scaled by sqrt(n)); codes and mask only depend on
 // y / Delta, so the factor is folded into per-row constants instead of
 // costing a multiply per element.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,7 +68,7 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
     push16_nonneg(w, p + 16);
     push16_nonneg(w, p);
     cw.w[0] = w;
-  } else if constexpr (B == 2 || B == 4) {
+  } else if constexpr (B == 2 || B == 4 || B == 8) {
     // u = clamp(floor(y / Delta + L/2), 0, L-1) = RNE(min(y / Delta + (L-1)/2, L-1)), saturated
     // at 0 by v_cvt_pk_u8_f32; the two differ only when y / Delta is exactly an integer
     // (y exactly on a decision threshold), where round-to-even may pick the upper code.
@@ -91,7 +96,7 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
       cw.w[w] = word;
     }
   } else {
-    // b = 3: codes straddle dword boundaries; clamp(floor(t), 0, L-1) = trunc(clamp(t, 0, L-1)).
+    // b = 3, 5, 6, 7: codes straddle dword boundaries; clamp(floor(t), 0, L-1) = trunc(clamp(t, 0, L-1)).
 #pragma unroll
     for (int i = 0; i < B; ++i) cw.w[i] = 0u;
 #pragma unroll
@@ -108,6 +113,7 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
 // quantise_run, on 8 entries.
 template <int B>
 __device__ __forceinline__ uint32_t quantise8(const float* v, float kk) {
+  static_assert(B >= 1 && B <= 4, "8 codes of at most 4 bits fit one dword");
   constexpr float L = static_cast<float>(1 << B);
   if constexpr (B == 1) {
     float p[8];
@@ -207,7 +213,7 @@ __device__ __forceinline__ void grid_values(const float* v, float kk, float c, f
     float u;
     if constexpr (B == 1) {
       u = v[i] * kk >= 0.f ? 1.f : 0.f;
-    } else if constexpr (B == 2 || B == 4) {
+    } else if constexpr (B == 2 || B == 4 || B == 8) {
       const float t = __builtin_fminf(__builtin_fmaf(v[i], kk, 0.5f * (L - 1.f)), L - 1.f);
       u = __builtin_fmaxf(__builtin_rintf(t), 0.f);
     } else {
@@ -688,9 +694,7 @@ __global__ void __launch_bounds__(256)
 // ----------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------
-namespace {
-
-int gcd_int(int a, int b) {
+inline int gcd_int(int a, int b) {
   while (b) {
     const int t = a % b;
     a = b;
@@ -699,7 +703,7 @@ int gcd_int(int a, int b) {
   return a;
 }
 
-int log2_exact(int v) {
+inline int log2_exact(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
   return l;
@@ -710,17 +714,7 @@ int log2_exact(int v) {
 // loads run ahead of the arithmetic.
 constexpr int64_t kFwdTileWorkgroups = 512;
 
-// Arguments of one forward launch, already validated.
-struct FwdLaunch {
-  int64_t rows, cols;
-  double alpha;
-  bool allow_mfma;
-  uint8_t* codes;  // may be null: codes are not written
-  float* scale;
-  uint8_t* mask;
-  void* dq;  // dequantised output (type chosen by the caller), or null
-  hipStream_t stream;
-};
+
 
 template <typename In, int LOGN, int B, typename Dq>
 hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
@@ -730,12 +724,13 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
   FwdConsts k;
   k.alpha = static_cast<float>(a.alpha);
   k.kk = static_cast<float>((L - 1.0) / (2.0 * a.alpha * sqrt_n));
-  k.thr = static_cast<float>(a.alpha * L * sqrt_n / (L - 1.0));
+  // Trusted: |y| <= s + trust * Delta / 2, i.e. |v| <= alpha sqrt(n) (1 + trust / (L - 1)) RMS.
+  k.thr = static_cast<float>(a.alpha * sqrt_n * (1.0 + a.trust / (L - 1.0)));
   k.inv_cols = static_cast<float>(1.0 / double(a.cols));
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(a.mask);
   Dq* dq = static_cast<Dq*>(a.dq);
   hipStream_t stream = a.stream;
-  if constexpr (sizeof(In) == 2) {
+  if constexpr (sizeof(In) == 2 && B <= 4) {
     if (a.allow_mfma && runs_per_row > 64 && runs_per_row % 16 == 0) {
       int rows_per_wg = 64 / gcd_int(runs_per_row, 64);
       if (rows_per_wg * runs_per_row > 1024) rows_per_wg = 1024 / runs_per_row;
@@ -792,7 +787,11 @@ hipError_t fwd_dispatch_bits(const In* x, int bits, const FwdLaunch& a) {
     case 1: return fwd_dispatch<In, LOGN, 1, Dq>(x, a);
     case 2: return fwd_dispatch<In, LOGN, 2, Dq>(x, a);
     case 3: return fwd_dispatch<In, LOGN, 3, Dq>(x, a);
-    default: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
+    case 4: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
+    case 5: return fwd_dispatch<In, LOGN, 5, Dq>(x, a);
+    case 6: return fwd_dispatch<In, LOGN, 6, Dq>(x, a);
+    case 7: return fwd_dispatch<In, LOGN, 7, Dq>(x, a);
+    default: return fwd_dispatch<In, LOGN, 8, Dq>(x, a);
   }
 }
 
@@ -805,14 +804,6 @@ hipError_t fwd_dispatch_block(const In* x, int log_block, int bits, const FwdLau
   }
 }
 
-template <typename In>
-hipError_t fwd_dispatch_dq(const In* x, int log_block, int bits, int dq_kind, const FwdLaunch& a) {
-  switch (dq_kind) {
-    case 1: return fwd_dispatch_block<In, uint16_t>(x, log_block, bits, a);
-    case 2: return fwd_dispatch_block<In, float>(x, log_block, bits, a);
-    default: return fwd_dispatch_block<In, void>(x, log_block, bits, a);
-  }
-}
 
 template <typename G>
 hipError_t bwd_dispatch(const G* grad, const uint8_t* mask, int64_t rows, int64_t cols, int log_block, G* out,
@@ -837,56 +828,30 @@ hipError_t bwd_dispatch(const G* grad, const uint8_t* mask, int64_t rows, int64_
   return hipGetLastError();
 }
 
+template <typename Out, int B>
+hipError_t dequant_launch(const uint8_t* codes, const float* scale, int64_t total_runs, uint32_t runs_per_row, Out* out,
+                          hipStream_t stream) {
+  const uint32_t grid = static_cast<uint32_t>((total_runs + 255) / 256);
+  hipLaunchKernelGGL((quest_dequant_kernel<Out, B>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
+                     runs_per_row, out);
+  return hipGetLastError();
+}
+
 template <typename Out>
 hipError_t dequant_dispatch(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits, Out* out,
                             hipStream_t stream) {
   const uint32_t runs_per_row = static_cast<uint32_t>(cols / RUN);
   const int64_t total_runs = rows * runs_per_row;
-  const uint32_t grid = static_cast<uint32_t>((total_runs + 255) / 256);
   switch (bits) {
-    case 1:
-      hipLaunchKernelGGL((quest_dequant_kernel<Out, 1>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
-                         runs_per_row, out);
-      break;
-    case 2:
-      hipLaunchKernelGGL((quest_dequant_kernel<Out, 2>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
-                         runs_per_row, out);
-      break;
-    case 3:
-      hipLaunchKernelGGL((quest_dequant_kernel<Out, 3>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
-                         runs_per_row, out);
-      break;
-    default:
-      hipLaunchKernelGGL((quest_dequant_kernel<Out, 4>), dim3(grid), dim3(256), 0, stream, codes, scale, total_runs,
-                         runs_per_row, out);
-      break;
+    case 1: return dequant_launch<Out, 1>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 2: return dequant_launch<Out, 2>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 3: return dequant_launch<Out, 3>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 4: return dequant_launch<Out, 4>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 5: return dequant_launch<Out, 5>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 6: return dequant_launch<Out, 6>(codes, scale, total_runs, runs_per_row, out, stream);
+    case 7: return dequant_launch<Out, 7>(codes, scale, total_runs, runs_per_row, out, stream);
+    default: return dequant_launch<Out, 8>(codes, scale, total_runs, runs_per_row, out, stream);
   }
-  return hipGetLastError();
-}
-
-}  // namespace
-
-hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
-                               double alpha, bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
-                               int dq_kind, hipStream_t stream) {
-  const FwdLaunch a{rows, cols, alpha, allow_mfma, codes, scale, mask, dq, stream};
-  if (x_is_bf16) return fwd_dispatch_dq(static_cast<const uint16_t*>(x), log_block, bits, dq_kind, a);
-  return fwd_dispatch_dq(static_cast<const float*>(x), log_block, bits, dq_kind, a);
-}
-
-hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
-                             void* out, int out_is_bf16, hipStream_t stream) {
-  if (out_is_bf16) return dequant_dispatch(codes, scale, rows, cols, bits, static_cast<uint16_t*>(out), stream);
-  return dequant_dispatch(codes, scale, rows, cols, bits, static_cast<float*>(out), stream);
-}
-
-hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
-                            int log_block, void* grad_out, hipStream_t stream) {
-  if (g_is_bf16)
-    return bwd_dispatch(static_cast<const uint16_t*>(grad), mask, rows, cols, log_block,
-                        static_cast<uint16_t*>(grad_out), stream);
-  return bwd_dispatch(static_cast<const float*>(grad), mask, rows, cols, log_block, static_cast<float*>(grad_out),
-                      stream);
 }
 
 }  // namespace quest

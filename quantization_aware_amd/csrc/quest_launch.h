@@ -6,13 +6,28 @@
 
 namespace quest {
 
-// x_is_bf16: 1 = bf16 input, 0 = fp32.  allow_mfma: bf16 rows of 16 m runs
-// use the matrix-core transform.  codes may be null (not written).  dq_kind:
-// 0 = no dequantised output, 1 = bf16, 2 = fp32 into dq.  All sizes already
-// validated.
-hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int64_t rows, int64_t cols, int log_block, int bits,
-                               double alpha, bool allow_mfma, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
-                               int dq_kind, hipStream_t stream);
+// Arguments of one forward launch, already validated.
+struct FwdLaunch {
+  int64_t rows, cols;
+  double alpha;     // clip scale alpha_b
+  double trust;     // outer trust factor: trusted iff |y| <= s + trust * Delta / 2
+  bool allow_mfma;  // bf16 rows of 16 m runs (b <= 4) use the matrix-core transform
+  uint8_t* codes;   // may be null: codes are not written
+  float* scale;
+  uint8_t* mask;
+  void* dq;  // dequantised output (type given by dq_kind), or null
+  hipStream_t stream;
+};
+
+// x_is_bf16: 1 = bf16 input, 0 = fp32.  dq_kind: 0 = no dequantised output,
+// 1 = bf16, 2 = fp32 into a.dq.  All sizes already validated.
+hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int log_block, int bits, int dq_kind,
+                               const FwdLaunch& a);
+
+// The forward for one dequantised-output type (separate translation units).
+hipError_t launch_fwd_nodq(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
+hipError_t launch_fwd_dq_bf16(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
+hipError_t launch_fwd_dq_f32(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
                              void* out, int out_is_bf16, hipStream_t stream);

@@ -19,18 +19,26 @@ from __future__ import annotations
 
 import torch
 
-from . import quantize_fwd_dq, trust_bwd
+from . import quantize_fwd_ex, trust_bwd
 
-__all__ = ["QuestLinearFunction", "quest_linear", "QuestLinear"]
+__all__ = ["QuestLinearFunction", "quest_linear", "QuestLinear", "default_trust", "ONE_BIT_OUTER_TRUST"]
+
+
+ONE_BIT_OUTER_TRUST = 1.30  # pith.science review of QuEST, "Assumptions & free parameters" (s*)
+
+
+def default_trust(bits: int) -> float:
+    """Outer trust factor used when none is given: 1.30 at 1 bit, 1 otherwise."""
+    return ONE_BIT_OUTER_TRUST if bits == 1 else 1.0
 
 
 class QuestLinearFunction(torch.autograd.Function):
     """y = Q(x) Q(w)^T for 2-D x (N x K) and w (M x K), K a multiple of `block`."""
 
     @staticmethod
-    def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype):
-        _, _, mask_x, qx = quantize_fwd_dq(x, block, bits_x, dq_dtype=compute_dtype, with_codes=False)
-        _, _, mask_w, qw = quantize_fwd_dq(w, block, bits_w, dq_dtype=compute_dtype, with_codes=False)
+    def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype, trust_x=1.0, trust_w=1.0):
+        _, _, mask_x, qx = quantize_fwd_ex(x, block, bits_x, trust=trust_x, with_codes=False, dq_dtype=compute_dtype)
+        _, _, mask_w, qw = quantize_fwd_ex(w, block, bits_w, trust=trust_w, with_codes=False, dq_dtype=compute_dtype)
         y = torch.nn.functional.linear(qx, qw)
         ctx.save_for_backward(qx, qw, mask_x, mask_w)
         ctx.block = block
@@ -50,15 +58,22 @@ class QuestLinearFunction(torch.autograd.Function):
             # products with a transposed operand view are avoided)
             g = torch.mm(dy.t().contiguous(), qx)
             dw = trust_bwd(g, mask_w, ctx.block, out=g).to(ctx.w_dtype)
-        return dx, dw, None, None, None, None
+        return dx, dw, None, None, None, None, None, None
 
 
 def quest_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None, block: int = 128,
-                 bits_x: int = 4, bits_w: int = 4, compute_dtype=torch.bfloat16) -> torch.Tensor:
-    """QuEST linear map of x (..., K) by w (M, K); leading axes of x are flattened."""
+                 bits_x: int = 4, bits_w: int = 4, compute_dtype=torch.bfloat16, trust_x: float | None = None,
+                 trust_w: float | None = None) -> torch.Tensor:
+    """QuEST linear map of x (..., K) by w (M, K); leading axes of x are flattened.
+
+    trust_x / trust_w: outer trust factors; by default 1.30 for 1-bit operands
+    (the factor the pages tune for their 1-bit runs) and 1 otherwise.
+    """
+    trust_x = default_trust(bits_x) if trust_x is None else trust_x
+    trust_w = default_trust(bits_w) if trust_w is None else trust_w
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1]).contiguous()
-    y = QuestLinearFunction.apply(x2, w.contiguous(), block, bits_x, bits_w, compute_dtype)
+    y = QuestLinearFunction.apply(x2, w.contiguous(), block, bits_x, bits_w, compute_dtype, trust_x, trust_w)
     if bias is not None:
         y = y + bias.to(y.dtype)
     return y.reshape(*lead, w.shape[0])
@@ -68,14 +83,18 @@ class QuestLinear(torch.nn.Module):
     """Drop-in linear layer trained with QuEST quantisation of weights and activations."""
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True, block: int = 128, bits_x: int = 4,
-                 bits_w: int = 4, compute_dtype=torch.bfloat16, device=None, dtype=None):
+                 bits_w: int = 4, compute_dtype=torch.bfloat16, trust_x: float | None = None,
+                 trust_w: float | None = None, device=None, dtype=None):
         super().__init__()
         if in_features % block:
             raise ValueError(f"in_features ({in_features}) must be a multiple of the Hadamard block ({block})")
         self.block, self.bits_x, self.bits_w, self.compute_dtype = block, bits_x, bits_w, compute_dtype
+        self.trust_x = default_trust(bits_x) if trust_x is None else trust_x
+        self.trust_w = default_trust(bits_w) if trust_w is None else trust_w
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
         self.bias = torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=dtype)) if bias else None
         torch.nn.init.kaiming_uniform_(self.weight, a=5 ** 0.5)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return quest_linear(x, self.weight, self.bias, self.block, self.bits_x, self.bits_w, self.compute_dtype)
+        return quest_linear(x, self.weight, self.bias, self.block, self.bits_x, self.bits_w, self.compute_dtype,
+                            self.trust_x, self.trust_w)

@@ -27,22 +27,25 @@ TOL_F32 = 1e-5
 TOL_BF16 = 2e-2
 
 
-def exempt_entries(y: np.ndarray, s: np.ndarray, b: int, band: float = BAND) -> np.ndarray:
-    """True where y lies within band * s_r of a decision or trust threshold."""
+def exempt_entries(y: np.ndarray, s: np.ndarray, b: int, band: float = BAND, trust: float = 1.0) -> np.ndarray:
+    """True where y lies within band * s_r of a decision or trust threshold.
+
+    The trust threshold is s_r (1 + trust / (L - 1)) (s_r L / (L - 1) for trust 1).
+    """
     big_l = 1 << b
     s = np.asarray(s, dtype=np.float64)[:, None]
     delta = 2.0 * s / (big_l - 1)
     safe = np.where(delta == 0.0, 1.0, delta)
     j = np.clip(np.round(y / safe), -(big_l // 2 - 1), big_l // 2 - 1)
     near_decision = np.abs(y - j * safe) <= band * s
-    near_trust = np.abs(np.abs(y) - s * big_l / (big_l - 1)) <= band * s
+    near_trust = np.abs(np.abs(y) - s * (1.0 + trust / (big_l - 1))) <= band * s
     ex = near_decision | near_trust
     ex[(delta == 0.0)[:, 0], :] = False
     return ex
 
 
 def check_fwd(x64: np.ndarray, block: int, b: int, codes, scale, mask, ref=None,
-              max_fraction: float | None = MAX_MISMATCH_FRACTION) -> dict:
+              max_fraction: float | None = MAX_MISMATCH_FRACTION, trust: float = 1.0) -> dict:
     """Assert GPU forward outputs (numpy uint8 / float32 arrays) match the oracle on x64.
 
     max_fraction bounds the share of entries (all inside the band) that differ.  It is a
@@ -51,13 +54,13 @@ def check_fwd(x64: np.ndarray, block: int, b: int, codes, scale, mask, ref=None,
     """
     rows, cols = x64.shape
     if ref is None:
-        ref = qo.quantize_fwd(x64, block, b)
+        ref = qo.quantize_fwd(x64, block, b, trust=trust)
     codes = np.asarray(codes).reshape(rows, cols * b // 8)
     mask = np.asarray(mask).reshape(rows, cols // 8)
     scale = np.asarray(scale, dtype=np.float64).reshape(rows)
     u = qo.unpack_lsb_first(codes, b, cols)
     m = qo.unpack_lsb_first(mask, 1, cols).astype(bool)
-    ex = exempt_entries(ref["y"], ref["scale"], b)
+    ex = exempt_entries(ref["y"], ref["scale"], b, trust=trust)
     bad_u = u != ref["u"]
     bad_m = m != ref["m"]
     hard_u = bad_u & ~ex

@@ -113,7 +113,7 @@ def test_empty_calls_are_noops(lib):
         (dict(block=512), qa.QUEST_EUNSUPPORTED),
         (dict(block=100), qa.QUEST_EUNSUPPORTED),
         (dict(b=0), qa.QUEST_EUNSUPPORTED),
-        (dict(b=5), qa.QUEST_EUNSUPPORTED),
+        (dict(b=9), qa.QUEST_EUNSUPPORTED),
         (dict(dt=7), qa.QUEST_EINVAL),
         (dict(rows=-1), qa.QUEST_EINVAL),
         (dict(cols=0), qa.QUEST_EINVAL),
@@ -171,7 +171,7 @@ def test_bwd_rejects(lib, kw, status):
     "kw,status",
     [
         (dict(b=0), qa.QUEST_EUNSUPPORTED),
-        (dict(b=8), qa.QUEST_EUNSUPPORTED),
+        (dict(b=9), qa.QUEST_EUNSUPPORTED),
         (dict(dt=5), qa.QUEST_EINVAL),
         (dict(cols=96), qa.QUEST_EINVAL),
         (dict(rows=-1), qa.QUEST_EINVAL),
@@ -203,7 +203,7 @@ def test_fwd_dq_empty_call_is_a_noop(lib):
     "kw,status",
     [
         (dict(block=32), qa.QUEST_EUNSUPPORTED),
-        (dict(b=5), qa.QUEST_EUNSUPPORTED),
+        (dict(b=9), qa.QUEST_EUNSUPPORTED),
         (dict(dt=7), qa.QUEST_EINVAL),
         (dict(dq_dt=3), qa.QUEST_EINVAL),
         (dict(cols=320), qa.QUEST_EINVAL),
@@ -224,6 +224,44 @@ def test_fwd_dq_empty_call_is_a_noop(lib):
 )
 def test_fwd_dq_rejects(lib, kw, status):
     assert fwd_dq(lib, **kw) == status
+
+
+def fwd_ex(lib, x=A, dt=qa.QUEST_BF16, rows=4, cols=256, block=128, b=4, trust=1.0, codes=B_, scale=C_, mask=D_,
+           dq=E_, dq_dt=qa.QUEST_BF16):
+    return lib.quest_quantize_fwd_ex(x, dt, rows, cols, block, b, trust, codes, scale, mask, dq, dq_dt, None)
+
+
+def test_fwd_ex_empty_call_is_a_noop(lib):
+    assert fwd_ex(lib, x=None, codes=None, scale=None, mask=None, dq=None, rows=0) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(b=9), qa.QUEST_EUNSUPPORTED),
+        (dict(b=0), qa.QUEST_EUNSUPPORTED),
+        (dict(trust=-0.5), qa.QUEST_EINVAL),
+        (dict(trust=float("nan")), qa.QUEST_EINVAL),
+        (dict(trust=float("inf")), qa.QUEST_EINVAL),
+        (dict(dq_dt=4), qa.QUEST_EINVAL),
+        (dict(x=None), qa.QUEST_EINVAL),
+        (dict(mask=None), qa.QUEST_EINVAL),
+        (dict(codes=B_ + 2), qa.QUEST_EALIGN),
+        (dict(dq=E_ + 2), qa.QUEST_EALIGN),
+        (dict(dq=A), qa.QUEST_EINVAL),
+        (dict(codes=None, dq=D_), qa.QUEST_EINVAL),  # dq == mask
+        (dict(b=8, codes=C_ - 512), qa.QUEST_EINVAL),  # 8-bit codes (1024 B) run over scale
+    ],
+)
+def test_fwd_ex_rejects(lib, kw, status):
+    assert fwd_ex(lib, **kw) == status
+
+
+def test_fwd_ex_unknown_dq_dtype_ignored_without_dq(lib):
+    # dq_dtype is only read when dq is given: with no dq an empty call still succeeds,
+    # with a dq it is rejected.
+    assert fwd_ex(lib, dq=None, dq_dt=9, rows=0) == qa.QUEST_OK
+    assert fwd_ex(lib, dq_dt=9, rows=0) == qa.QUEST_EINVAL
 
 
 def test_fwd_still_requires_codes(lib):

@@ -26,7 +26,7 @@ import torch
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
-from quantization_aware_amd.linear import QuestLinear, quest_linear
+from quantization_aware_amd.linear import QuestLinear, default_trust, quest_linear
 from quest_inputs import TensorSpec, make_tensor, to_float64
 from parity import exempt_entries
 
@@ -77,7 +77,7 @@ def close(got: torch.Tensor, ref: np.ndarray, what: str, tols, skip=None, block=
     assert rel <= tol_norm, f"{what}: relative Frobenius error {rel} (outside the band's reach)"
 
 
-def band_reach(f: dict, bx: int, bw: int, block: int):
+def band_reach(f: dict, bx: int, bw: int, block: int, trust_x: float = 1.0, trust_w: float = 1.0):
     """Entries of y, dx and dw that an operand entry inside the threshold band can move.
 
     A band entry (within 1e-6 s of a decision or trust threshold) may take the
@@ -85,8 +85,8 @@ def band_reach(f: dict, bx: int, bw: int, block: int):
     shifts its row of y, dx or dw and, through the other operand's product,
     the Hadamard block of its column.
     """
-    bx_ = exempt_entries(f["fx"]["y"], f["fx"]["scale"], bx)
-    bw_ = exempt_entries(f["fw"]["y"], f["fw"]["scale"], bw)
+    bx_ = exempt_entries(f["fx"]["y"], f["fx"]["scale"], bx, trust=trust_x)
+    bw_ = exempt_entries(f["fw"]["y"], f["fw"]["scale"], bw, trust=trust_w)
     rx, rw = bx_.any(axis=1), bw_.any(axis=1)
     k = bx_.shape[1]
     blk_x = np.repeat(bx_.reshape(bx_.shape[0], k // block, block).any(axis=(0, 2)), block)
@@ -114,9 +114,9 @@ def test_linear_matches_oracle(dev, n, k, m, block, bx, bw, compute_dtype):
     y = quest_linear(xg, wg, block=block, bits_x=bx, bits_w=bw, compute_dtype=compute_dtype)
     y.backward(dy.to(compute_dtype))
     torch.cuda.synchronize()
-    f = qo.qat_linear_fwd(to_float64(x), to_float64(w), block, bx, bw)
+    f = qo.qat_linear_fwd(to_float64(x), to_float64(w), block, bx, bw, default_trust(bx), default_trust(bw))
     dx_ref, dw_ref = qo.qat_linear_bwd(to_float64(dy), f, block)
-    skip_y, skip_dx, skip_dw = band_reach(f, bx, bw, block)
+    skip_y, skip_dx, skip_dw = band_reach(f, bx, bw, block, default_trust(bx), default_trust(bw))
     log(f"band reach: {int(skip_y.sum())} of y, {int(skip_dx.sum())} of dx, {int(skip_dw.sum())} of dw")
     close(y.detach(), f["y"], "y", tols, skip_y)
     close(xg.grad, dx_ref, "dx", tols, skip_dx, block)

@@ -239,7 +239,7 @@ def test_shapes_bwd(dev, rows, cols, block, dt):
     check_grad(out.float().cpu().numpy(), expect, block, TOL_F32 if dt == "f32" else TOL_BF16)
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("cols", [64, 640, 5632])
 def test_shapes_dequantize(dev, b, cols):
     rows = 37
@@ -457,3 +457,64 @@ def test_fwd_dq(dev, rows, cols, block, dt, b, dq_dtype, with_codes):
     ex = exempt_entries(ref["y"], ref["scale"], b)
     check_values(dq.float().cpu().numpy(), qo.dequantize(ref["codes"], ref["scale"], cols, b),
                  TOL_BF16 if dq_dtype == torch.bfloat16 else TOL_F32, skip=ex)
+
+
+# ---------------------------------------------------------------------------
+# 5..8-bit codes (vector-ALU kernels for every input), and the outer trust
+# factor (quest_quantize_fwd_ex).
+# ---------------------------------------------------------------------------
+WIDE_BITS_SHAPES = [
+    (96, 2048, 128, "bf16"),  # tiles (bf16 rows that take the matrix cores at b <= 4)
+    (33, 256, 64, "f32"),
+    (7, 5632, 256, "bf16"),  # rows
+    (1000, 640, 64, "bf16"),
+    (5, 32768, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("rows,cols,block,dt", WIDE_BITS_SHAPES)
+@pytest.mark.parametrize("b", [5, 6, 7, 8])
+def test_wide_bits_fwd_and_dequantize(dev, rows, cols, block, dt, b):
+    spec = TensorSpec(f"wide{rows}x{cols}", rows, cols, dt, "student_t", 4, 8600 + rows + cols + b,
+                      outlier_cols=max(1, cols // 100), outlier_scale=20.0)
+    log(f"{b}-bit fwd {rows}x{cols} block {block} {dt}")
+    x = make_tensor(spec, dev)
+    codes, scale, mask = fwd_gpu(x, block, b)
+    _, _, _, dq = qa.quantize_fwd_dq(x, block, b, dq_dtype=torch.float32)
+    torch.cuda.synchronize()
+    x64 = to_float64(x)
+    ref = qo.quantize_fwd(x64, block, b)
+    check_fwd(x64, block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), ref=ref)
+    check_values(dq.cpu().numpy(), qo.dequantize(ref["codes"], ref["scale"], cols, b), TOL_F32,
+                 skip=exempt_entries(ref["y"], ref["scale"], b))
+
+
+TRUST_CASES = [
+    # rows, cols, block, dtype, b, trust
+    (130, 2048, 128, "bf16", 1, 1.3),  # matrix-core tiles; the 1-bit outer trust factor of the pages
+    (64, 512, 64, "bf16", 4, 0.0),
+    (9, 5632, 128, "bf16", 1, 1.3),  # matrix-core rows
+    (40, 1024, 256, "f32", 2, 2.0),  # vector-ALU tiles
+    (300, 768, 64, "bf16", 3, 0.5),  # vector-ALU rows
+    (17, 2048, 128, "f32", 6, 1.3),
+]
+
+
+@pytest.mark.parametrize("rows,cols,block,dt,b,trust", TRUST_CASES)
+def test_outer_trust_factor(dev, rows, cols, block, dt, b, trust):
+    spec = TensorSpec(f"trust{rows}x{cols}", rows, cols, dt, "student_t", 3, 8700 + rows + cols + b,
+                      outlier_cols=max(1, cols // 100), outlier_scale=20.0)
+    log(f"trust {trust} b={b} fwd {rows}x{cols} block {block} {dt}")
+    x = make_tensor(spec, dev)
+    codes, scale, mask, dq = qa.quantize_fwd_ex(x, block, b, trust=trust, dq_dtype=torch.bfloat16)
+    c1, s1, m1 = fwd_gpu(x, block, b)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, c1) and torch.equal(scale, s1)  # the factor only moves the mask
+    x64 = to_float64(x)
+    ref = qo.quantize_fwd(x64, block, b, trust=trust)
+    stats = check_fwd(x64, block, b, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), ref=ref,
+                      trust=trust)
+    m_ref1 = qo.quantize_fwd(x64, block, b)["m"]
+    if trust != 1.0:
+        assert (ref["m"] != m_ref1).any(), "the factor should change some mask bits on heavy-tailed rows"
+    log(f"  {stats}")

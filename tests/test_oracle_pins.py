@@ -219,7 +219,7 @@ def _brute_force_codes(y, s, b):
     return out
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_codes_equal_brute_force_nearest_level(b):
     rng = np.random.default_rng(100 + b)
     y = rng.standard_normal((8, 256)) * rng.uniform(0.5, 3, size=(8, 1))
@@ -229,7 +229,7 @@ def test_codes_equal_brute_force_nearest_level(b):
     assert np.array_equal(u, bf)
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_scale_from_original_domain_norm(b):
     # Orthogonality: the Hadamard-domain RMS equals ||x_row|| / sqrt(C); s = alpha_b * that.
     rng = np.random.default_rng(200 + b)
@@ -240,10 +240,11 @@ def test_scale_from_original_domain_norm(b):
     assert np.max(np.abs(out["scale"] - expect) / expect) <= 1e-13
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_mask_closed_form(b):
     rng = np.random.default_rng(300 + b)
-    y = rng.standard_normal((16, 512)) * 1.7
+    # Gaussian rows for b <= 4; beyond, alpha_b lies past the sample's range, so heavy tails
+    y = (rng.standard_normal((16, 512)) if b <= 4 else rng.standard_t(3, size=(16, 512))) * 1.7
     u, s, m, q = qo.quantize_rows(y, b, qo.fit_alpha(b))
     big_l = 1 << b
     thr = s[:, None] * big_l / (big_l - 1)
@@ -269,7 +270,7 @@ def _place_at_fraction_of_threshold(rest, b, kappa, j_steps):
     return c * math.sqrt(float(np.sum(rest**2)) / (cols - c * c))
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_mask_and_codes_on_both_sides_of_each_threshold(b):
     # Trust threshold: the outer level sits at s, so a clipped entry is within half a step
     # exactly when |y| <= s + Delta/2 = (L/2) Delta.  Decision thresholds sit at j Delta.
@@ -296,7 +297,7 @@ def test_mask_and_codes_on_both_sides_of_each_threshold(b):
                 assert m[0, 0]
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_scale_invariance_and_sign_symmetry(b):
     rng = np.random.default_rng(400 + b)
     x = rng.standard_normal((4, 256))
@@ -312,7 +313,7 @@ def test_scale_invariance_and_sign_symmetry(b):
     assert np.array_equal(neg["m"], base["m"])
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_untrusted_fraction_for_gaussian_rows(b):
     # iid N(0,1) stays iid N(0,1) under an orthonormal transform, so the untrusted
     # fraction is P(|X| > alpha_b L/(L-1)) = 2 (1 - Phi(alpha_b L/(L-1))).
@@ -351,7 +352,7 @@ def test_zero_row_reading():
         assert np.all(qo.dequantize(out["codes"], out["scale"], 128, b)[0] == 0.0)
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_vectorised_quantiser_matches_scalar_loop(b):
     rng = np.random.default_rng(700 + b)
     y = rng.standard_normal((4, 128)) * 2.0
@@ -385,7 +386,7 @@ def test_packing_rejects_out_of_range():
         qo.pack_lsb_first(np.array([[16, 0]]), 4)
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_dequantize_returns_grid_values(b):
     rng = np.random.default_rng(900 + b)
     x = rng.standard_normal((6, 384)) * 3
@@ -512,3 +513,61 @@ def test_qat_linear_untrusted_entries_get_no_gradient():
     assert np.abs(gw[~f["fw"]["m"]]).max() <= 1e-12 * np.abs(gw).max()
     assert np.allclose(gx[f["fx"]["m"]], (dy @ f["qw"])[f["fx"]["m"]], rtol=1e-12, atol=1e-12)
     assert np.allclose(gw[f["fw"]["m"]], (dy.T @ f["qx"])[f["fw"]["m"]], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Outer trust factor (the 1-bit runs use s* = 1.30).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+@pytest.mark.parametrize("trust", [0.0, 0.5, 1.3, 2.0])
+def test_trust_factor_closed_form(b, trust):
+    # Trusted iff |y| <= s + trust * Delta / 2 = s (1 + trust / (L - 1)), away from the boundary.
+    rng = np.random.default_rng(90 + b)
+    y = rng.standard_t(4, size=(64, 256))
+    alpha = qo.fit_alpha(b)
+    _, s, m, _ = qo.quantize_rows(y, b, alpha, trust)
+    bound = s[:, None] * (1.0 + trust / ((1 << b) - 1))
+    clear = np.abs(np.abs(y) - bound) > 1e-9 * s[:, None]
+    assert np.array_equal(m[clear], (np.abs(y) <= bound)[clear])
+
+
+def test_trust_factor_one_is_the_plain_mask_and_monotone():
+    rng = np.random.default_rng(91)
+    y = rng.standard_t(3, size=(32, 512))
+    alpha = qo.fit_alpha(2)
+    _, _, m1, _ = qo.quantize_rows(y, 2, alpha)
+    _, _, m1b, q = qo.quantize_rows(y, 2, alpha, 1.0)
+    delta = 2.0 * alpha * np.sqrt(np.mean(y * y, axis=1)) / 3.0
+    assert np.array_equal(m1, m1b) and np.array_equal(m1, np.abs(q - y) <= delta[:, None] / 2.0)
+    prev = None
+    for t in (0.0, 0.3, 1.0, 1.3, 4.0):
+        _, _, m, _ = qo.quantize_rows(y, 2, alpha, t)
+        if prev is not None:
+            assert np.all(m >= prev)  # a larger outer region trusts a superset
+        prev = m
+    _, s, m0, _ = qo.quantize_rows(y, 2, alpha, 0.0)
+    assert np.array_equal(m0, np.abs(y) <= s[:, None])  # trust 0: every clipped entry untrusted
+
+
+def test_trust_factor_loop_matches_vectorised():
+    rng = np.random.default_rng(92)
+    y = rng.standard_t(4, size=(6, 64))
+    for b, t in ((1, 1.3), (3, 0.7), (5, 2.0)):
+        a = qo.fit_alpha(b)
+        loop = qo.quantize_rows_loop(y.tolist(), b, a, t)
+        vec = qo.quantize_rows(y, b, a, t)
+        assert np.array_equal(loop[0], vec[0]) and np.array_equal(loop[2], vec[2])  # codes, mask
+        assert np.allclose(loop[1], vec[1], rtol=1e-14, atol=0)  # scale (sum order differs)
+        assert np.allclose(loop[3], vec[3], rtol=1e-14, atol=0)
+
+
+def test_one_bit_outer_trust_untrusted_fraction():
+    # b = 1, s* = 1.30: trusted iff |y| <= 2.3 alpha_1 RMS; for Gaussian rows the untrusted
+    # fraction is 2 (1 - Phi(2.3 sqrt(2/pi))) (RMS estimated per 4096-entry row).
+    from scipy.stats import norm
+
+    rng = np.random.default_rng(93)
+    y = rng.standard_normal((256, 4096))
+    _, _, m, _ = qo.quantize_rows(y, 1, qo.fit_alpha(1), 1.3)
+    expect = 2.0 * norm.sf(2.3 * np.sqrt(2.0 / np.pi))
+    assert abs((~m).mean() - expect) < 4e-4
