@@ -518,3 +518,52 @@ def test_outer_trust_factor(dev, rows, cols, block, dt, b, trust):
     if trust != 1.0:
         assert (ref["m"] != m_ref1).any(), "the factor should change some mask bits on heavy-tailed rows"
     log(f"  {stats}")
+
+
+# ---------------------------------------------------------------------------
+# Beyond 32-bit element offsets: 2^21 + 1025 rows of 2048 bf16 (4.3e9
+# elements, 8.6 GB per tensor).  Rows on both sides of element 2^32 and the
+# last rows are recomputed by the oracle.
+# ---------------------------------------------------------------------------
+def test_beyond_32bit_offsets(dev):
+    # Rows are read and written as slices (views and copies): torch's own
+    # advanced-indexing kernels are kept off tensors of more than 2^32 elements.
+    rows, cols, block, b = (1 << 21) + 1025, 2048, 128, 4
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < 48 << 30:
+        pytest.skip("needs about 40 GB of free device memory")
+    spec = TensorSpec("huge.x", rows, cols, "bf16", "student_t", 4, 8800, outlier_cols=20, outlier_scale=20.0)
+    gspec = TensorSpec("huge.g", rows, cols, "bf16", "normal", 1e-3, 8801)
+    log(f"fwd/dequant/bwd {rows}x{cols} ({rows * cols} elements)")
+    boundary_row = (1 << 32) // cols  # first row at or past element 2^32
+    spans = [(0, 2), (boundary_row - 1, 3), (rows - 2, 2)]  # rows 0-1, both sides of 2^32, the last two
+
+    def gather(t):
+        return torch.cat([t[lo:lo + n] for lo, n in spans]).cpu()
+
+    x = make_tensor(spec, dev)
+    codes, scale, mask = fwd_gpu(x, block, b)
+    x64 = to_float64(gather(x))
+    ref = qo.quantize_fwd(x64, block, b)
+    check_fwd(x64, block, b, gather(codes).numpy(), gather(scale.view(-1, 1)).numpy().ravel(), gather(mask).numpy(),
+              ref=ref)
+    deq = qa.dequantize(codes, scale, rows, cols, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_values(gather(deq).float().numpy().astype(np.float64),
+                 qo.dequantize(ref["codes"], ref["scale"], cols, b), TOL_BF16,
+                 skip=exempt_entries(ref["y"], ref["scale"], b))
+    del deq, x
+    torch.cuda.empty_cache()
+    g = make_tensor(gspec, dev)
+    k = 0
+    for lo, n in spans:  # the oracle's own mask on the checked rows
+        mask[lo:lo + n].copy_(torch.from_numpy(ref["mask"][k:k + n]))
+        k += n
+    out = qa.trust_bwd(g, mask, block, out=g)  # in place: one 8.6 GB buffer
+    torch.cuda.synchronize()
+    k = 0
+    for lo, n in spans:  # the gradient rows again, regenerated on the same device
+        g_rows = make_tensor(gspec, dev, row_start=lo, row_count=n)
+        expect = qo.trust_bwd(to_float64(g_rows), ref["mask"][k:k + n], block)
+        check_grad(out[lo:lo + n].float().cpu().numpy(), expect, block, TOL_BF16)
+        k += n
