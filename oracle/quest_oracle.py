@@ -16,6 +16,9 @@ each function names the page and section it follows):
   half a grid step.
 * Backward: the Hadamard-domain gradient is multiplied by the stored mask and
   transformed back by the inverse Hadamard matrix.
+* Product of two quantised operands (b <= 4): each grid value over its row's
+  step is a half-integer, held as an FP6 E2M3 element; the product is the
+  float64 matrix product of the decoded, rescaled operands.
 
 Everything is float64 NumPy.  The Hadamard product is the dense O(n^2)
 definition (a matrix product against the explicit n x n matrix), the clip
@@ -66,6 +69,11 @@ __all__ = [
     "trust_bwd",
     "qat_linear_fwd",
     "qat_linear_bwd",
+    "e2m3_value",
+    "e2m3_encode",
+    "operand_e2m3",
+    "operand_step",
+    "quest_gemm",
 ]
 
 
@@ -463,3 +471,82 @@ def qat_linear_bwd(dy: np.ndarray, fwd: dict, block: int) -> tuple:
     dx = trust_bwd(dy @ fwd["qw"], fwd["mask_x"], block)
     dw = trust_bwd(dy.T @ fwd["qx"], fwd["mask_w"], block)
     return dx, dw
+
+
+# ---------------------------------------------------------------------------
+# Low-precision product of two quantised operands.
+# The pages time QuEST's 4-bit matrix products against BF16 ones, with the
+# quantisation, dequantisation and Hadamard costs included (pith.science
+# review of QuEST, Figure 5 caption; atlas.scime.ai summary, "Key results").
+# On the midrise grid every level is a half-integer multiple of the step,
+# q = (u - (L - 1)/2) * Delta, so for b <= 4 the half-integer fits the FP6
+# E2M3 element format exactly and the product of two operands is
+# Delta_a Delta_b times a sum of products of half-integers.
+# E2M3 is the FP6 element type of the OCP Microscaling (MX) Formats
+# specification v1.0: one sign bit, two exponent bits with bias 1, three
+# mantissa bits, subnormals at exponent 0, no infinities and no NaN.
+# ---------------------------------------------------------------------------
+
+def e2m3_value(code) -> np.ndarray:
+    """Decode 6-bit E2M3 codes (sign bit 5, exponent bits 4..3, mantissa bits 2..0)."""
+    code = np.asarray(code, dtype=np.int64)
+    if code.size and (code.min() < 0 or code.max() > 63):
+        raise ValueError("E2M3 codes are 6-bit")
+    sign = np.where((code >> 5) & 1, -1.0, 1.0)
+    exp = (code >> 3) & 3
+    man = (code & 7).astype(np.float64)
+    mag = np.where(exp == 0, man / 8.0, (1.0 + man / 8.0) * np.exp2(exp - 1.0))
+    return sign * mag
+
+
+def e2m3_encode(v) -> np.ndarray:
+    """Encode values that E2M3 holds exactly; anything else is an error.
+
+    |v| < 1 is a subnormal (exponent field 0, mantissa |v| * 8); otherwise the
+    exponent field is floor(log2 |v|) + 1 and the mantissa (|v| / 2^(e-1) - 1) * 8.
+    Zero encodes as +0.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.abs(v)
+    out = np.zeros(v.shape, dtype=np.int64)
+    sub = mag < 1.0
+    man_sub = mag * 8.0
+    e = np.where(sub, 0, np.floor(np.log2(np.where(sub, 1.0, mag))).astype(np.int64) + 1)
+    man_norm = (mag / np.exp2(np.maximum(e, 1) - 1.0) - 1.0) * 8.0
+    man = np.where(sub, man_sub, man_norm)
+    if np.any(e > 3) or np.any(man != np.round(man)) or np.any(man < 0) or np.any(man > 7):
+        raise ValueError("value not exactly representable in E2M3")
+    out = (np.where(v < 0, 1, 0) << 5) | (e << 3) | man.astype(np.int64)
+    return out
+
+
+def operand_e2m3(codes: np.ndarray, cols: int, b: int) -> np.ndarray:
+    """Matrix-core operand of packed b-bit codes: u - (L - 1)/2 as E2M3, 6 bits per element.
+
+    Returns R x (C * 6 / 8) uint8, an LSB-first 6-bit stream per row (the
+    same stream layout as the codes).  Defined for b <= 4, where the largest
+    half-integer (L - 1)/2 = 7.5 is E2M3's largest value.
+    """
+    if not 1 <= b <= 4:
+        raise ValueError("the E2M3 operand holds b <= 4 bit grids")
+    big_l = 1 << b
+    u = unpack_lsb_first(codes, b, cols)
+    return pack_lsb_first(e2m3_encode(u - (big_l - 1) / 2.0), 6)
+
+
+def operand_step(scale: np.ndarray, b: int) -> np.ndarray:
+    """Grid step Delta = 2 s / (L - 1) of each row, from its clip scale s."""
+    return 2.0 * np.asarray(scale, dtype=np.float64) / ((1 << b) - 1)
+
+
+def quest_gemm(a_op: np.ndarray, a_scale: np.ndarray, bits_a: int, b_op: np.ndarray, b_scale: np.ndarray,
+               bits_b: int, k: int) -> np.ndarray:
+    """y = Q(a) Q(b)^T from two E2M3 operands (M x K and N x K) and their clip scales.
+
+    Q(.)[r, c] = e2m3_value(field c of row r) * Delta_r; the product is a
+    float64 matrix product of the decoded operands.  With Hadamard-domain
+    operands this is the layer output of ``qat_linear_fwd``.
+    """
+    va = e2m3_value(unpack_lsb_first(a_op, 6, k)) * operand_step(a_scale, bits_a)[:, None]
+    vb = e2m3_value(unpack_lsb_first(b_op, 6, k)) * operand_step(b_scale, bits_b)[:, None]
+    return va @ vb.T

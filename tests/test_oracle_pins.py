@@ -571,3 +571,77 @@ def test_one_bit_outer_trust_untrusted_fraction():
     _, _, m, _ = qo.quantize_rows(y, 1, qo.fit_alpha(1), 1.3)
     expect = 2.0 * norm.sf(2.3 * np.sqrt(2.0 / np.pi))
     assert abs((~m).mean() - expect) < 4e-4
+
+
+# ---------------------------------------------------------------------------
+# FP6 E2M3 operand and the product of two quantised operands.
+# E2M3 facts from the OCP Microscaling Formats specification v1.0 (FP6 E2M3
+# element type): exponent bias 1, largest normal 7.5, smallest normal 1.0,
+# largest subnormal 0.875, smallest subnormal 0.125, no Inf or NaN.
+# ---------------------------------------------------------------------------
+
+def test_e2m3_format_facts():
+    v = qo.e2m3_value(np.arange(64))
+    assert v[0] == 0.0 and v[32] == 0.0
+    assert np.array_equal(v[32:], -v[:32])
+    pos = v[:32]
+    assert np.all(np.diff(pos) > 0)
+    assert pos[1] == 0.125 and pos[7] == 0.875 and pos[8] == 1.0 and pos[31] == 7.5
+    # three mantissa bits: 8 values per binade; subnormals share the first binade's spacing
+    assert np.all(np.diff(pos[:17]) == 0.125)
+    assert np.all(np.diff(pos[16:25]) == 0.25)
+    assert np.all(np.diff(pos[24:32]) == 0.5)
+
+
+def test_e2m3_encode_round_trip_and_rejects():
+    v = qo.e2m3_value(np.arange(64))
+    codes = qo.e2m3_encode(v)
+    assert np.array_equal(qo.e2m3_value(codes), v)
+    halves = np.arange(-7.5, 8.0, 1.0)
+    assert np.array_equal(qo.e2m3_value(qo.e2m3_encode(halves)), halves)
+    for bad in (0.3, 8.0, 7.25, -2.125):
+        with pytest.raises(ValueError):
+            qo.e2m3_encode(np.array([bad]))
+
+
+def test_operand_hand_packed_example():
+    # b = 4 codes 8, 7, 15, 0 are the half-integers +0.5, -0.5, +7.5, -7.5,
+    # E2M3 codes 4 (0 00 100), 36 (1 00 100), 31 (0 11 111), 63 (1 11 111);
+    # as a 24-bit LSB-first stream 4 + 36*2^6 + 31*2^12 + 63*2^18 = 0xFDF904.
+    codes = qo.pack_lsb_first(np.array([[8, 7, 15, 0]]), 4)
+    op = qo.operand_e2m3(codes, 4, 4)
+    assert op.tolist() == [[0x04, 0xF9, 0xFD]]
+    with pytest.raises(ValueError):
+        qo.operand_e2m3(qo.pack_lsb_first(np.zeros((1, 8), dtype=np.int64), 5), 8, 5)
+
+
+@pytest.mark.parametrize("ba,bb", [(1, 1), (2, 4), (3, 3), (4, 4), (4, 1)])
+def test_quest_gemm_equals_exact_integer_product(ba, bb):
+    # An independent route: the odd integers 2u - L + 1 multiplied in exact
+    # int64 arithmetic, scaled by s_a s_b / ((L_a - 1)(L_b - 1)).
+    rng = np.random.default_rng(100 + 10 * ba + bb)
+    m, n, k = 7, 5, 192
+    ua = rng.integers(0, 1 << ba, size=(m, k))
+    ub = rng.integers(0, 1 << bb, size=(n, k))
+    sa = rng.uniform(0.1, 3.0, size=m)
+    sb = rng.uniform(0.1, 3.0, size=n)
+    ops_a = qo.operand_e2m3(qo.pack_lsb_first(ua, ba), k, ba)
+    ops_b = qo.operand_e2m3(qo.pack_lsb_first(ub, bb), k, bb)
+    y = qo.quest_gemm(ops_a, sa, ba, ops_b, sb, bb, k)
+    ia = 2 * ua - (1 << ba) + 1
+    ib = 2 * ub - (1 << bb) + 1
+    exact = (ia @ ib.T).astype(np.float64)
+    ref = exact * (sa / ((1 << ba) - 1))[:, None] * (sb / ((1 << bb) - 1))[None, :]
+    assert np.allclose(y, ref, rtol=1e-13, atol=0.0)
+
+
+@pytest.mark.parametrize("bx,bw", [(4, 4), (2, 3)])
+def test_quest_gemm_is_the_layer_product(bx, bw):
+    rng = np.random.default_rng(7 + bx)
+    x = rng.standard_t(4, size=(9, 256))
+    w = rng.normal(0.0, 0.02, size=(6, 256))
+    f = qo.qat_linear_fwd(x, w, 128, bx, bw)
+    fx, fw = f["fx"], f["fw"]
+    y = qo.quest_gemm(qo.operand_e2m3(fx["codes"], 256, bx), fx["scale"], bx,
+                      qo.operand_e2m3(fw["codes"], 256, bw), fw["scale"], bw, 256)
+    assert np.allclose(y, f["y"], rtol=1e-12, atol=1e-15)
