@@ -196,6 +196,84 @@ quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t 
 quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_t* mask, int64_t rows, int64_t cols,
                              int block, void* grad_out, void* stream);
 
+/*
+ * The matrix-core operand of a quantised tensor, for products of two of them
+ * (quest_gemm).  The pages time QuEST's 4-bit matrix products against BF16
+ * ones, quantisation, dequantisation and Hadamard costs included
+ * (pith.science review of QuEST, Figure 5 caption; atlas.scime.ai summary,
+ * "Key results").  Every level of the midrise grid is a half-integer
+ * multiple of the row's step Delta_r = 2 s_r / (L - 1):
+ *   q = (u - (L - 1)/2) * Delta_r,
+ * and for b <= 4 the half-integer h = u - (L - 1)/2 (|h| <= 7.5) is held
+ * exactly by the FP6 E2M3 element type of the OCP Microscaling Formats
+ * specification v1.0 (sign bit 5, exponent bits 4..3 with bias 1, mantissa
+ * bits 2..0; subnormals at exponent 0), the operand type of gfx950's
+ * 6-bit matrix instructions.
+ *
+ * Operand layout (tiled for the matrix cores; cols a multiple of 128):
+ *   rows form blocks of 32 (the last block padded), each row block is
+ *   cols / 128 consecutive 3072-byte blocks of 128 columns, and a block is
+ *   two 1536-byte halves of 64 columns, each 64 slots of 24 bytes.  Slot l
+ *   of half e of block c of row block R holds row 32 R + l % 32, columns
+ *   128 c + 64 e + 32 (l / 32) + (0 .. 31) as 6-bit fields, LSB-first
+ *   (field i in bits [6 i, 6 i + 6) of the slot, bit j of byte t is bit
+ *   8 t + j).  Run j (columns 32 j .. 32 j + 31) of row r therefore starts at
+ *     (r / 32) * (cols / 128) * 3072 + (j / 4) * 3072 + (j / 2 % 2) * 1536
+ *       + (32 (j % 2) + r % 32) * 24.
+ *   The padding rows of the last row block are not written; a product only
+ *   uses them for outputs it does not store.
+ */
+
+/* Bytes of the operand: ceil(rows / 32) * 32 * cols * 3 / 4 (0 unless cols is a
+   positive multiple of 128 and rows >= 0). */
+size_t quest_operand_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Forward writing the matrix-core operand: the quantiser of
+ * quest_quantize_fwd_ex, whose levels go to `operand` instead of a
+ * dequantised tensor.  Codes and mask are optional (an inference forward
+ * needs neither).
+ *   b        1 .. 4 (QUEST_EUNSUPPORTED otherwise)
+ *   cols     a multiple of 128 as well as of `block` (QUEST_EUNSUPPORTED)
+ *   codes    device output or NULL (not written)
+ *   scale    device output, rows floats (required)
+ *   mask     device output or NULL (not written)
+ *   operand  device output, quest_operand_bytes(rows, cols) bytes, 16-byte
+ *            aligned, overlapping no other argument (required when rows > 0)
+ * Everything else as for quest_quantize_fwd_ex.  The operand's levels are
+ * those of the codes: h = u - (L - 1)/2 for the code u the call stores.
+ */
+quest_status quest_quantize_fwd_op(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                   int b, double trust, uint8_t* codes, float* scale, uint8_t* mask,
+                                   uint8_t* operand, void* stream);
+
+/*
+ * Product of two quantised operands along their quantised axis:
+ *   out[i, j] = Delta_a[i] Delta_b[j] * sum_c h_a[i, c] h_b[j, c],
+ *   Delta = 2 s / (L - 1) from each operand's clip scale and bit width,
+ * which is Q(A) Q(B)^T for the grid values Q of both (in the Hadamard
+ * domain, where the product of two transformed operands equals the product
+ * of their original-domain reconstructions: pith.science review of QuEST,
+ * "Assumptions & free parameters").  Both operands come from
+ * quest_quantize_fwd_op with the same cols = k.  The sum of half-integer
+ * products is accumulated exactly in fp32; the result is rounded three
+ * times (Delta_a Delta_b, the product, and the output type).
+ *   a, a_scale  device, quest_operand_bytes(m, k) bytes and m floats (s_r)
+ *   b, b_scale  device, quest_operand_bytes(n, k) bytes and n floats
+ *   m, n        >= 0 (0: nothing is done); m <= 2^30, n <= 2^20
+ *   a_bits, b_bits  1 .. 4: the bit widths the operands were quantised to
+ *   k           the common number of columns: a positive multiple of 128,
+ *               at most 65536 (QUEST_EUNSUPPORTED; above that the fp32 sum
+ *               would no longer be exact)
+ *   out         device output, m x n row-major elements of out_dtype
+ *               (QUEST_F32 or QUEST_BF16, round to nearest even), 16-byte
+ *               aligned, overlapping no input (QUEST_EINVAL)
+ * All pointers 16-byte aligned (QUEST_EALIGN).
+ */
+quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a_bits, const uint8_t* b,
+                        const float* b_scale, int64_t n, int b_bits, int64_t k, void* out, quest_dtype out_dtype,
+                        void* stream);
+
 /* Bytes of the packed codes: rows * cols * b / 8 (0 on invalid sizes). */
 size_t quest_codes_bytes(int64_t rows, int64_t cols, int b);
 

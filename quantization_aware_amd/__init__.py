@@ -23,6 +23,9 @@ __all__ = [
     "quantize_fwd",
     "quantize_fwd_dq",
     "quantize_fwd_ex",
+    "quantize_fwd_op",
+    "operand_bytes",
+    "gemm",
     "dequantize",
     "trust_bwd",
     "EXPORTED_SYMBOLS",
@@ -38,6 +41,9 @@ EXPORTED_SYMBOLS = (
     "quest_quantize_fwd",
     "quest_quantize_fwd_dq",
     "quest_quantize_fwd_ex",
+    "quest_quantize_fwd_op",
+    "quest_gemm",
+    "quest_operand_bytes",
     "quest_dequantize",
     "quest_trust_bwd",
     "quest_codes_bytes",
@@ -77,6 +83,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_quantize_fwd_dq.restype = c_int
     lib.quest_quantize_fwd_ex.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp, c_int, vp]
     lib.quest_quantize_fwd_ex.restype = c_int
+    lib.quest_quantize_fwd_op.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp, vp]
+    lib.quest_quantize_fwd_op.restype = c_int
+    lib.quest_gemm.argtypes = [vp, vp, i64, c_int, vp, vp, i64, c_int, i64, vp, c_int, vp]
+    lib.quest_gemm.restype = c_int
+    lib.quest_operand_bytes.argtypes = [i64, i64]
+    lib.quest_operand_bytes.restype = ctypes.c_size_t
     lib.quest_dequantize.argtypes = [vp, vp, i64, i64, c_int, vp, c_int, vp]
     lib.quest_dequantize.restype = c_int
     lib.quest_trust_bwd.argtypes = [vp, c_int, vp, i64, i64, c_int, vp, vp]
@@ -234,6 +246,55 @@ def quantize_fwd_ex(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
     )
     _check("quest_quantize_fwd_ex", st)
     return codes, scale, mask, dq
+
+
+def operand_bytes(rows: int, cols: int) -> int:
+    """Bytes of the tiled FP6 operand of a rows x cols tensor (quest_operand_bytes)."""
+    return int(load_library().quest_operand_bytes(rows, cols))
+
+
+def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, with_codes: bool = False,
+                    with_mask: bool = False, operand=None, scale=None, stream=None):
+    """Forward writing the matrix-core operand (quest_quantize_fwd_op).
+
+    Returns (codes or None, scale, mask or None, operand); the operand is a
+    flat uint8 tensor of operand_bytes(rows, cols) bytes.
+    """
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev) if with_codes else None
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev) if with_mask else None
+    if operand is None:
+        operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=dev)
+    st = lib.quest_quantize_fwd_op(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),
+        codes.data_ptr() if codes is not None else None, scale.data_ptr(),
+        mask.data_ptr() if mask is not None else None, operand.data_ptr(), _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd_op", st)
+    return codes, scale, mask, operand
+
+
+def gemm(a: torch.Tensor, a_scale: torch.Tensor, m: int, a_bits: int, b: torch.Tensor, b_scale: torch.Tensor,
+         n: int, b_bits: int, k: int, out_dtype=torch.bfloat16, out=None, stream=None) -> torch.Tensor:
+    """Product of two matrix-core operands (quest_gemm): an m x n tensor of out_dtype."""
+    lib = load_library()
+    for name, t in (("a", a), ("a_scale", a_scale), ("b", b), ("b_scale", b_scale)):
+        _device_tensor(name, t)
+    dev = a.device
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _device_tensor("out", out)
+    st = lib.quest_gemm(a.data_ptr(), a_scale.data_ptr(), m, int(a_bits), b.data_ptr(), b_scale.data_ptr(), n,
+                        int(b_bits), k, out.data_ptr(), _dtype_code(out), _stream_handle(dev, stream))
+    _check("quest_gemm", st)
+    return out
 
 
 def dequantize(codes: torch.Tensor, scale: torch.Tensor, rows: int, cols: int, b: int,

@@ -24,7 +24,12 @@ SOURCES = [
     "quest_fwd_nodq.hip",
     "quest_fwd_dq_bf16.hip",
     "quest_fwd_dq_f32.hip",
+    "quest_fwd_op.hip",
+    "quest_gemm.hip",
 ]
+# Sources whose matrix-core accumulators live in AGPRs: they are built without
+# the VGPR-only MFMA form.
+AGPR_SOURCES = {"quest_gemm.hip"}
 ARCH = "gfx950"
 NOISE = "is not a recognized feature for this target"  # the host pass does not know the GPU feature below
 
@@ -36,7 +41,8 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found; libquest needs ROCm's hipcc to build")
 
 
-def compile_flags() -> list[str]:
+def compile_flags(source: str = "") -> list[str]:
+    vgpr_form = [] if source in AGPR_SOURCES else ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     return [
         f"--offload-arch={ARCH}",
         "-O3",
@@ -47,16 +53,16 @@ def compile_flags() -> list[str]:
         "-target-feature",
         "-Xclang",
         "-packed-fp32-ops",
-        # Matrix-core results go straight to VGPRs (no accumulator-register copies).
-        "-mllvm",
-        "-amdgpu-mfma-vgpr-form",
+        # Matrix-core results go straight to VGPRs (no accumulator-register
+        # copies), except in the sources listed in AGPR_SOURCES.
+        *vgpr_form,
         "-I",
         os.path.join(ROOT, "include"),
     ]
 
 
 def compile_command(source: str, obj: str) -> list[str]:
-    return [hipcc_path(), *compile_flags(), "-c", os.path.join(CSRC, source), "-o", obj]
+    return [hipcc_path(), *compile_flags(source), "-c", os.path.join(CSRC, source), "-o", obj]
 
 
 def link_command(objs: list[str], out_path: str) -> list[str]:

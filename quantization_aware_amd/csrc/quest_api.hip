@@ -128,7 +128,15 @@ quest_status from_hip(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_
 // before launching.
 quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                  double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
-                                 void* dq, quest_dtype dq_dtype, bool dq_required, void* stream);
+                                 bool mask_required, void* dq, quest_dtype dq_dtype, bool dq_required,
+                                 uint8_t* operand, void* stream);
+
+// Largest contraction length of quest_gemm: sums of k products of
+// half-integers up to 7.5 stay below 2^22 in magnitude, so fp32 accumulates
+// them exactly.
+constexpr int64_t kGemmMaxK = 65536;
+constexpr int64_t kGemmMaxN = int64_t(1) << 20;
+constexpr int64_t kGemmMaxM = int64_t(1) << 30;
 
 }  // namespace
 
@@ -165,22 +173,66 @@ const char* quest_status_string(quest_status s) {
 
 quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                 uint8_t* codes, float* scale, uint8_t* mask, void* stream) {
-  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, true, scale, mask, nullptr, QUEST_BF16,
-                             false, stream);
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, true, scale, mask, true, nullptr,
+                             QUEST_BF16, false, nullptr, stream);
 }
 
 quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                    uint8_t* codes, float* scale, uint8_t* mask, void* dq, quest_dtype dq_dtype,
                                    void* stream) {
-  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, false, scale, mask, dq, dq_dtype, true,
-                             stream);
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, false, scale, mask, true, dq, dq_dtype,
+                             true, nullptr, stream);
 }
 
 quest_status quest_quantize_fwd_ex(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                    double trust, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
                                    quest_dtype dq_dtype, void* stream) {
-  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, trust, codes, false, scale, mask, dq, dq_dtype, false,
-                             stream);
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, trust, codes, false, scale, mask, true, dq, dq_dtype,
+                             false, nullptr, stream);
+}
+
+size_t quest_operand_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || cols % 128 != 0) return 0;
+  return static_cast<size_t>((rows + 31) / 32) * 32 * static_cast<size_t>(cols / 4 * 3);
+}
+
+quest_status quest_quantize_fwd_op(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                   double trust, uint8_t* codes, float* scale, uint8_t* mask, uint8_t* operand,
+                                   void* stream) {
+  if (rows > 0 && !operand) return QUEST_EINVAL;
+  return quantize_fwd_common(x, x_dtype, rows, cols, block, b, trust, codes, false, scale, mask, false, nullptr,
+                             QUEST_BF16, false, rows > 0 ? operand : nullptr, stream);
+}
+
+quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a_bits, const uint8_t* b,
+                        const float* b_scale, int64_t n, int b_bits, int64_t k, void* out, quest_dtype out_dtype,
+                        void* stream) {
+  if (a_bits < 1 || a_bits > 4 || b_bits < 1 || b_bits > 4) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(out_dtype) || m < 0 || n < 0 || k <= 0) return QUEST_EINVAL;
+  if (k % 128 != 0 || k > kGemmMaxK || n > kGemmMaxN || m > kGemmMaxM) return QUEST_EUNSUPPORTED;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (tiles > INT32_MAX) return QUEST_EUNSUPPORTED;
+  if (m == 0 || n == 0) return QUEST_OK;
+  if (!a || !a_scale || !b || !b_scale || !out) return QUEST_EINVAL;
+  if (!aligned16(a) || !aligned16(a_scale) || !aligned16(b) || !aligned16(b_scale) || !aligned16(out))
+    return QUEST_EALIGN;
+  const size_t no = static_cast<size_t>(m) * static_cast<size_t>(n) * dtype_size(out_dtype);
+  if (overlaps(out, no, a, quest_operand_bytes(m, k)) || overlaps(out, no, b, quest_operand_bytes(n, k)) ||
+      overlaps(out, no, a_scale, static_cast<size_t>(m) * 4) || overlaps(out, no, b_scale, static_cast<size_t>(n) * 4))
+    return QUEST_EINVAL;
+  quest::GemmLaunch g;
+  g.a = a;
+  g.sa = a_scale;
+  g.m = static_cast<int>(m);
+  g.b = b;
+  g.sb = b_scale;
+  g.n = static_cast<int>(n);
+  g.k = static_cast<int>(k);
+  g.ka = static_cast<float>(2.0 / double((1 << a_bits) - 1));
+  g.kb = static_cast<float>(2.0 / double((1 << b_bits) - 1));
+  g.out = out;
+  g.stream = static_cast<hipStream_t>(stream);
+  return from_hip(quest::launch_gemm_e2m3(g, out_dtype == QUEST_BF16));
 }
 
 quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,
@@ -224,28 +276,32 @@ namespace {
 
 quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
                                  double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
-                                 void* dq, quest_dtype dq_dtype, bool dq_required, void* stream) {
+                                 bool mask_required, void* dq, quest_dtype dq_dtype, bool dq_required,
+                                 uint8_t* operand, void* stream) {
   const int lb = log2_block(block);
   if (lb < 0 || b < 1 || b > kMaxBits) return QUEST_EUNSUPPORTED;
+  if (operand && (b > 4 || cols % 128 != 0)) return QUEST_EUNSUPPORTED;
   if (!dtype_ok(x_dtype)) return QUEST_EINVAL;
   if ((dq || dq_required) && !dtype_ok(dq_dtype)) return QUEST_EINVAL;
   if (!(trust >= 0.0) || !std::isfinite(trust)) return QUEST_EINVAL;
   const quest_status sh = check_shape(rows, cols, block);
   if (sh != QUEST_OK) return sh;
   if (rows == 0) return QUEST_OK;
-  if (!x || !scale || !mask || (codes_required && !codes) || (dq_required && !dq)) return QUEST_EINVAL;
-  if (!aligned16(x) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(mask) ||
-      (dq && !aligned16(dq)))
+  if (!x || !scale || (mask_required && !mask) || (codes_required && !codes) || (dq_required && !dq)) return QUEST_EINVAL;
+  if (!aligned16(x) || (codes && !aligned16(codes)) || !aligned16(scale) || (mask && !aligned16(mask)) ||
+      (dq && !aligned16(dq)) || (operand && !aligned16(operand)))
     return QUEST_EALIGN;
   const size_t nx = static_cast<size_t>(rows * cols) * dtype_size(x_dtype);
   const size_t nc = codes ? quest_codes_bytes(rows, cols, b) : 0;
   const size_t ns = static_cast<size_t>(rows) * sizeof(float);
-  const size_t nm = quest_mask_bytes(rows, cols);
+  const size_t nm = mask ? quest_mask_bytes(rows, cols) : 0;
   const size_t nd = dq ? static_cast<size_t>(rows * cols) * dtype_size(dq_dtype) : 0;
+  const size_t no = operand ? quest_operand_bytes(rows, cols) : 0;
   if (overlaps(x, nx, codes, nc) || overlaps(x, nx, scale, ns) || overlaps(x, nx, mask, nm) ||
       overlaps(codes, nc, scale, ns) || overlaps(codes, nc, mask, nm) || overlaps(scale, ns, mask, nm) ||
       overlaps(dq, nd, x, nx) || overlaps(dq, nd, codes, nc) || overlaps(dq, nd, scale, ns) ||
-      overlaps(dq, nd, mask, nm))
+      overlaps(dq, nd, mask, nm) || overlaps(operand, no, x, nx) || overlaps(operand, no, codes, nc) ||
+      overlaps(operand, no, scale, ns) || overlaps(operand, no, mask, nm))
     return QUEST_EINVAL;
   std::call_once(g_env_once, read_env);
   quest::FwdLaunch a;
@@ -257,9 +313,9 @@ quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t row
   a.codes = codes;
   a.scale = scale;
   a.mask = mask;
-  a.dq = dq;
+  a.dq = operand ? static_cast<void*>(operand) : dq;
   a.stream = static_cast<hipStream_t>(stream);
-  const int dq_kind = dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
+  const int dq_kind = operand ? 3 : dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
   return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, lb, b, dq_kind, a));
 }
 

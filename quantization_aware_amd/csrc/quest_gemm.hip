@@ -1,0 +1,315 @@
+// Product of two QuEST-quantised operands on the gfx950 matrix cores.
+//
+// QuEST's 4-bit layers multiply two quantised operands, whose levels are
+// half-integer multiples of each row's step (pith.science review of QuEST,
+// Figure 5 caption: per-layer speedups of the 4-bit product over BF16,
+// quantisation, dequantisation and Hadamard costs included; atlas.scime.ai
+// summary, "Key results").  For b <= 4 each level over its row's step,
+// u - (L - 1)/2, is a half-integer of magnitude at most 7.5, which the FP6
+// E2M3 element type holds exactly (OCP Microscaling Formats v1.0).  So
+//   y[i][j] = Delta_a[i] Delta_b[j] * sum_k va[i][k] vb[j][k]
+// is one FP6 x FP6 matrix product (v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit block scales) followed by a per-row and per-column scaling.  Products
+// of half-integers are quarter-integers and their sums stay below 2^22 in
+// magnitude for k <= 65536, so the fp32 accumulation is exact; the only
+// roundings are those of Delta, Delta_a Delta_b and the final product.
+//
+// Operand layout (written by the forward pass, see include/quest.h): rows in
+// blocks of 32, k in chunks of 128; block (rb, c) is 3072 contiguous bytes at
+// (rb * k / 128 + c) * 3072, holding two 1536-byte fragments (k-halves of 64),
+// each 64 lane slots of 24 bytes: slot l carries row 32 rb + l % 32, the 32
+// values starting at k = 128 c + 64 ks + 32 (l / 32), as 6-bit fields
+// LSB-first -- exactly the register operand of one lane of the 32x32x64
+// instruction.
+//
+// Kernel: a workgroup (4 waves, one per SIMD) computes a 256 x 256 output
+// tile, each wave a 128 x 128 quadrant (16 accumulator tiles of 32 x 32 in
+// AGPRs).  Operand blocks stream from HBM/L2 straight into LDS (buffer loads
+// with the LDS-destination bit, 1 KB per wave instruction), three stages deep.
+// Per stage (k = 128) a wave runs 32 MFMAs in two halves; the fragment reads
+// of the next half and the loads of the stage after next are interleaved
+// with them, and one barrier per stage publishes the next stage.  The
+// epilogue scales by Delta_a Delta_b and writes whole row segments through
+// LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "quest_launch.h"
+
+namespace quest {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileM = 256, kTileN = 256;  // workgroup output tile
+constexpr int kFrag = 64 * 24;             // one 32-row x 64-k fragment
+constexpr int kBlock = 2 * kFrag;          // one 32-row x 128-k block
+constexpr int kOpStage = 8 * kBlock;       // one operand's 256 rows of a stage
+constexpr int kStage = 2 * kOpStage;       // both operands
+constexpr int kNowhereOff = 0x7FFFFFF0;    // past every window: stores there are dropped
+
+// Raw buffer resource: base, byte count, 32-bit raw format; out-of-range
+// loads return zero and out-of-range stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// The same resource as four dwords, for the asm loads below.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{static_cast<int32_t>(static_cast<uint32_t>(a)), static_cast<int32_t>((a >> 32) & 0xFFFFu),
+               static_cast<int32_t>(bytes), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even (finite values)
+}
+
+// 16 bytes from global memory into LDS at lds_base + 16 * lane.  Written as
+// asm so that the compiler's wait counting leaves these loads alone: each
+// stage is read only after an explicit vmcnt wait and a barrier.  The load
+// has no register results.
+__device__ __forceinline__ void dma16(uint32_t lds_base, int32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter limited (lgkm and exp left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x3F70 | N);
+}
+
+template <typename Out, bool kVec>
+__global__ void __launch_bounds__(256)
+    quest_gemm_e2m3_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
+                           const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k, float ka,
+                           float kb, Out* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  auto stage_mem = [&](auto bi) -> uint8_t* { return lds + decltype(bi)::value * kStage; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
+  // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
+  // contiguous range of tiles, walked in groups of 8 tile rows, so that the
+  // tiles sharing operand blocks share an L2.
+  const int grid = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  const int full = grid & ~7;
+  if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
+  const int group = 8 * tiles_n;
+  const int first_m = (pid / group) * 8;
+  const int gm = min(tiles_m - first_m, 8);
+  const int tm = first_m + (pid % group) % gm, tn = (pid % group) / gm;
+
+  const int chunks = k >> 7;
+  const uint32_t rb_bytes = static_cast<uint32_t>(chunks) * kBlock;  // one 32-row block, all of k
+  const int rb_a = (m + 31) >> 5, rb_b = (n + 31) >> 5;
+  const i32x4 ra = raw_rsrc(a + static_cast<size_t>(tm) * 8 * rb_bytes, min(rb_a - tm * 8, 8) * rb_bytes);
+  const i32x4 rb = raw_rsrc(b + static_cast<size_t>(tn) * 8 * rb_bytes, min(rb_b - tn * 8, 8) * rb_bytes);
+
+  // Stage st into LDS: each operand's 8 blocks are 24 KB = 24 wave
+  // instructions; wave w issues t = w + 4 u, u < 6, for both operands.
+  auto fetch = [&](int st, auto bi) {
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage_mem(bi)));
+    const i32x4 qa = ra, qb = rb;
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int t = wave + 4 * u, blk = t / 3, part = t % 3;
+      const int goff = blk * static_cast<int>(rb_bytes) + st * kBlock + part * 1024 + lane * 16;
+      const uint32_t la = base + blk * kBlock + part * 1024;
+      dma16(__builtin_amdgcn_readfirstlane(la), goff, qa);
+      dma16(__builtin_amdgcn_readfirstlane(la + kOpStage), goff, qb);
+    }
+  };
+  // Fragment (block rbk, k-half ks) of operand op: this lane's 24 bytes.
+  auto frag = [&](auto bi, int op, int rbk, int ks) -> v8i {
+    const u32x2* s = reinterpret_cast<const u32x2*>(stage_mem(bi) + op * kOpStage + rbk * kBlock + ks * kFrag + lane * 24);
+    const u32x2 x0 = s[0], x1 = s[1], x2 = s[2];
+    return v8i{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x1[0]),
+               static_cast<int>(x1[1]), static_cast<int>(x2[0]), static_cast<int>(x2[1]), 0, 0};
+  };
+
+  // acc[j][i]: 32 x 32 tile of the product B A^T for B block j and A block i,
+  // so lane l holds output row 32 i + l % 32 and four consecutive columns per
+  // register quad.
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  const int stages = chunks;
+  fetch(0, I0{});
+  fetch(stages > 1 ? 1 : 0, I1{});
+  wait_vmcnt<12>();  // stage 0 has landed (stage 1 may be in flight)
+  __syncthreads();
+  v8i f0a[4], f0b[4], f1a[4], f1b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
+    f0b[i] = frag(I0{}, 1, wn * 4 + i, 0);
+  }
+  // One stage: bi holds stage s, bn stage s + 1, b2 receives stage s + 2.
+  // b2 last held stage s - 1, whose reads every wave finished before the
+  // previous barrier.
+  auto step = [&](int s, auto bi, auto bn, auto b2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f1a[i] = frag(bi, 0, wm * 4 + i, 1);
+      f1b[i] = frag(bi, 1, wn * 4 + i, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0b[j], f0a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
+    fetch(s + 2 < stages ? s + 2 : stages - 1, b2);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two vector-memory loads
+    }
+    wait_vmcnt<12>();                   // stage s + 1 has landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // and this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f0a[i] = frag(bn, 0, wm * 4 + i, 0);
+      f0b[i] = frag(bn, 1, wn * 4 + i, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1b[j], f1a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
+  int s = 0;
+  for (; s + 3 <= stages; s += 3) {
+    step(s, I0{}, I1{}, I2{});
+    step(s + 1, I1{}, I2{}, I0{});
+    step(s + 2, I2{}, I0{}, I1{});
+  }
+  if (s < stages) step(s++, I0{}, I1{}, I2{});
+  if (s < stages) step(s++, I1{}, I2{}, I0{});
+  wait_vmcnt<0>();  // no load into LDS in flight before it is reused
+  __syncthreads();
+
+  // Epilogue.  Row and column factors Delta = s * 2 / (L - 1) go to LDS.
+  float* fac = reinterpret_cast<float*>(lds);  // [0, 256): rows, [256, 512): columns
+  {
+    const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
+    const auto rsb = make_rsrc(sb + static_cast<size_t>(tn) * kTileN, min(n - tn * kTileN, kTileN) * 4);
+    const float va = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0));
+    const float vb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, tid * 4, 0, 0));
+    fac[tid] = va * ka;
+    fac[kTileM + tid] = vb * kb;
+  }
+  __syncthreads();
+  // Each wave stages a 32 x 128 slab of its quadrant in its own LDS region
+  // and writes it as whole 128-column row segments.
+  constexpr int kOut = static_cast<int>(sizeof(Out));
+  constexpr int kPitch = 128 * kOut + 16;      // slab row pitch in bytes
+  constexpr int kPer = 16 / kOut;              // outputs per 16-byte chunk
+  constexpr int kLanesPerRow = 128 / kPer;
+  static_assert(4 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
+  uint8_t* slab = lds + kStage + wave * 32 * kPitch;  // the factors stay in the first
+  const int rows_left = m - tm * kTileM;
+  const auto rout = make_rsrc(out + static_cast<size_t>(tm) * kTileM * n,
+                              static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float fa = fac[wm * 128 + 32 * i + r32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 128
+        const float4 fb = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 128 + cl]);
+        const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
+        const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
+        uint8_t* d = slab + r32 * kPitch + cl * kOut;
+        if constexpr (kOut == 4) {
+          *reinterpret_cast<u32x4*>(d) =
+              u32x4{__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+        } else {
+          *reinterpret_cast<u32x2*>(d) =
+              u32x2{bf16_bits(y0) | (bf16_bits(y1) << 16), bf16_bits(y2) | (bf16_bits(y3) << 16)};
+        }
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < 32 * kLanesPerRow / 64; ++t) {
+      const int sr = t * (64 / kLanesPerRow) + lane / kLanesPerRow, sc = (lane % kLanesPerRow) * kPer;
+      const int row = wm * 128 + 32 * i + sr;  // within the tile
+      const int col = tn * kTileN + wn * 128 + sc;
+      const uint8_t* src = slab + sr * kPitch + sc * kOut;
+      if constexpr (kVec) {
+        // n is a multiple of kPer: a chunk is wholly inside or wholly past the row
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        const int off = col < n ? (row * n + col) * kOut : kNowhereOff;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int off = col + e < n ? (row * n + col + e) * kOut : kNowhereOff;
+          if constexpr (kOut == 4) {
+            __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src + 4 * e), rout, off, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const uint16_t*>(src + 2 * e), rout, off, 0, 0);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <typename Out, bool kVec>
+hipError_t launch(const GemmLaunch& g) {
+  const int tiles = ((g.m + kTileM - 1) / kTileM) * ((g.n + kTileN - 1) / kTileN);
+  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec>), dim3(tiles), dim3(256), 0,
+                     static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
+                     static_cast<Out*>(g.out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_e2m3(const GemmLaunch& g, bool out_bf16) {
+  if (out_bf16) return g.n % 8 == 0 ? launch<uint16_t, true>(g) : launch<uint16_t, false>(g);
+  return g.n % 4 == 0 ? launch<float, true>(g) : launch<float, false>(g);
+}
+
+}  // namespace quest

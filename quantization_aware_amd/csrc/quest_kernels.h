@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "quest_device.h"
 #include "quest_launch.h"
@@ -51,6 +52,7 @@ struct FwdConsts {
   float kk;
   float thr;
   float inv_cols;
+  int chunks;  // cols / 128: 3072-byte blocks per row block of the matrix-core operand
 };
 
 // Quantise 32 transformed values v (= tau * sqrt(n) * y) into b-bit codes,
@@ -200,27 +202,30 @@ struct DqOut<void> {
   static constexpr int U = 1;
 };
 
-// Grid values (2u - L + 1) s / (L - 1) of N entries whose codes are computed
-// from v with factor kk by quantise_run / quantise8 (the same arithmetic, so
-// each value is the grid value of the stored code).  c = s / (L - 1),
-// rounded as by quest_dequantize, and the product is rounded once, so the
-// values equal quest_dequantize's on the same codes and scale.
+// Code u of one entry as a float, computed from v with factor kk by the
+// arithmetic of quantise_run / quantise8, so it equals the stored code.
+template <int B>
+__device__ __forceinline__ float grid_code(float v, float kk) {
+  constexpr float L = static_cast<float>(1 << B);
+  if constexpr (B == 1) {
+    return v * kk >= 0.f ? 1.f : 0.f;
+  } else if constexpr (B == 2 || B == 4 || B == 8) {
+    const float t = __builtin_fminf(__builtin_fmaf(v, kk, 0.5f * (L - 1.f)), L - 1.f);
+    return __builtin_fmaxf(__builtin_rintf(t), 0.f);
+  } else {
+    return __builtin_truncf(__builtin_amdgcn_fmed3f(__builtin_fmaf(v, kk, 0.5f * L), 0.f, L - 1.f));
+  }
+}
+
+// Grid values (2u - L + 1) s / (L - 1) of N entries (codes from grid_code).
+// c = s / (L - 1), rounded as by quest_dequantize, and the product is
+// rounded once, so the values equal quest_dequantize's on the same codes and
+// scale.
 template <int B, int N>
 __device__ __forceinline__ void grid_values(const float* v, float kk, float c, float* q) {
   constexpr float L = static_cast<float>(1 << B);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    float u;
-    if constexpr (B == 1) {
-      u = v[i] * kk >= 0.f ? 1.f : 0.f;
-    } else if constexpr (B == 2 || B == 4 || B == 8) {
-      const float t = __builtin_fminf(__builtin_fmaf(v[i], kk, 0.5f * (L - 1.f)), L - 1.f);
-      u = __builtin_fmaxf(__builtin_rintf(t), 0.f);
-    } else {
-      u = __builtin_truncf(__builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], kk, 0.5f * L), 0.f, L - 1.f));
-    }
-    q[i] = __builtin_fmaf(u, 2.f, 1.f - L) * c;
-  }
+  for (int i = 0; i < N; ++i) q[i] = __builtin_fmaf(grid_code<B>(v[i], kk), 2.f, 1.f - L) * c;
 }
 
 // c = s / (L - 1) for the grid values (a correctly rounded fp32 division, as
@@ -228,6 +233,92 @@ __device__ __forceinline__ void grid_values(const float* v, float kk, float c, f
 template <int B>
 __device__ __forceinline__ float grid_step_half(float s) {
   return s / static_cast<float>((1 << B) - 1);
+}
+
+// Matrix-core operand output (quest_quantize_fwd_op): for every run (32
+// consecutive entries of a row) the half-integers u - (L - 1)/2, b <= 4, as
+// FP6 E2M3 fields in the run's 24-byte lane slot of the tiled layout that
+// quest_gemm reads.  Rows form blocks of 32, a row block holds `chunks`
+// 3072-byte blocks of 128 columns, and run j of row r sits at
+//   (r / 32) * chunks * 3072 + (j / 4) * 3072 + (j / 2 % 2) * 1536 + (32 (j % 2) + r % 32) * 24.
+struct OperandOut {};
+template <>
+struct DqOut<OperandOut> {
+  static constexpr bool kOn = true;
+  static constexpr int U = 1;
+};
+template <typename Dq>
+constexpr bool kIsOperand = std::is_same<Dq, OperandOut>::value;
+
+constexpr int kOpBlockBytes = 3072;  // 32 rows x 128 columns at 6 bits
+
+// Offset of run j of a row inside its row block.
+__device__ __forceinline__ int operand_slot(int row_in_block, int j) {
+  return (j >> 2) * kOpBlockBytes + ((j >> 1) & 1) * 1536 + (32 * (j & 1) + row_in_block) * 24;
+}
+
+// 32 values in field order (value i -> bits [6 i, 6 i + 6)) to six dwords.
+// The conversion takes the even-indexed values first and the odd-indexed
+// second and interleaves them; every input is a half-integer of magnitude at
+// most 7.5, so it is exact.
+__device__ __forceinline__ void e2m3_pack32(const float (&h)[RUN], uint32_t (&w)[6]) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  f32x16 ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = h[2 * i];
+    od[i] = h[2 * i + 1];
+  }
+  const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  w[0] = r[0];
+  w[1] = r[1];
+  w[2] = r[2];
+  w[3] = r[3];
+  w[4] = r[4];
+  w[5] = r[5];
+}
+
+// One run per lane: the lane's 32 values v (factor kk) into the operand
+// window `op_r` at byte offset `off` (kNowhere drops the run).
+template <int B>
+__device__ __forceinline__ void store_operand_run(const float (&v)[RUN], float kk, rsrc_t op_r, int off) {
+  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
+  float h[RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) h[i] = grid_code<B>(v[i], kk) - kHalf;
+  uint32_t w[6];
+  e2m3_pack32(h, w);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, op_r, off, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, op_r, off == kNowhere ? kNowhere : off + 8, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[4], w[5]}, op_r, off == kNowhere ? kNowhere : off + 16, 0, kNonTemporal);
+}
+
+// Matrix-core kernels: v[8 j .. 8 j + 7] of lane (g, n) are entries
+// 8 g .. 8 g + 7 of run 16 j + n (factor kk[j]).  Each slot's eight fields
+// (48 bits) are split into a low dword and a high half-word, a transpose
+// between lane quarters and slots hands lane l the four quarters of run l,
+// which it stores at byte offset `off` of `op_r`.
+template <int B>
+__device__ __forceinline__ void mfma_store_operand(const float (&v)[RUN], const float (&kk)[4], int lane, rsrc_t op_r,
+                                                   int off) {
+  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
+  float h[RUN];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[8 * j + i] = grid_code<B>(v[8 * j + i], kk[j]) - kHalf;
+  uint32_t d[6];
+  e2m3_pack32(h, d);
+  uint32_t lo[4] = {d[0], (d[1] >> 16) | (d[2] << 16), d[3], (d[4] >> 16) | (d[5] << 16)};
+  uint32_t hi[4] = {d[1] & 0xFFFFu, d[2] >> 16, d[4] & 0xFFFFu, d[5] >> 16};
+  transpose_quarters(lo);
+  transpose_quarters(hi);
+  const uint32_t w0 = lo[0], w1 = hi[0] | (lo[1] << 16), w2 = (lo[1] >> 16) | (hi[1] << 16);
+  const uint32_t w3 = lo[2], w4 = hi[2] | (lo[3] << 16), w5 = (lo[3] >> 16) | (hi[3] << 16);
+  (void)lane;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, op_r, off, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w2, w3}, op_r, off == kNowhere ? kNowhere : off + 8, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w4, w5}, op_r, off == kNowhere ? kNowhere : off + 16, 0, kNonTemporal);
 }
 
 // Codes, mask and scale of one run per lane, once its row's sum of squares is
@@ -299,10 +390,21 @@ __global__ void __launch_bounds__(256)
     ss = group_sum(ss, log_runs_per_row);
     const int64_t run0 = t * 64;
     const rsrc_t codes_r = window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B);
-    const rsrc_t mask_r = window_at(mask, run0 * 4, total_runs * 4, 64 * 4);
+    const rsrc_t mask_r = window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4);
     const rsrc_t scale_r = window_at(scale, t * rows_per_tile * 4, rows * 4, rows_per_tile * 4);
     const RowConsts c = fwd_quantise_store<B>(v, tau, ss, k, lane, codes_r, mask_r, scale_r, scale_off);
-    fwd_store_dq<B>(v, c, dq, run0, total_runs, lane, stage);
+    if constexpr (kIsOperand<Dq>) {
+      // The tile's rows lie in one 32-row block (rows_per_tile divides 32).
+      const int64_t row0 = t * rows_per_tile;
+      const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
+      const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                    static_cast<uint32_t>(rb_bytes));
+      const int slot = operand_slot(static_cast<int>(row0 & 31) + (lane >> log_runs_per_row),
+                                    lane & ((1 << log_runs_per_row) - 1));
+      store_operand_run<B>(v, c.kk, op_r, run0 + lane < total_runs ? slot : kNowhere);
+    } else {
+      fwd_store_dq<B>(v, c, dq, run0, total_runs, lane, stage);
+    }
   };
 
   // Three tile buffers, fetched two tiles ahead.  Every fetch is issued (past
@@ -464,8 +566,17 @@ __global__ void __launch_bounds__(256)
     }
     const int64_t run0 = t * 64;
     mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
-                           window_at(mask, run0 * 4, total_runs * 4, 64 * 4));
-    if constexpr (DqOut<Dq>::kOn) {
+                           window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
+    if constexpr (kIsOperand<Dq>) {
+      // After the transpose lane l holds run l of the tile; the tile's rows
+      // lie in one 32-row block.
+      const int64_t row0 = t * ROWS;
+      const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
+      const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                    static_cast<uint32_t>(rb_bytes));
+      const int slot = operand_slot(static_cast<int>(row0 & 31) + (lane >> LOGR), lane & ((1 << LOGR) - 1));
+      mfma_store_operand<B>(v, kk, lane, op_r, run0 + lane < total_runs ? slot : kNowhere);
+    } else if constexpr (DqOut<Dq>::kOn) {
       constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
       mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, total_runs * RB, 64 * RB));
     }
@@ -567,8 +678,24 @@ __global__ void __launch_bounds__(1024)
   const int64_t run0 = wg_first_run + 64 * wave;
   const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
   mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
-                         window_at(mask, run0 * 4, run_end * 4, 64 * 4));
-  if constexpr (DqOut<Dq>::kOn) {
+                         window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
+  if constexpr (kIsOperand<Dq>) {
+    // After the transpose lane l holds run 64 w + l of the workgroup.
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+    const int64_t last = (row0 + rows_per_wg < rows ? row0 + rows_per_wg : rows) - 1;
+    const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
+    const int64_t rb0 = row0 >> 5;
+    const rsrc_t op_r = window_at(dq, rb0 * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                  static_cast<uint32_t>(((last >> 5) - rb0 + 1) * rb_bytes));
+    const int wr = 64 * wave + lane;
+    const int lrow = wr / runs_per_row;
+    const int64_t row = row0 + lrow;
+    const bool live = lrow < rows_per_wg && row < rows;
+    const int off = live ? static_cast<int>(((row >> 5) - rb0) * rb_bytes) +
+                               operand_slot(static_cast<int>(row & 31), wr - lrow * runs_per_row)
+                         : kNowhere;
+    mfma_store_operand<B>(v, kk, lane, op_r, off);
+  } else if constexpr (DqOut<Dq>::kOn) {
     constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
     mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, run_end * RB, 64 * RB));
   }
@@ -623,14 +750,29 @@ __global__ void __launch_bounds__(1024)
   }
   const uint32_t wg_runs = static_cast<uint32_t>(rows_per_wg * runs_per_row);
   const rsrc_t codes_r = window_at(codes, wg_first_run * 4 * B, codes ? total_runs * 4 * B : 0, wg_runs * 4 * B);
-  const rsrc_t mask_r = window_at(mask, wg_first_run * 4, total_runs * 4, wg_runs * 4);
+  const rsrc_t mask_r = window_at(mask, wg_first_run * 4, mask ? total_runs * 4 : 0, wg_runs * 4);
   const rsrc_t scale_r =
       window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
   const int scale_off = (run_in_row == 0 && lrow < rows_per_wg) ? lrow * 4 : kNowhere;
   const RowConsts c = fwd_quantise_store<B>(v, tau, ss, k, tid, codes_r, mask_r, scale_r, scale_off);
   // Lanes past the workgroup's rows must not write the next workgroup's runs.
   const int64_t wg_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
-  fwd_store_dq<B>(v, c, dq, wg_first_run + wave_tid0, wg_end, lane, stage_all[wave_tid0 >> 6]);
+  if constexpr (kIsOperand<Dq>) {
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+    const int64_t last = (row0 + rows_per_wg < rows ? row0 + rows_per_wg : rows) - 1;
+    const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
+    const int64_t rb0 = row0 >> 5;
+    const rsrc_t op_r = window_at(dq, rb0 * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                  static_cast<uint32_t>(((last >> 5) - rb0 + 1) * rb_bytes));
+    const int64_t row = row0 + lrow;
+    const bool live = lrow < rows_per_wg && row < rows;
+    const int off = live ? static_cast<int>(((row >> 5) - rb0) * rb_bytes) +
+                               operand_slot(static_cast<int>(row & 31), run_in_row)
+                         : kNowhere;
+    store_operand_run<B>(v, c.kk, op_r, off);
+  } else {
+    fwd_store_dq<B>(v, c, dq, wg_first_run + wave_tid0, wg_end, lane, stage_all[wave_tid0 >> 6]);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -727,6 +869,7 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
   // Trusted: |y| <= s + trust * Delta / 2, i.e. |v| <= alpha sqrt(n) (1 + trust / (L - 1)) RMS.
   k.thr = static_cast<float>(a.alpha * sqrt_n * (1.0 + a.trust / (L - 1.0)));
   k.inv_cols = static_cast<float>(1.0 / double(a.cols));
+  k.chunks = static_cast<int>(a.cols / 128);
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(a.mask);
   Dq* dq = static_cast<Dq*>(a.dq);
   hipStream_t stream = a.stream;
@@ -783,15 +926,24 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
 
 template <typename In, int LOGN, typename Dq>
 hipError_t fwd_dispatch_bits(const In* x, int bits, const FwdLaunch& a) {
-  switch (bits) {
-    case 1: return fwd_dispatch<In, LOGN, 1, Dq>(x, a);
-    case 2: return fwd_dispatch<In, LOGN, 2, Dq>(x, a);
-    case 3: return fwd_dispatch<In, LOGN, 3, Dq>(x, a);
-    case 4: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
-    case 5: return fwd_dispatch<In, LOGN, 5, Dq>(x, a);
-    case 6: return fwd_dispatch<In, LOGN, 6, Dq>(x, a);
-    case 7: return fwd_dispatch<In, LOGN, 7, Dq>(x, a);
-    default: return fwd_dispatch<In, LOGN, 8, Dq>(x, a);
+  if constexpr (kIsOperand<Dq>) {  // the operand holds grids of at most 4 bits
+    switch (bits) {
+      case 1: return fwd_dispatch<In, LOGN, 1, Dq>(x, a);
+      case 2: return fwd_dispatch<In, LOGN, 2, Dq>(x, a);
+      case 3: return fwd_dispatch<In, LOGN, 3, Dq>(x, a);
+      default: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
+    }
+  } else {
+    switch (bits) {
+      case 1: return fwd_dispatch<In, LOGN, 1, Dq>(x, a);
+      case 2: return fwd_dispatch<In, LOGN, 2, Dq>(x, a);
+      case 3: return fwd_dispatch<In, LOGN, 3, Dq>(x, a);
+      case 4: return fwd_dispatch<In, LOGN, 4, Dq>(x, a);
+      case 5: return fwd_dispatch<In, LOGN, 5, Dq>(x, a);
+      case 6: return fwd_dispatch<In, LOGN, 6, Dq>(x, a);
+      case 7: return fwd_dispatch<In, LOGN, 7, Dq>(x, a);
+      default: return fwd_dispatch<In, LOGN, 8, Dq>(x, a);
+    }
   }
 }
 

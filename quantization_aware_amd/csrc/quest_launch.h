@@ -20,7 +20,8 @@ struct FwdLaunch {
 };
 
 // x_is_bf16: 1 = bf16 input, 0 = fp32.  dq_kind: 0 = no dequantised output,
-// 1 = bf16, 2 = fp32 into a.dq.  All sizes already validated.
+// 1 = bf16, 2 = fp32 into a.dq, 3 = the matrix-core operand into a.dq
+// (bits <= 4, cols a multiple of 128).  All sizes already validated.
 hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int log_block, int bits, int dq_kind,
                                const FwdLaunch& a);
 
@@ -28,11 +29,30 @@ hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int log_block, int 
 hipError_t launch_fwd_nodq(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 hipError_t launch_fwd_dq_bf16(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 hipError_t launch_fwd_dq_f32(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
+hipError_t launch_fwd_op(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
                              void* out, int out_is_bf16, hipStream_t stream);
 
 hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
                             int log_block, void* grad_out, hipStream_t stream);
+
+// Arguments of one product of two matrix-core operands, already validated:
+// out (m x n, row-major) = Delta_a Delta_b * (A B^T) with Delta = scale * k*.
+struct GemmLaunch {
+  const uint8_t* a;  // tiled E2M3 operand, m rows
+  const float* sa;   // clip scale per row of a
+  int m;
+  const uint8_t* b;  // tiled E2M3 operand, n rows
+  const float* sb;
+  int n;
+  int k;     // a multiple of 128
+  float ka;  // 2 / (L_a - 1)
+  float kb;  // 2 / (L_b - 1)
+  void* out;
+  hipStream_t stream;
+};
+
+hipError_t launch_gemm_e2m3(const GemmLaunch& g, bool out_bf16);
 
 }  // namespace quest

@@ -9,6 +9,7 @@ hipError_t launch_quantize_fwd(const void* x, int x_is_bf16, int log_block, int 
   switch (dq_kind) {
     case 1: return launch_fwd_dq_bf16(x, x_is_bf16, log_block, bits, a);
     case 2: return launch_fwd_dq_f32(x, x_is_bf16, log_block, bits, a);
+    case 3: return launch_fwd_op(x, x_is_bf16, log_block, bits, a);
     default: return launch_fwd_nodq(x, x_is_bf16, log_block, bits, a);
   }
 }

@@ -206,6 +206,26 @@ WORKLOADS = {
 }
 
 
+# The seven products of one 1.6B-scale Llama block at 16384 tokens: the
+# activations (16384 x 2048 into q, k, v, o, gate and up; the 16384 x 5632
+# MLP intermediate into down) times the C3 weights, both quantised to 4 bits
+# along the contraction axis (block 128).
+LAYER_TOKENS = 16384
+LAYER_ACT_2048 = TensorSpec("L.x2048", LAYER_TOKENS, 2048, "bf16", "student_t", 4, 7, outlier_cols=20,
+                            outlier_scale=20.0)
+LAYER_ACT_5632 = TensorSpec("L.x5632", LAYER_TOKENS, 5632, "bf16", "student_t", 4, 8, outlier_cols=56,
+                            outlier_scale=20.0)
+
+
+def layer_products() -> list[tuple[str, TensorSpec, TensorSpec]]:
+    """(name, activation spec, weight spec) of the block's seven matrix products."""
+    out = []
+    for w in WORKLOADS["C3"].fwd:
+        act = LAYER_ACT_5632 if w.cols == 5632 else LAYER_ACT_2048
+        out.append((w.name.split(".", 1)[1], act, w))
+    return out
+
+
 def to_float64(t: torch.Tensor):
     """Exact float64 NumPy copy of a float32 / bfloat16 tensor (for the oracle)."""
     return t.detach().to("cpu").to(torch.float64).numpy()

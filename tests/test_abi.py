@@ -9,6 +9,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import quantization_aware_amd as qa
@@ -282,3 +283,84 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(qa, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         qa.load_library(str(tmp_path / "missing.so"))
+
+
+# ---------------------------------------------------------------------------
+# Matrix-core operand forward and the product of two operands
+# ---------------------------------------------------------------------------
+
+def fwd_op(lib, x=A, dt=qa.QUEST_BF16, rows=4, cols=256, block=128, b=4, trust=1.0, codes=None, scale=C_, mask=None,
+           op=E_):
+    return lib.quest_quantize_fwd_op(x, dt, rows, cols, block, b, trust, codes, scale, mask, op, None)
+
+
+def gemm(lib, a=A, sa=B_, m=300, ab=4, b=C_, sb=D_, n=200, bb=4, k=256, out=E_, dt=qa.QUEST_BF16):
+    return lib.quest_gemm(a, sa, m, ab, b, sb, n, bb, k, out, dt, None)
+
+
+def test_operand_bytes(lib):
+    assert lib.quest_operand_bytes(45, 384) == 64 * 384 * 3 // 4
+    assert lib.quest_operand_bytes(32, 128) == 3072
+    assert lib.quest_operand_bytes(33, 128) == 2 * 3072
+    assert lib.quest_operand_bytes(0, 128) == 0
+    assert lib.quest_operand_bytes(4, 192) == 0
+    assert lib.quest_operand_bytes(-1, 128) == 0
+    rng = np.random.default_rng(0)
+    op = rng.integers(0, 256, size=(45, 384 * 3 // 4), dtype=np.uint8)
+    assert qo.tile_operand(op, 45, 384).size == lib.quest_operand_bytes(45, 384)
+
+
+def test_fwd_op_and_gemm_empty_calls_are_noops(lib):
+    assert fwd_op(lib, x=None, scale=None, op=None, rows=0) == qa.QUEST_OK
+    assert gemm(lib, a=None, sa=None, b=None, sb=None, out=None, m=0) == qa.QUEST_OK
+    assert gemm(lib, a=None, sa=None, b=None, sb=None, out=None, n=0) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(b=5), qa.QUEST_EUNSUPPORTED),
+        (dict(b=0), qa.QUEST_EUNSUPPORTED),
+        (dict(cols=192, block=64), qa.QUEST_EUNSUPPORTED),  # not a multiple of 128
+        (dict(block=512), qa.QUEST_EUNSUPPORTED),
+        (dict(dt=5), qa.QUEST_EINVAL),
+        (dict(trust=-1.0), qa.QUEST_EINVAL),
+        (dict(x=None), qa.QUEST_EINVAL),
+        (dict(scale=None), qa.QUEST_EINVAL),
+        (dict(op=None), qa.QUEST_EINVAL),
+        (dict(op=E_ + 8), qa.QUEST_EALIGN),
+        (dict(mask=D_ + 4), qa.QUEST_EALIGN),
+        (dict(op=A), qa.QUEST_EINVAL),  # overlaps x
+        (dict(op=C_ - 1024), qa.QUEST_EINVAL),  # 6144 operand bytes (32 padded rows) run over scale
+        (dict(codes=E_ + 64), qa.QUEST_EINVAL),  # codes inside the operand
+    ],
+)
+def test_fwd_op_rejects(lib, kw, status):
+    assert fwd_op(lib, **kw) == status
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(ab=5), qa.QUEST_EUNSUPPORTED),
+        (dict(bb=0), qa.QUEST_EUNSUPPORTED),
+        (dict(k=192), qa.QUEST_EUNSUPPORTED),
+        (dict(k=65536 + 128), qa.QUEST_EUNSUPPORTED),
+        (dict(n=2 ** 20 + 1), qa.QUEST_EUNSUPPORTED),
+        (dict(m=2 ** 30 + 1), qa.QUEST_EUNSUPPORTED),
+        (dict(k=0), qa.QUEST_EINVAL),
+        (dict(k=-128), qa.QUEST_EINVAL),
+        (dict(m=-1), qa.QUEST_EINVAL),
+        (dict(dt=7), qa.QUEST_EINVAL),
+        (dict(a=None), qa.QUEST_EINVAL),
+        (dict(sb=None), qa.QUEST_EINVAL),
+        (dict(out=None), qa.QUEST_EINVAL),
+        (dict(a=A + 8), qa.QUEST_EALIGN),
+        (dict(sa=B_ + 4), qa.QUEST_EALIGN),
+        (dict(out=E_ + 4), qa.QUEST_EALIGN),
+        (dict(out=A), qa.QUEST_EINVAL),  # overlaps a
+        (dict(out=D_ - 4096), qa.QUEST_EINVAL),  # 120000 output bytes run over b_scale
+    ],
+)
+def test_gemm_rejects(lib, kw, status):
+    assert gemm(lib, **kw) == status

@@ -645,3 +645,22 @@ def test_quest_gemm_is_the_layer_product(bx, bw):
     y = qo.quest_gemm(qo.operand_e2m3(fx["codes"], 256, bx), fx["scale"], bx,
                       qo.operand_e2m3(fw["codes"], 256, bw), fw["scale"], bw, 256)
     assert np.allclose(y, f["y"], rtol=1e-12, atol=1e-15)
+
+
+def test_tiled_operand_slot_positions_and_round_trip():
+    # Byte j of the 24 bytes of run (r, t) = columns 32 t .. 32 t + 31 of row r sits at
+    # (r // 32) * (C / 128) * 3072 + (t // 4) * 3072 + (t // 2 % 2) * 1536 + (32 (t % 2) + r % 32) * 24 + j.
+    rows, cols = 45, 384
+    rng = np.random.default_rng(5)
+    op = rng.integers(0, 256, size=(rows, cols * 6 // 8), dtype=np.uint8)
+    tiled = qo.tile_operand(op, rows, cols)
+    assert tiled.size == 64 * cols * 6 // 8
+    for r, t, j in [(0, 0, 0), (1, 0, 5), (31, 1, 23), (32, 2, 0), (44, 11, 17), (7, 6, 9)]:
+        pos = (r // 32) * (cols // 128) * 3072 + (t // 4) * 3072 + (t // 2 % 2) * 1536 + (32 * (t % 2) + r % 32) * 24 + j
+        assert tiled[pos] == op[r, 24 * t + j]
+    assert np.array_equal(qo.untile_operand(tiled, rows, cols), op)
+    # padding rows of the last row block are zero
+    pad = [(45 + i) % 32 for i in range(64 - 45)]
+    last = tiled[(1 * (cols // 128)) * 3072:].reshape(cols // 128, 2, 64, 24)
+    for rr in pad:
+        assert not last[:, :, rr, :].any() and not last[:, :, 32 + rr, :].any()
