@@ -51,6 +51,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-block-products", action="store_true",
+                   help="skip the 4-bit products of a 1.6B-scale block (FP6 matrix cores vs BF16)")
+    p.add_argument("--product-reps", type=int, default=50, help="back-to-back launches per product timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain elementwise copy of known size (for counter calibration)")
     return p.parse_args()
@@ -128,6 +131,93 @@ def cpu_baseline(x_dev, g_dev, target_seconds):
         "sample": f"{done} rows ({done * COLS} elements; {done / ROWS:.2f} passes over the 16384x2048 workload, "
         f"in {chunk}-row chunks), fwd then bwd, {elapsed:.1f} s of oracle time",
         "cpu_count": os.cpu_count(),
+    }
+
+
+FP6_PEAK_TFLOPS = 10100.0  # MI355X dense FP6/FP4 matrix peak
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def block_products(lib, qa, torch, dev, reps):
+    """The seven 4-bit products of a 1.6B-scale Llama block at 16384 tokens.
+
+    Per product: the activation's forward into the matrix-core operand
+    (Hadamard, RMS scale, codes as FP6 levels), the FP6 product with the
+    pre-quantised weight (bf16 output), and torch's BF16 product of the same
+    bf16 tensors (hipBLASLt) -- each timed as `reps` back-to-back launches
+    between HIP events on the launch stream.  The block total quantises each
+    distinct activation once (attention input for q, k, v; attention output
+    for o; MLP input for gate and up; MLP intermediate for down).
+    """
+    from quest_inputs import LAYER_ACT_2048, LAYER_ACT_5632, layer_products, make_tensor
+
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(launch):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def check(name, st):
+        if st:
+            raise qa.QuestError(name, st, lib.quest_status_string(st).decode())
+
+    acts = {}
+    for spec in (LAYER_ACT_2048, LAYER_ACT_5632):
+        x = make_tensor(spec, dev)
+        op = torch.empty((qa.operand_bytes(spec.rows, spec.cols),), dtype=torch.uint8, device=dev)
+        sc = torch.empty((spec.rows,), dtype=torch.float32, device=dev)
+        args = (ctypes.c_void_p(x.data_ptr()), qa.QUEST_BF16, spec.rows, spec.cols, BLOCK, 4, ctypes.c_double(1.0),
+                None, ctypes.c_void_p(sc.data_ptr()), None, ctypes.c_void_p(op.data_ptr()), sh)
+        t_q = timed(lambda: check("quest_quantize_fwd_op", lib.quest_quantize_fwd_op(*args)))
+        acts[spec.cols] = {"x": x, "op": op, "scale": sc, "quant_ms": t_q}
+    rows = []
+    for name, act, wt in layer_products():
+        a = acts[act.cols]
+        m, k, n = act.rows, act.cols, wt.rows
+        w = make_tensor(wt, dev)
+        _, w_scale, _, w_op = qa.quantize_fwd_op(w, BLOCK, 4)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        gargs = (ctypes.c_void_p(a["op"].data_ptr()), ctypes.c_void_p(a["scale"].data_ptr()), m, 4,
+                 ctypes.c_void_p(w_op.data_ptr()), ctypes.c_void_p(w_scale.data_ptr()), n, 4, k,
+                 ctypes.c_void_p(out.data_ptr()), qa.QUEST_BF16, sh)
+        t_g = timed(lambda: check("quest_gemm", lib.quest_gemm(*gargs)))
+        x = a["x"]
+        t_b = timed(lambda: torch.nn.functional.linear(x, w))
+        flops = 2.0 * m * n * k
+        rows.append({
+            "product": name, "m": m, "n": n, "k": k,
+            "quest_gemm_us": 1000 * t_g, "quantise_activation_us": 1000 * a["quant_ms"],
+            "bf16_us": 1000 * t_b,
+            "fp6_tflops": flops / (t_g * 1e9), "bf16_tflops": flops / (t_b * 1e9),
+            "speedup_product": t_b / t_g,
+            "speedup_with_quantisation": t_b / (t_g + a["quant_ms"]),
+        })
+        del w, w_op, w_scale, out
+    t_fp6 = sum(r["quest_gemm_us"] for r in rows) + 3 * acts[2048]["quant_ms"] * 1000 + acts[5632]["quant_ms"] * 1000
+    t_bf16 = sum(r["bf16_us"] for r in rows)
+    flops = sum(2.0 * r["m"] * r["n"] * r["k"] for r in rows)
+    big = max(rows, key=lambda r: r["m"] * r["n"] * r["k"] / r["quest_gemm_us"])
+    return {
+        "workload": "the q, k, v, o, gate, up, down products of a 1.6B-scale Llama block at 16384 tokens, "
+                    "activations and weights quantised to 4 bits (block 128) vs the same bf16 products",
+        "products": rows,
+        "block_fp6_us": t_fp6,
+        "block_bf16_us": t_bf16,
+        "block_speedup": t_bf16 / t_fp6,
+        "block_tflops_fp6_incl_quantisation": flops / (t_fp6 * 1e6),
+        "roofline": {"bound": "mfma", "kernel": "quest_gemm_e2m3_kernel<bf16>", "product": big["product"],
+                     "achieved": round(big["fp6_tflops"], 1), "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(big["fp6_tflops"] / FP6_PEAK_TFLOPS, 4)},
+        "reps": reps,
     }
 
 
@@ -363,6 +453,8 @@ def main():
                    "one_stream_ms_per_step": one_stream_ms,
                    "host_enqueue_s": enqueue, "one_stream_host_enqueue_s": enqueue_one},
     }
+    if not args.no_block_products:
+        out["block_products"] = block_products(lib, qa, torch, dev, args.product_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x0, g0, args.cpu_seconds)
     print(json.dumps(out), flush=True)

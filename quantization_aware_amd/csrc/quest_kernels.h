@@ -250,6 +250,23 @@ struct DqOut<OperandOut> {
 template <typename Dq>
 constexpr bool kIsOperand = std::is_same<Dq, OperandOut>::value;
 
+// Workgroup index of the forward kernels.  Workgroups are dealt to the 8 XCDs
+// round-robin; an operand's 128-byte lines each hold parts of several
+// neighbouring rows, so for the operand workgroup b takes the logical index
+// (b % 8) * (G / 8) + b / 8: each XCD then works through one contiguous range
+// of rows and every line is completed inside one L2 (the last G % 8
+// workgroups keep their index).  Other outputs keep the launch order.
+template <typename Dq>
+__device__ __forceinline__ int64_t fwd_wg_index() {
+  const int64_t b = blockIdx.x;
+  if constexpr (!kIsOperand<Dq>) {
+    return b;
+  } else {
+    const int64_t full = static_cast<int64_t>(gridDim.x) & ~int64_t(7);
+    return b < full ? (b & 7) * (full >> 3) + (b >> 3) : b;
+  }
+}
+
 constexpr int kOpBlockBytes = 3072;  // 32 rows x 128 columns at 6 bits
 
 // Offset of run j of a row inside its row block.
@@ -288,9 +305,9 @@ __device__ __forceinline__ void store_operand_run(const float (&v)[RUN], float k
   for (int i = 0; i < RUN; ++i) h[i] = grid_code<B>(v[i], kk) - kHalf;
   uint32_t w[6];
   e2m3_pack32(h, w);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, op_r, off, 0, kNonTemporal);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, op_r, off == kNowhere ? kNowhere : off + 8, 0, kNonTemporal);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[4], w[5]}, op_r, off == kNowhere ? kNowhere : off + 16, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, op_r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, op_r, off == kNowhere ? kNowhere : off + 8, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[4], w[5]}, op_r, off == kNowhere ? kNowhere : off + 16, 0, 0);
 }
 
 // Matrix-core kernels: v[8 j .. 8 j + 7] of lane (g, n) are entries
@@ -316,9 +333,9 @@ __device__ __forceinline__ void mfma_store_operand(const float (&v)[RUN], const 
   const uint32_t w0 = lo[0], w1 = hi[0] | (lo[1] << 16), w2 = (lo[1] >> 16) | (hi[1] << 16);
   const uint32_t w3 = lo[2], w4 = hi[2] | (lo[3] << 16), w5 = (lo[3] >> 16) | (hi[3] << 16);
   (void)lane;
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, op_r, off, 0, kNonTemporal);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w2, w3}, op_r, off == kNowhere ? kNowhere : off + 8, 0, kNonTemporal);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w4, w5}, op_r, off == kNowhere ? kNowhere : off + 16, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, op_r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w2, w3}, op_r, off == kNowhere ? kNowhere : off + 8, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w4, w5}, op_r, off == kNowhere ? kNowhere : off + 16, 0, 0);
 }
 
 // Codes, mask and scale of one run per lane, once its row's sum of squares is
@@ -375,7 +392,7 @@ __global__ void __launch_bounds__(256)
   const int64_t rows = total_runs >> log_runs_per_row;
   const int64_t tiles = (total_runs + 63) >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
   if (tile >= tiles) return;
   const int rows_per_tile = 64 >> log_runs_per_row;
   const int scale_off = (lane & ((1 << log_runs_per_row) - 1)) == 0 ? (lane >> log_runs_per_row) * 4 : kNowhere;
@@ -518,7 +535,7 @@ __global__ void __launch_bounds__(256)
   const int64_t rows = total_runs >> LOGR;
   const int64_t tiles = (total_runs + 63) >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
   if (tile >= tiles) return;
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
@@ -623,11 +640,12 @@ __global__ void __launch_bounds__(1024)
                                FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
                                uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
   __shared__ float group_ss[64];
+  const int64_t wg = fwd_wg_index<Dq>();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t total_runs = rows * runs_per_row;
   const uint32_t wg_runs = static_cast<uint32_t>(rows_per_wg * runs_per_row);
-  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * wg_runs;
+  const int64_t wg_first_run = wg * wg_runs;
   const int groups_per_row = runs_per_row >> 4;
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
@@ -681,7 +699,7 @@ __global__ void __launch_bounds__(1024)
                          window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
   if constexpr (kIsOperand<Dq>) {
     // After the transpose lane l holds run 64 w + l of the workgroup.
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+    const int64_t row0 = wg * rows_per_wg;
     const int64_t last = (row0 + rows_per_wg < rows ? row0 + rows_per_wg : rows) - 1;
     const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
     const int64_t rb0 = row0 >> 5;
@@ -705,7 +723,7 @@ __global__ void __launch_bounds__(1024)
   const bool first = lane < 4 && my_group % groups_per_row == 0 && my_row < rows_per_wg;
   const float my_scale = my_row == row_a ? ca.scale : cb.scale;
   const rsrc_t scale_r =
-      window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
+      window_at(scale, wg * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), scale_r, first ? my_row * 4 : kNowhere, 0, 0);
 }
 
@@ -725,12 +743,13 @@ __global__ void __launch_bounds__(1024)
   constexpr int US = U > DqOut<Dq>::U ? U : DqOut<Dq>::U;
   __shared__ u32x4 stage_all[16][64 * US];
   __shared__ float part[1024];
+  const int64_t wg = fwd_wg_index<Dq>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int lrow = tid / runs_per_row;
   const int run_in_row = tid - lrow * runs_per_row;
   const int64_t total_runs = rows * runs_per_row;
-  const int64_t wg_first_run = static_cast<int64_t>(blockIdx.x) * rows_per_wg * runs_per_row;
+  const int64_t wg_first_run = wg * rows_per_wg * runs_per_row;
   const int wave_tid0 = __builtin_amdgcn_readfirstlane(tid) & ~63;
 
   uint32_t raw[4 * U];
@@ -752,13 +771,13 @@ __global__ void __launch_bounds__(1024)
   const rsrc_t codes_r = window_at(codes, wg_first_run * 4 * B, codes ? total_runs * 4 * B : 0, wg_runs * 4 * B);
   const rsrc_t mask_r = window_at(mask, wg_first_run * 4, mask ? total_runs * 4 : 0, wg_runs * 4);
   const rsrc_t scale_r =
-      window_at(scale, static_cast<int64_t>(blockIdx.x) * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
+      window_at(scale, wg * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
   const int scale_off = (run_in_row == 0 && lrow < rows_per_wg) ? lrow * 4 : kNowhere;
   const RowConsts c = fwd_quantise_store<B>(v, tau, ss, k, tid, codes_r, mask_r, scale_r, scale_off);
   // Lanes past the workgroup's rows must not write the next workgroup's runs.
   const int64_t wg_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
   if constexpr (kIsOperand<Dq>) {
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+    const int64_t row0 = wg * rows_per_wg;
     const int64_t last = (row0 + rows_per_wg < rows ? row0 + rows_per_wg : rows) - 1;
     const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
     const int64_t rb0 = row0 >> 5;
