@@ -68,9 +68,12 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
                static_cast<int32_t>(bytes), 0x00020000};
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even (finite values)
+// Two floats to bf16 with round to nearest even (the gfx950 conversion instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // 16 bytes from global memory into LDS at lds_base + 16 * lane.  Written as
@@ -244,6 +247,13 @@ __global__ void __launch_bounds__(256)
   const auto rout = make_rsrc(out + static_cast<size_t>(tm) * kTileM * n,
                               static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
   const int r32 = lane & 31, h = lane >> 5;
+  // column factors of the lane's 64 columns: 32 j + 8 q + 4 h + (0..3)
+  float4 fbs[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 128 + 32 * j + 8 * q + 4 * h]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float fa = fac[wm * 128 + 32 * i + r32];
@@ -252,7 +262,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 128
-        const float4 fb = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 128 + cl]);
+        const float4 fb = fbs[j][q];
         const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
         const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
         uint8_t* d = slab + r32 * kPitch + cl * kOut;
@@ -261,7 +271,7 @@ __global__ void __launch_bounds__(256)
               u32x4{__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
         } else {
           *reinterpret_cast<u32x2*>(d) =
-              u32x2{bf16_bits(y0) | (bf16_bits(y1) << 16), bf16_bits(y2) | (bf16_bits(y3) << 16)};
+              u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
         }
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
