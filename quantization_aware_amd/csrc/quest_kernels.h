@@ -312,12 +312,11 @@ __device__ __forceinline__ void store_operand_run(const float (&v)[RUN], float k
 
 // Matrix-core kernels: v[8 j .. 8 j + 7] of lane (g, n) are entries
 // 8 g .. 8 g + 7 of run 16 j + n (factor kk[j]).  Each slot's eight fields
-// (48 bits) are split into a low dword and a high half-word, a transpose
-// between lane quarters and slots hands lane l the four quarters of run l,
-// which it stores at byte offset `off` of `op_r`.
+// (48 bits) are split into a low dword and a high half-word, and a
+// transpose between lane quarters and slots hands lane l the four quarters
+// of run l: its six dwords, in field order.
 template <int B>
-__device__ __forceinline__ void mfma_store_operand(const float (&v)[RUN], const float (&kk)[4], int lane, rsrc_t op_r,
-                                                   int off) {
+__device__ __forceinline__ void mfma_operand_words(const float (&v)[RUN], const float (&kk)[4], uint32_t (&w)[6]) {
   constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
   float h[RUN];
 #pragma unroll
@@ -330,12 +329,46 @@ __device__ __forceinline__ void mfma_store_operand(const float (&v)[RUN], const 
   uint32_t hi[4] = {d[1] & 0xFFFFu, d[2] >> 16, d[4] & 0xFFFFu, d[5] >> 16};
   transpose_quarters(lo);
   transpose_quarters(hi);
-  const uint32_t w0 = lo[0], w1 = hi[0] | (lo[1] << 16), w2 = (lo[1] >> 16) | (hi[1] << 16);
-  const uint32_t w3 = lo[2], w4 = hi[2] | (lo[3] << 16), w5 = (lo[3] >> 16) | (hi[3] << 16);
-  (void)lane;
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, op_r, off, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w2, w3}, op_r, off == kNowhere ? kNowhere : off + 8, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w4, w5}, op_r, off == kNowhere ? kNowhere : off + 16, 0, 0);
+  w[0] = lo[0];
+  w[1] = hi[0] | (lo[1] << 16);
+  w[2] = (lo[1] >> 16) | (hi[1] << 16);
+  w[3] = lo[2];
+  w[4] = hi[2] | (lo[3] << 16);
+  w[5] = (lo[3] >> 16) | (hi[3] << 16);
+}
+
+// Six operand dwords (one run) to byte offset `off` of `op_r` (kNowhere drops them).
+__device__ __forceinline__ void store_operand_words(const uint32_t (&w)[6], rsrc_t op_r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, op_r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, op_r, off == kNowhere ? kNowhere : off + 8, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[4], w[5]}, op_r, off == kNowhere ? kNowhere : off + 16, 0, 0);
+}
+
+// Operand staging in LDS for a workgroup that holds R consecutive rows of one
+// 32-row block (R divides 32, the first row a multiple of R): in the tiled
+// layout the R rows' slots of one run j are adjacent, 24 R contiguous bytes.
+// Run j of row r goes to LDS byte j (24 R + 8) + 24 r (the 8-byte pad spreads
+// the runs over the banks); the pieces are then written out by the whole
+// workgroup as 8-byte stores that cover whole pieces, not 24-byte slots.
+__device__ __forceinline__ void stage_operand_words(uint8_t* st, int j, int r, int R, const uint32_t (&w)[6]) {
+  u32x2* d = reinterpret_cast<u32x2*>(st + j * (24 * R + 8) + 24 * r);
+  d[0] = u32x2{w[0], w[1]};
+  d[1] = u32x2{w[2], w[3]};
+  d[2] = u32x2{w[4], w[5]};
+}
+
+// Write the staged pieces of runs 0 .. runs - 1 (R rows from row r0 of its
+// block) through `op_r`, the window of that row block.  Thread t of n takes
+// the 8-byte words t, t + n, ...
+__device__ __forceinline__ void flush_operand(const uint8_t* st, int R, int runs, int r0_in_block, rsrc_t op_r, int t,
+                                              int n) {
+  const int per = 3 * R;  // words per piece
+  const int words = runs * per;
+  for (int q = t; q < words; q += n) {
+    const int j = q / per, within = q - j * per;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(st + j * (24 * R + 8) + 8 * within);
+    __builtin_amdgcn_raw_buffer_store_b64(v, op_r, operand_slot(r0_in_block, j) + 8 * within, 0, 0);
+  }
 }
 
 // Codes, mask and scale of one run per lane, once its row's sum of squares is
@@ -536,7 +569,12 @@ __global__ void __launch_bounds__(256)
   const int64_t tiles = (total_runs + 63) >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
   int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
-  if (tile >= tiles) return;
+  // The operand is staged per workgroup step (a barrier per tile), so the
+  // four waves then run the same steps: a wave past the last tile computes
+  // on zeros and every store it makes is dropped or lands in padding.
+  const int64_t tile_end = kIsOperand<Dq> ? tiles + wave : tiles;
+  if (tile >= tile_end) return;
+  __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
   const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
@@ -585,14 +623,19 @@ __global__ void __launch_bounds__(256)
     mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
                            window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
     if constexpr (kIsOperand<Dq>) {
-      // After the transpose lane l holds run l of the tile; the tile's rows
-      // lie in one 32-row block.
-      const int64_t row0 = t * ROWS;
+      // After the transpose lane l holds run l of the tile.  The workgroup's
+      // four tiles are 4 ROWS consecutive rows of one 32-row block.
+      uint32_t w[6];
+      mfma_operand_words<B>(v, kk, w);
+      stage_operand_words(opstage, lane & ((1 << LOGR) - 1), wave * ROWS + (lane >> LOGR), 4 * ROWS, w);
+      __syncthreads();
+      const int64_t row0 = (t - wave) * ROWS;
       const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
       const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
                                     static_cast<uint32_t>(rb_bytes));
-      const int slot = operand_slot(static_cast<int>(row0 & 31) + (lane >> LOGR), lane & ((1 << LOGR) - 1));
-      mfma_store_operand<B>(v, kk, lane, op_r, run0 + lane < total_runs ? slot : kNowhere);
+      flush_operand(opstage, 4 * ROWS, 1 << LOGR, static_cast<int>(row0 & 31), op_r, static_cast<int>(threadIdx.x),
+                    256);
+      __syncthreads();
     } else if constexpr (DqOut<Dq>::kOn) {
       constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
       mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, total_runs * RB, 64 * RB));
@@ -611,15 +654,15 @@ __global__ void __launch_bounds__(256)
     fetch(tile + 2 * stride, c);
     process(tile, a);
     tile += stride;
-    if (tile >= tiles) break;
+    if (tile >= tile_end) break;
     fetch(tile + 2 * stride, a);
     process(tile, b);
     tile += stride;
-    if (tile >= tiles) break;
+    if (tile >= tile_end) break;
     fetch(tile + 2 * stride, b);
     process(tile, c);
     tile += stride;
-    if (tile >= tiles) break;
+    if (tile >= tile_end) break;
   }
 }
 
@@ -709,10 +752,12 @@ __global__ void __launch_bounds__(1024)
     const int lrow = wr / runs_per_row;
     const int64_t row = row0 + lrow;
     const bool live = lrow < rows_per_wg && row < rows;
+    uint32_t w[6];
+    mfma_operand_words<B>(v, kk, w);
     const int off = live ? static_cast<int>(((row >> 5) - rb0) * rb_bytes) +
                                operand_slot(static_cast<int>(row & 31), wr - lrow * runs_per_row)
                          : kNowhere;
-    mfma_store_operand<B>(v, kk, lane, op_r, off);
+    store_operand_words(w, op_r, off);
   } else if constexpr (DqOut<Dq>::kOn) {
     constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
     mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, run_end * RB, 64 * RB));

@@ -69,6 +69,8 @@ FWD_OP_CASES = [
     (29, 640, "f32", 128, 3, 1.0),
     (64, 128, "bf16", 128, 4, 1.0),
     (1, 256, "f32", 256, 1, 1.3),
+    (7, 10752, "bf16", 128, 4, 1.0),  # wide rows, 3 rows per workgroup: unstaged stores
+    (130, 4096, "bf16", 128, 2, 1.0),  # wide rows, 1 row per workgroup
 ]
 
 
