@@ -19,6 +19,8 @@ each function names the page and section it follows):
 * Product of two quantised operands (b <= 4): each grid value over its row's
   step is a half-integer, held as an FP6 E2M3 element; the product is the
   float64 matrix product of the decoded, rescaled operands.
+* Other grids: FP4 (E2M1) levels with a Gaussian-MSE-optimal scale, and
+  2:4-sparse b-bit codes (2 of every 4 Hadamard-domain entries kept).
 
 Everything is float64 NumPy.  The Hadamard product is the dense O(n^2)
 definition (a matrix product against the explicit n x n matrix), the clip
@@ -76,6 +78,19 @@ __all__ = [
     "quest_gemm",
     "tile_operand",
     "untile_operand",
+    "gaussian_mse_levels",
+    "gaussian_mse_levels_derivative",
+    "fit_alpha_levels",
+    "e2m1_value",
+    "e2m1_round",
+    "fit_alpha_fp4",
+    "quantize_rows_fp4",
+    "quantize_fwd_fp4",
+    "dequantize_fp4",
+    "sparse24_keep",
+    "quantize_rows_sparse24",
+    "quantize_fwd_sparse24",
+    "dequantize_sparse24",
 ]
 
 
@@ -597,3 +612,226 @@ def untile_operand(tiled: np.ndarray, rows: int, cols: int) -> np.ndarray:
                     first_col = 128 * c + 64 * e + 32 * (lane // 32)
                     out[row, first_col * 6 // 8:(first_col + 32) * 6 // 8] = blocks[rb, c, e, lane]
     return out[:rows]
+
+
+# ---------------------------------------------------------------------------
+# Other grids: FP4 levels and 2:4-sparse integer codes.
+# The pages extend the method to an FP4 format and to 2:4-sparse INT4
+# (pith.science review of QuEST, the list of contributions and the captions
+# of Figures 3 and 4; atlas.scime.ai summary, "Key results": FP4 fits a
+# slightly worse scaling law than INT4, which the authors attribute to a
+# higher Gaussian MSE once clipping is allowed; the ablation table: 2:4
+# sparsity added to INT4).  FP4 is the E2M1 element type of the OCP MX
+# specification v1.0: sign bit 3, exponent bits 2..1 with bias 1, mantissa
+# bit 0, subnormals at exponent 0, no infinities or NaN; magnitudes
+# 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+# ---------------------------------------------------------------------------
+
+def gaussian_mse_levels(levels) -> float:
+    """E[(Q(X) - X)^2], X ~ N(0, 1), for nearest-level rounding onto `levels` (sorted).
+
+    Cells run between midpoints of neighbouring levels; the outer cells are
+    unbounded (clipping).  Same per-cell closed form as ``gaussian_mse``.
+    """
+    lv = [float(v) for v in levels]
+    th = [-math.inf] + [0.5 * (lv[k - 1] + lv[k]) for k in range(1, len(lv))] + [math.inf]
+    total = 0.0
+    for k, level in enumerate(lv):
+        a, c = th[k], th[k + 1]
+        total += (1.0 + level * level) * (_std_normal_cdf(c) - _std_normal_cdf(a))
+        total -= _t_times_pdf(c) - _t_times_pdf(a)
+        total += 2.0 * level * (_std_normal_pdf(c) - _std_normal_pdf(a))
+    return total
+
+
+def gaussian_mse_levels_derivative(unit_levels, alpha: float) -> float:
+    """d/d alpha of gaussian_mse_levels(alpha * unit_levels) (cell edges contribute nothing)."""
+    lv = [alpha * float(v) for v in unit_levels]
+    th = [-math.inf] + [0.5 * (lv[k - 1] + lv[k]) for k in range(1, len(lv))] + [math.inf]
+    total = 0.0
+    for k, unit in enumerate(unit_levels):
+        a, c = th[k], th[k + 1]
+        first_moment = _std_normal_pdf(a) - _std_normal_pdf(c)
+        mass = _std_normal_cdf(c) - _std_normal_cdf(a)
+        total += float(unit) * (first_moment - float(unit) * alpha * mass)
+    return -2.0 * total
+
+
+def fit_alpha_levels(unit_levels) -> float:
+    """alpha minimising the Gaussian MSE of the grid alpha * unit_levels (largest level 1).
+
+    Golden-section search on [0.05, 8], then bisection on the derivative, as
+    ``fit_alpha``.
+    """
+    f = lambda a: gaussian_mse_levels([a * v for v in unit_levels])
+    guess = _golden_section_min(f, 0.05, 8.0, 1e-9)
+    lo, hi = guess * (1.0 - 1e-4), guess * (1.0 + 1e-4)
+    while gaussian_mse_levels_derivative(unit_levels, lo) > 0.0:
+        lo *= 0.9
+    while gaussian_mse_levels_derivative(unit_levels, hi) < 0.0:
+        hi *= 1.1
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            break
+        if gaussian_mse_levels_derivative(unit_levels, mid) < 0.0:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def e2m1_value(code) -> np.ndarray:
+    """Decode 4-bit E2M1 codes (sign bit 3, exponent bits 2..1, mantissa bit 0)."""
+    code = np.asarray(code, dtype=np.int64)
+    if code.size and (code.min() < 0 or code.max() > 15):
+        raise ValueError("E2M1 codes are 4-bit")
+    sign = np.where((code >> 3) & 1, -1.0, 1.0)
+    exp = (code >> 1) & 3
+    man = (code & 1).astype(np.float64)
+    mag = np.where(exp == 0, man * 0.5, (1.0 + man * 0.5) * np.exp2(exp - 1.0))
+    return sign * mag
+
+
+FP4_MAGNITUDES = e2m1_value(np.arange(8))  # 0, 0.5, 1, 1.5, 2, 3, 4, 6
+FP4_UNIT_LEVELS = np.concatenate([-FP4_MAGNITUDES[:0:-1], FP4_MAGNITUDES]) / 6.0  # 15 levels, largest 1
+
+
+def e2m1_round(z) -> np.ndarray:
+    """E2M1 code of the level nearest to z; a tie goes to the code with mantissa bit 0;
+    beyond 6 in magnitude the code saturates at +-6.  The sign bit is that of z (-0 keeps it)."""
+    z = np.asarray(z, dtype=np.float64)
+    mag = np.abs(z)
+    dist = np.abs(mag[..., None] - FP4_MAGNITUDES)  # to each magnitude level
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best  # nearest levels (two on a tie)
+    # among the nearest, prefer an even code (mantissa bit 0), then the smaller code
+    score = np.where(cand, (np.arange(8) & 1) * 16 + np.arange(8), 1000)
+    code = np.argmin(score, axis=-1)
+    code = np.where(mag > 6.0, 7, code)
+    return np.where(np.signbit(z), code | 8, code).astype(np.int64)
+
+
+def fit_alpha_fp4() -> float:
+    """alpha of the FP4 grid: its largest level sits at alpha * RMS."""
+    return fit_alpha_levels(FP4_UNIT_LEVELS)
+
+
+def quantize_rows_fp4(y: np.ndarray, alpha: float, trust: float = 1.0):
+    """FP4 quantiser of Hadamard-domain rows y (R x C).
+
+    s = alpha * RMS (the largest level), q = e2m1(code) * s / 6 with
+    code = e2m1_round(6 y / s).  Trust (the pages' rule of at most half a
+    quantisation interval, read for an uneven grid): inside [-s, s] the error
+    must not exceed half the interval between the two levels around y;
+    beyond it, t times half the outermost interval, (6 - 4)/2 * s/6.  A zero
+    row gives s = 0, code 0, q = 0, mask 1.
+    Returns (codes, s, m, q).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    rms = np.sqrt(np.mean(y * y, axis=1))
+    s = alpha * rms
+    zero_row = s == 0.0
+    safe_s = np.where(zero_row, 1.0, s)
+    code = e2m1_round(6.0 * y / safe_s[:, None])
+    code[zero_row, :] = 0
+    unit = s[:, None] / 6.0
+    q = e2m1_value(code) * unit
+    err = np.abs(q - y)
+    a = np.abs(y) / np.where(zero_row, 1.0, unit[:, 0])[:, None]  # |y| in units of s/6
+    idx = np.clip(np.searchsorted(FP4_MAGNITUDES, a, side="right") - 1, 0, 6)
+    half_local = 0.5 * (FP4_MAGNITUDES[idx + 1] - FP4_MAGNITUDES[idx]) * unit
+    half_outer = 0.5 * (FP4_MAGNITUDES[7] - FP4_MAGNITUDES[6]) * unit
+    inside = np.abs(y) <= s[:, None]
+    m = np.where(inside, err <= half_local, err <= trust * half_outer)
+    m[zero_row, :] = True
+    return code, s, m, q
+
+
+def quantize_fwd_fp4(x: np.ndarray, block: int, alpha: float | None = None, trust: float = 1.0) -> dict:
+    """Hadamard -> RMS -> FP4 levels -> trust mask; codes packed 4 bits per element LSB-first."""
+    if alpha is None:
+        alpha = fit_alpha_fp4()
+    y = blockwise_hadamard(x, block)
+    code, s, m, q = quantize_rows_fp4(y, alpha, trust)
+    return {"codes": pack_lsb_first(code, 4), "scale": s, "mask": pack_lsb_first(m.astype(np.int64), 1), "y": y,
+            "u": code, "m": m, "q": q, "alpha": alpha}
+
+
+def dequantize_fp4(codes: np.ndarray, scale: np.ndarray, cols: int) -> np.ndarray:
+    """FP4 grid values e2m1(code) * s / 6."""
+    code = unpack_lsb_first(codes, 4, cols)
+    return e2m1_value(code) * np.asarray(scale, dtype=np.float64)[:, None] / 6.0
+
+
+def sparse24_keep(y: np.ndarray) -> np.ndarray:
+    """2:4 pattern: in each group of 4 consecutive entries of a row the 2 largest |y| stay
+    (on equal magnitudes the lower index wins)."""
+    y = np.asarray(y, dtype=np.float64)
+    rows, cols = y.shape
+    g = np.abs(y).reshape(rows, cols // 4, 4)
+    keep = np.zeros(g.shape, dtype=bool)
+    for r in range(rows):
+        for k in range(cols // 4):
+            order = sorted(range(4), key=lambda i: (-g[r, k, i], i))
+            keep[r, k, order[0]] = True
+            keep[r, k, order[1]] = True
+    return keep.reshape(rows, cols)
+
+
+def quantize_rows_sparse24(y: np.ndarray, b: int, alpha: float, trust: float = 1.0):
+    """2:4-sparse b-bit quantiser of Hadamard-domain rows y (R x C, C a multiple of 4).
+
+    The pattern keeps 2 of every 4 entries (``sparse24_keep``); the clip
+    scale is s = alpha_b * RMS of the kept entries; kept entries take the
+    b-bit code and level of ``quantize_rows`` (with that s); pruned entries
+    reconstruct as 0.  The mask is the literal trust rule on the sparse
+    reconstruction: kept entries as in ``quantize_rows``, pruned ones trusted
+    iff |0 - y| <= Delta / 2.
+    Returns (keep, u_kept (R x C/2, in index order), s, m, q).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    rows, cols = y.shape
+    keep = sparse24_keep(y)
+    kept = y[keep].reshape(rows, cols // 2)
+    u, s, m_kept, q_kept = quantize_rows(kept, b, alpha, trust)
+    big_l = 1 << b
+    delta = 2.0 * s / (big_l - 1)
+    q = np.zeros_like(y)
+    q[keep] = q_kept.reshape(-1)
+    m = np.abs(y) <= delta[:, None] / 2.0
+    m[keep] = m_kept.reshape(-1)
+    return keep, u, s, m, q
+
+
+def quantize_fwd_sparse24(x: np.ndarray, block: int, b: int, alpha: float | None = None, trust: float = 1.0) -> dict:
+    """Hadamard -> 2:4 pattern -> RMS of the kept entries -> b-bit codes -> trust mask.
+
+    Packed per row: the kept entries' codes (C/2 codes of b bits, LSB-first,
+    in index order) and their positions inside their group of 4 (C/2
+    2-bit fields, LSB-first); the mask as for the dense quantiser.
+    """
+    if alpha is None:
+        alpha = fit_alpha(b)
+    y = blockwise_hadamard(x, block)
+    keep, u, s, m, q = quantize_rows_sparse24(y, b, alpha, trust)
+    rows, cols = y.shape
+    pos = np.nonzero(keep.reshape(rows, cols // 4, 4))[2].reshape(rows, cols // 2)
+    return {"codes": pack_lsb_first(u, b), "index": pack_lsb_first(pos, 2), "scale": s,
+            "mask": pack_lsb_first(m.astype(np.int64), 1), "y": y, "u": u, "keep": keep, "m": m, "q": q,
+            "alpha": alpha}
+
+
+def dequantize_sparse24(codes: np.ndarray, index: np.ndarray, scale: np.ndarray, cols: int, b: int) -> np.ndarray:
+    """Dense Hadamard-domain values of a 2:4-sparse code stream (pruned entries 0)."""
+    big_l = 1 << b
+    u = unpack_lsb_first(codes, b, cols // 2)
+    pos = unpack_lsb_first(index, 2, cols // 2)
+    rows = u.shape[0]
+    s = np.asarray(scale, dtype=np.float64)
+    vals = (2 * u - big_l + 1) * s[:, None] / (big_l - 1)
+    out = np.zeros((rows, cols), dtype=np.float64)
+    grp = np.arange(cols // 2) // 2
+    for r in range(rows):
+        out[r, 4 * grp + pos[r]] = vals[r]
+    return out
