@@ -699,7 +699,9 @@ FP4_UNIT_LEVELS = np.concatenate([-FP4_MAGNITUDES[:0:-1], FP4_MAGNITUDES]) / 6.0
 
 def e2m1_round(z) -> np.ndarray:
     """E2M1 code of the level nearest to z; a tie goes to the code with mantissa bit 0;
-    beyond 6 in magnitude the code saturates at +-6.  The sign bit is that of z (-0 keeps it)."""
+    beyond 6 in magnitude the code saturates at +-6.  The sign bit is that of z, except on
+    the zero level, which is always code 0: one code per level of the grid, so that codes
+    compare as levels do."""
     z = np.asarray(z, dtype=np.float64)
     mag = np.abs(z)
     dist = np.abs(mag[..., None] - FP4_MAGNITUDES)  # to each magnitude level
@@ -709,7 +711,7 @@ def e2m1_round(z) -> np.ndarray:
     score = np.where(cand, (np.arange(8) & 1) * 16 + np.arange(8), 1000)
     code = np.argmin(score, axis=-1)
     code = np.where(mag > 6.0, 7, code)
-    return np.where(np.signbit(z), code | 8, code).astype(np.int64)
+    return np.where(np.signbit(z) & (code != 0), code | 8, code).astype(np.int64)
 
 
 def fit_alpha_fp4() -> float:

@@ -695,6 +695,9 @@ def test_e2m1_round_nearest_ties_even_saturating():
     for t, want in ties.items():
         assert qo.e2m1_value(qo.e2m1_round(np.array([t])))[0] == want
         assert qo.e2m1_value(qo.e2m1_round(np.array([-t])))[0] == -want
+    # the zero level has the one code 0 (both signs, and -0 itself)
+    assert qo.e2m1_round(np.array([-0.0, -0.2, 0.0, 0.2])).tolist() == [0, 0, 0, 0]
+    assert qo.e2m1_round(np.array([-0.3, -7.0])).tolist() == [9, 15]
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
