@@ -387,6 +387,27 @@ def main():
     ]
     fwd_dq_avg = timed_launches(lambda s_: check("quest_quantize_fwd_dq", f_fwd_dq(*fwd_dq_args[s_])))
     fwd_dq_bytes = ROWS * COLS * 2 + ROWS * COLS * 2 + ROWS * COLS // 8 + 4 * ROWS
+    # The other grids at the same workload: FP4 codes, and 2:4-sparse 4-bit codes with their positions.
+    fp4_codes = [torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    s24_codes = [torch.empty((ROWS, COLS // 4), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    s24_index = [torch.empty((ROWS, COLS // 8), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    f_fp4, f_s24 = lib.quest_quantize_fwd_fp4, lib.quest_quantize_fwd_sparse24
+    fp4_args = [
+        (ctypes.c_void_p(xs[i].data_ptr()), qa.QUEST_BF16, ROWS, COLS, BLOCK, 1.0,
+         ctypes.c_void_p(fp4_codes[i].data_ptr()), ctypes.c_void_p(scales[i].data_ptr()),
+         ctypes.c_void_p(masks[i].data_ptr()), None, qa.QUEST_BF16, sh)
+        for i in range(N_SETS)
+    ]
+    s24_args = [
+        (ctypes.c_void_p(xs[i].data_ptr()), qa.QUEST_BF16, ROWS, COLS, BLOCK, 4, 1.0,
+         ctypes.c_void_p(s24_codes[i].data_ptr()), ctypes.c_void_p(s24_index[i].data_ptr()),
+         ctypes.c_void_p(scales[i].data_ptr()), ctypes.c_void_p(masks[i].data_ptr()), None, qa.QUEST_BF16, sh)
+        for i in range(N_SETS)
+    ]
+    fp4_avg = timed_launches(lambda s_: check("quest_quantize_fwd_fp4", f_fp4(*fp4_args[s_])))
+    s24_avg = timed_launches(lambda s_: check("quest_quantize_fwd_sparse24", f_s24(*s24_args[s_])))
+    fp4_bytes = ROWS * COLS * 2 + ROWS * COLS // 2 + ROWS * COLS // 8 + 4 * ROWS
+    s24_bytes = ROWS * COLS * 2 + ROWS * COLS // 4 + ROWS * COLS // 8 + ROWS * COLS // 8 + 4 * ROWS
     fwd_bytes = alg_bytes_fwd(ROWS, COLS, 2, BITS)
     bwd_bytes = alg_bytes_bwd(ROWS, COLS, 2)
     copy_bytes = 2 * ROWS * COLS * 2
@@ -444,6 +465,12 @@ def main():
                 "avg_us": 1000 * fwd_dq_avg, "alg_bytes": fwd_dq_bytes,
                 "gbps": fwd_dq_bytes / (fwd_dq_avg * 1e6),
                 "frac_of_peak": round(fwd_dq_bytes / (fwd_dq_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+            "quest_quantize_fwd_fp4 (FP4 codes, mask, scale)": {
+                "avg_us": 1000 * fp4_avg, "alg_bytes": fp4_bytes, "gbps": fp4_bytes / (fp4_avg * 1e6),
+                "frac_of_peak": round(fp4_bytes / (fp4_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+            "quest_quantize_fwd_sparse24 (b=4: kept codes, positions, mask, scale)": {
+                "avg_us": 1000 * s24_avg, "alg_bytes": s24_bytes, "gbps": s24_bytes / (s24_avg * 1e6),
+                "frac_of_peak": round(s24_bytes / (s24_avg * 1e6) / HBM_PEAK_GBPS, 4)},
         },
         "copy_reference": {"kernel": "torch.neg, 16384x2048 bf16", "bytes": copy_bytes, "avg_us": 1000 * copy_avg,
                            "gbps": copy_gbps, "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},

@@ -274,6 +274,73 @@ quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a
                         const float* b_scale, int64_t n, int b_bits, int64_t k, void* out, quest_dtype out_dtype,
                         void* stream);
 
+/*
+ * Other grids of the pages: FP4 levels and 2:4-sparse codes.  The pages
+ * extend the method to an FP4 format and to 2:4-sparse INT4 (pith.science
+ * review of QuEST, the list of contributions and the captions of Figures 3
+ * and 4; atlas.scime.ai summary, "Key results": FP4 fits a slightly worse
+ * scaling law, which the authors put down to a higher Gaussian MSE when
+ * clipping is allowed; the ablation table: 2:4 sparsity added to INT4).
+ * Both run the same Hadamard transform, RMS scale and trust rule; the trust
+ * backward (quest_trust_bwd) takes their masks unchanged.
+ */
+
+/* alpha of the FP4 grid (largest level at alpha * RMS), minimising the
+   expected squared error for a standard Gaussian; host, cached. */
+double quest_fit_alpha_fp4(void);
+
+/*
+ * Forward onto the FP4 grid: levels e2m1(code) * s / 6 with the E2M1
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (OCP MX v1.0) and
+ * s = quest_fit_alpha_fp4() * RMS.  The code is the E2M1 bit pattern (sign
+ * bit 3) of the level nearest to 6 y / s (ties to the code with mantissa bit
+ * 0, saturating at +-6; the zero level is code 0), packed 4 bits per element
+ * LSB-first (quest_codes_bytes(rows, cols, 4)).  Trusted iff
+ * |y| <= s (1 + t / 6): beyond the grid, t times half the outermost interval.
+ *   codes  device output or NULL;  mask  device output (required)
+ *   dq     device output of dq_dtype or NULL: e2m1(code) * (s / 6)
+ * Everything else as for quest_quantize_fwd_ex.
+ */
+quest_status quest_quantize_fwd_fp4(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                    double trust, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                                    quest_dtype dq_dtype, void* stream);
+
+/*
+ * Forward onto the 2:4-sparse b-bit grid (b = 1..4, QUEST_EUNSUPPORTED
+ * otherwise).  In every group of 4 consecutive Hadamard-domain entries of a
+ * row (columns 4g .. 4g + 3) the 2 of largest |y| are kept (on equal
+ * magnitudes the lower index); s = alpha_b * RMS of the kept entries; kept
+ * entries take the code and level of the dense quantiser with that s; pruned
+ * entries reconstruct as 0.  Mask: kept entries as in quest_quantize_fwd_ex;
+ * pruned entries trusted iff |y| <= Delta / 2 (the trust rule with q = 0).
+ *   codes  device output or NULL: per row the cols / 2 kept codes, b bits
+ *          each, LSB-first in column order (quest_sparse24_codes_bytes)
+ *   index  device output or NULL: per row the kept entries' positions inside
+ *          their group, 2 bits each, LSB-first in the same order
+ *          (quest_sparse24_index_bytes)
+ *   dq     device output or NULL: the dense reconstruction (zeros pruned)
+ * Everything else as for quest_quantize_fwd_ex.
+ */
+quest_status quest_quantize_fwd_sparse24(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                         int b, double trust, uint8_t* codes, uint8_t* index, float* scale,
+                                         uint8_t* mask, void* dq, quest_dtype dq_dtype, void* stream);
+
+/* FP4 codes back to e2m1(code) * (s / 6), rounded to out_dtype.  Arguments
+   as for quest_dequantize with b = 4. */
+quest_status quest_dequantize_fp4(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, void* out,
+                                  quest_dtype out_dtype, void* stream);
+
+/* 2:4-sparse codes back to the dense reconstruction: (2u - L + 1) s / (L - 1)
+   at the kept positions, 0 elsewhere.  b = 1..4; index as written by
+   quest_quantize_fwd_sparse24; otherwise as quest_dequantize. */
+quest_status quest_dequantize_sparse24(const uint8_t* codes, const uint8_t* index, const float* scale, int64_t rows,
+                                       int64_t cols, int b, void* out, quest_dtype out_dtype, void* stream);
+
+/* Bytes of the 2:4-sparse codes: rows * (cols / 2) * b / 8; of the positions:
+   rows * cols / 8 (0 on invalid sizes: cols a positive multiple of 64, b 1..4). */
+size_t quest_sparse24_codes_bytes(int64_t rows, int64_t cols, int b);
+size_t quest_sparse24_index_bytes(int64_t rows, int64_t cols);
+
 /* Bytes of the packed codes: rows * cols * b / 8 (0 on invalid sizes). */
 size_t quest_codes_bytes(int64_t rows, int64_t cols, int b);
 

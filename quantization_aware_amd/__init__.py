@@ -26,6 +26,10 @@ __all__ = [
     "quantize_fwd_op",
     "operand_bytes",
     "gemm",
+    "quantize_fwd_fp4",
+    "quantize_fwd_sparse24",
+    "dequantize_fp4",
+    "dequantize_sparse24",
     "dequantize",
     "trust_bwd",
     "EXPORTED_SYMBOLS",
@@ -44,6 +48,13 @@ EXPORTED_SYMBOLS = (
     "quest_quantize_fwd_op",
     "quest_gemm",
     "quest_operand_bytes",
+    "quest_fit_alpha_fp4",
+    "quest_quantize_fwd_fp4",
+    "quest_quantize_fwd_sparse24",
+    "quest_dequantize_fp4",
+    "quest_dequantize_sparse24",
+    "quest_sparse24_codes_bytes",
+    "quest_sparse24_index_bytes",
     "quest_dequantize",
     "quest_trust_bwd",
     "quest_codes_bytes",
@@ -89,6 +100,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_gemm.restype = c_int
     lib.quest_operand_bytes.argtypes = [i64, i64]
     lib.quest_operand_bytes.restype = ctypes.c_size_t
+    lib.quest_fit_alpha_fp4.argtypes = []
+    lib.quest_fit_alpha_fp4.restype = ctypes.c_double
+    lib.quest_quantize_fwd_fp4.argtypes = [vp, c_int, i64, i64, c_int, ctypes.c_double, vp, vp, vp, vp, c_int, vp]
+    lib.quest_quantize_fwd_fp4.restype = c_int
+    lib.quest_quantize_fwd_sparse24.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp,
+                                                vp, c_int, vp]
+    lib.quest_quantize_fwd_sparse24.restype = c_int
+    lib.quest_dequantize_fp4.argtypes = [vp, vp, i64, i64, vp, c_int, vp]
+    lib.quest_dequantize_fp4.restype = c_int
+    lib.quest_dequantize_sparse24.argtypes = [vp, vp, vp, i64, i64, c_int, vp, c_int, vp]
+    lib.quest_dequantize_sparse24.restype = c_int
+    lib.quest_sparse24_codes_bytes.argtypes = [i64, i64, c_int]
+    lib.quest_sparse24_codes_bytes.restype = ctypes.c_size_t
+    lib.quest_sparse24_index_bytes.argtypes = [i64, i64]
+    lib.quest_sparse24_index_bytes.restype = ctypes.c_size_t
     lib.quest_dequantize.argtypes = [vp, vp, i64, i64, c_int, vp, c_int, vp]
     lib.quest_dequantize.restype = c_int
     lib.quest_trust_bwd.argtypes = [vp, c_int, vp, i64, i64, c_int, vp, vp]
@@ -294,6 +320,82 @@ def gemm(a: torch.Tensor, a_scale: torch.Tensor, m: int, a_bits: int, b: torch.T
     st = lib.quest_gemm(a.data_ptr(), a_scale.data_ptr(), m, int(a_bits), b.data_ptr(), b_scale.data_ptr(), n,
                         int(b_bits), k, out.data_ptr(), _dtype_code(out), _stream_handle(dev, stream))
     _check("quest_gemm", st)
+    return out
+
+
+def quantize_fwd_fp4(x: torch.Tensor, block: int, trust: float = 1.0, with_codes: bool = True, dq_dtype=None,
+                     stream=None):
+    """Forward onto the FP4 grid (quest_quantize_fwd_fp4): (codes or None, scale, mask, dq or None)."""
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if with_codes else None
+    scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
+    dq = torch.empty((rows, cols), dtype=dq_dtype, device=dev) if dq_dtype is not None else None
+    st = lib.quest_quantize_fwd_fp4(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), float(trust),
+        codes.data_ptr() if codes is not None else None, scale.data_ptr(), mask.data_ptr(),
+        dq.data_ptr() if dq is not None else None, _dtype_code(dq) if dq is not None else QUEST_BF16,
+        _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd_fp4", st)
+    return codes, scale, mask, dq
+
+
+def quantize_fwd_sparse24(x: torch.Tensor, block: int, b: int, trust: float = 1.0, with_codes: bool = True,
+                          dq_dtype=None, stream=None):
+    """Forward onto the 2:4-sparse b-bit grid (quest_quantize_fwd_sparse24).
+
+    Returns (codes or None, index or None, scale, mask, dq or None).
+    """
+    lib = load_library()
+    _device_tensor("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows x cols)")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols // 2 * b // 8), dtype=torch.uint8, device=dev) if with_codes else None
+    index = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev) if with_codes else None
+    scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
+    dq = torch.empty((rows, cols), dtype=dq_dtype, device=dev) if dq_dtype is not None else None
+    st = lib.quest_quantize_fwd_sparse24(
+        x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),
+        codes.data_ptr() if codes is not None else None, index.data_ptr() if index is not None else None,
+        scale.data_ptr(), mask.data_ptr(), dq.data_ptr() if dq is not None else None,
+        _dtype_code(dq) if dq is not None else QUEST_BF16, _stream_handle(dev, stream),
+    )
+    _check("quest_quantize_fwd_sparse24", st)
+    return codes, index, scale, mask, dq
+
+
+def dequantize_fp4(codes: torch.Tensor, scale: torch.Tensor, rows: int, cols: int, out_dtype=torch.float32,
+                   stream=None) -> torch.Tensor:
+    """FP4 codes back to their levels (quest_dequantize_fp4)."""
+    lib = load_library()
+    _device_tensor("codes", codes)
+    _device_tensor("scale", scale)
+    out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    st = lib.quest_dequantize_fp4(codes.data_ptr(), scale.data_ptr(), rows, cols, out.data_ptr(), _dtype_code(out),
+                                  _stream_handle(codes.device, stream))
+    _check("quest_dequantize_fp4", st)
+    return out
+
+
+def dequantize_sparse24(codes: torch.Tensor, index: torch.Tensor, scale: torch.Tensor, rows: int, cols: int, b: int,
+                        out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """2:4-sparse codes back to the dense reconstruction (quest_dequantize_sparse24)."""
+    lib = load_library()
+    for name, t in (("codes", codes), ("index", index), ("scale", scale)):
+        _device_tensor(name, t)
+    out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    st = lib.quest_dequantize_sparse24(codes.data_ptr(), index.data_ptr(), scale.data_ptr(), rows, cols, int(b),
+                                       out.data_ptr(), _dtype_code(out), _stream_handle(codes.device, stream))
+    _check("quest_dequantize_sparse24", st)
     return out
 
 

@@ -26,6 +26,7 @@ SOURCES = [
     "quest_fwd_dq_f32.hip",
     "quest_fwd_op.hip",
     "quest_gemm.hip",
+    "quest_grids.hip",
 ]
 # Sources whose matrix-core accumulators live in AGPRs: they are built without
 # the VGPR-only MFMA form.

@@ -66,12 +66,45 @@ double solve_alpha(int b) {
   return 0.5 * (lo + hi);
 }
 
+// The same least-squares fixed point for an arbitrary symmetric level set
+// (levels c_k alpha with the largest c_k = 1): used for the FP4 grid, whose
+// E2M1 magnitudes over 6 are 0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1.
+constexpr double kFp4Unit[15] = {-1.0,      -4.0 / 6.0, -3.0 / 6.0, -2.0 / 6.0, -1.5 / 6.0, -1.0 / 6.0,
+                                 -0.5 / 6.0, 0.0,       0.5 / 6.0,  1.0 / 6.0,  1.5 / 6.0,  2.0 / 6.0,
+                                 3.0 / 6.0,  4.0 / 6.0, 1.0};
+
+double alpha_update_levels(double alpha, const double* unit, int n) {
+  double num = 0.0, den = 0.0;
+  for (int k = 0; k < n; ++k) {
+    const double lo = k == 0 ? -std::numeric_limits<double>::infinity() : 0.5 * (unit[k - 1] + unit[k]) * alpha;
+    const double hi = k == n - 1 ? std::numeric_limits<double>::infinity() : 0.5 * (unit[k] + unit[k + 1]) * alpha;
+    num += unit[k] * (gauss_pdf(lo) - gauss_pdf(hi));
+    den += unit[k] * unit[k] * (gauss_cdf(hi) - gauss_cdf(lo));
+  }
+  return num / den;
+}
+
+double solve_alpha_fp4() {
+  double lo = 0.01, hi = 32.0;
+  for (int it = 0; it < 400; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (alpha_update_levels(mid, kFp4Unit, 15) > mid)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
 constexpr int kMaxBits = 8;
 double g_alpha[kMaxBits + 1];
+double g_alpha_fp4 = 0.0;
 std::once_flag g_alpha_once;
 
 void fill_alpha_table() {
   for (int b = 1; b <= kMaxBits; ++b) g_alpha[b] = solve_alpha(b);
+  g_alpha_fp4 = solve_alpha_fp4();
 }
 
 // Forward kernel selection, read once per process: QUEST_FWD_KERNEL=valu keeps
@@ -130,6 +163,12 @@ quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t row
                                  double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
                                  bool mask_required, void* dq, quest_dtype dq_dtype, bool dq_required,
                                  uint8_t* operand, void* stream);
+
+// Forward onto the FP4 grid (b == 0) or the 2:4-sparse b-bit grid.  Codes,
+// index and dq may be NULL; scale and mask are required.
+quest_status quantize_grid_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                  double trust, uint8_t* codes, uint8_t* index, float* scale, uint8_t* mask, void* dq,
+                                  quest_dtype dq_dtype, void* stream);
 
 // Largest contraction length of quest_gemm: sums of k products of
 // half-integers up to 7.5 stay below 2^22 in magnitude, so fp32 accumulates
@@ -235,6 +274,70 @@ quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a
   return from_hip(quest::launch_gemm_e2m3(g, out_dtype == QUEST_BF16));
 }
 
+double quest_fit_alpha_fp4(void) {
+  std::call_once(g_alpha_once, fill_alpha_table);
+  return g_alpha_fp4;
+}
+
+size_t quest_sparse24_codes_bytes(int64_t rows, int64_t cols, int b) {
+  if (rows < 0 || cols <= 0 || cols % 64 != 0 || b < 1 || b > 4) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(cols / 2 * b / 8);
+}
+
+size_t quest_sparse24_index_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || cols % 64 != 0) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(cols / 8);
+}
+
+quest_status quest_quantize_fwd_fp4(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                    double trust, uint8_t* codes, float* scale, uint8_t* mask, void* dq,
+                                    quest_dtype dq_dtype, void* stream) {
+  return quantize_grid_common(x, x_dtype, rows, cols, block, 0, trust, codes, nullptr, scale, mask, dq, dq_dtype,
+                              stream);
+}
+
+quest_status quest_quantize_fwd_sparse24(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block,
+                                         int b, double trust, uint8_t* codes, uint8_t* index, float* scale,
+                                         uint8_t* mask, void* dq, quest_dtype dq_dtype, void* stream) {
+  if (b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  return quantize_grid_common(x, x_dtype, rows, cols, block, b, trust, codes, index, scale, mask, dq, dq_dtype,
+                              stream);
+}
+
+quest_status quest_dequantize_fp4(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, void* out,
+                                  quest_dtype out_dtype, void* stream) {
+  if (!dtype_ok(out_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, 64);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!codes || !scale || !out) return QUEST_EINVAL;
+  if (!aligned16(codes) || !aligned16(scale) || !aligned16(out)) return QUEST_EALIGN;
+  const size_t nc = quest_codes_bytes(rows, cols, 4);
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t no = static_cast<size_t>(rows * cols) * dtype_size(out_dtype);
+  if (overlaps(out, no, codes, nc) || overlaps(out, no, scale, ns)) return QUEST_EINVAL;
+  return from_hip(quest::launch_dequantize_fp4(codes, scale, rows, cols, out, out_dtype == QUEST_BF16,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+quest_status quest_dequantize_sparse24(const uint8_t* codes, const uint8_t* index, const float* scale, int64_t rows,
+                                       int64_t cols, int b, void* out, quest_dtype out_dtype, void* stream) {
+  if (b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(out_dtype)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, 64);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!codes || !index || !scale || !out) return QUEST_EINVAL;
+  if (!aligned16(codes) || !aligned16(index) || !aligned16(scale) || !aligned16(out)) return QUEST_EALIGN;
+  const size_t nc = quest_sparse24_codes_bytes(rows, cols, b);
+  const size_t ni = quest_sparse24_index_bytes(rows, cols);
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t no = static_cast<size_t>(rows * cols) * dtype_size(out_dtype);
+  if (overlaps(out, no, codes, nc) || overlaps(out, no, index, ni) || overlaps(out, no, scale, ns)) return QUEST_EINVAL;
+  return from_hip(quest::launch_dequantize_sparse24(codes, index, scale, rows, cols, b, out, out_dtype == QUEST_BF16,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int b, void* out,
                               quest_dtype out_dtype, void* stream) {
   if (b < 1 || b > kMaxBits) return QUEST_EUNSUPPORTED;
@@ -317,6 +420,53 @@ quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t row
   a.stream = static_cast<hipStream_t>(stream);
   const int dq_kind = operand ? 3 : dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
   return from_hip(quest::launch_quantize_fwd(x, x_dtype == QUEST_BF16, lb, b, dq_kind, a));
+}
+
+}  // namespace
+
+namespace {
+
+quest_status quantize_grid_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                  double trust, uint8_t* codes, uint8_t* index, float* scale, uint8_t* mask, void* dq,
+                                  quest_dtype dq_dtype, void* stream) {
+  const int lb = log2_block(block);
+  if (lb < 0) return QUEST_EUNSUPPORTED;
+  if (!dtype_ok(x_dtype) || (dq && !dtype_ok(dq_dtype))) return QUEST_EINVAL;
+  if (!(trust >= 0.0) || !std::isfinite(trust)) return QUEST_EINVAL;
+  const quest_status sh = check_shape(rows, cols, block);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!x || !scale || !mask) return QUEST_EINVAL;
+  if (!aligned16(x) || (codes && !aligned16(codes)) || (index && !aligned16(index)) || !aligned16(scale) ||
+      !aligned16(mask) || (dq && !aligned16(dq)))
+    return QUEST_EALIGN;
+  const size_t nx = static_cast<size_t>(rows * cols) * dtype_size(x_dtype);
+  const size_t nc = codes ? (b == 0 ? quest_codes_bytes(rows, cols, 4) : quest_sparse24_codes_bytes(rows, cols, b)) : 0;
+  const size_t ni = index ? quest_sparse24_index_bytes(rows, cols) : 0;
+  const size_t ns = static_cast<size_t>(rows) * sizeof(float);
+  const size_t nm = quest_mask_bytes(rows, cols);
+  const size_t nd = dq ? static_cast<size_t>(rows * cols) * dtype_size(dq_dtype) : 0;
+  const void* bufs[6] = {x, codes, index, scale, mask, dq};
+  const size_t lens[6] = {nx, nc, ni, ns, nm, nd};
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return QUEST_EINVAL;
+  std::call_once(g_alpha_once, fill_alpha_table);
+  quest::GridLaunch a;
+  a.rows = rows;
+  a.cols = cols;
+  a.alpha = b == 0 ? g_alpha_fp4 : g_alpha[b];
+  a.trust = trust;
+  a.bits = b == 0 ? 4 : b;
+  a.sparse24 = b == 0 ? 0 : 1;
+  a.codes = codes;
+  a.index = index;
+  a.scale = scale;
+  a.mask = mask;
+  a.dq = dq;
+  a.stream = static_cast<hipStream_t>(stream);
+  const int dq_kind = dq ? (dq_dtype == QUEST_BF16 ? 1 : 2) : 0;
+  return from_hip(quest::launch_fwd_grid(x, x_dtype == QUEST_BF16, lb, dq_kind, a));
 }
 
 }  // namespace

@@ -772,6 +772,20 @@ __global__ void __launch_bounds__(1024)
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), scale_r, first ? my_row * 4 : kNowhere, 0, 0);
 }
 
+// LDS of the row-per-workgroup kernels, sized at launch by their wave count:
+// per wave a staging area of 64 * US 16-byte slots, then one float per lane
+// for the partial row sums.
+extern __shared__ u32x4 rows_lds[];
+
+inline size_t rows_lds_bytes(int threads, int us) {
+  return static_cast<size_t>(threads / 64) * 64 * static_cast<size_t>(us) * 16 + static_cast<size_t>(threads) * 4;
+}
+
+template <int US>
+__device__ __forceinline__ float* rows_part() {
+  return reinterpret_cast<float*>(rows_lds + (blockDim.x >> 6) * 64 * US);
+}
+
 // Rows that span several wavefronts (or whose run count is not a power of
 // two): a workgroup holds rows_per_wg whole rows, lane t holding run
 // (first run of the workgroup) + t.  Lanes reduce in aligned groups of
@@ -786,8 +800,8 @@ __global__ void __launch_bounds__(1024)
                           uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
   constexpr int U = sizeof(In) * 2;
   constexpr int US = U > DqOut<Dq>::U ? U : DqOut<Dq>::U;
-  __shared__ u32x4 stage_all[16][64 * US];
-  __shared__ float part[1024];
+  u32x4* const stage_all = rows_lds;
+  float* const part = rows_part<US>();
   const int64_t wg = fwd_wg_index<Dq>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -798,7 +812,8 @@ __global__ void __launch_bounds__(1024)
   const int wave_tid0 = __builtin_amdgcn_readfirstlane(tid) & ~63;
 
   uint32_t raw[4 * U];
-  wave_load_runs<U>(x, (wg_first_run + wave_tid0) * U, total_runs * U, lane, stage_all[wave_tid0 >> 6], raw);
+  u32x4* const stage = stage_all + (wave_tid0 >> 6) * 64 * US;
+  wave_load_runs<U>(x, (wg_first_run + wave_tid0) * U, total_runs * U, lane, stage, raw);
   float v[RUN];
   float ss;
   const float tau = fwd_transform<In, LOGN>(raw, v, ss, tid);
@@ -835,7 +850,7 @@ __global__ void __launch_bounds__(1024)
                          : kNowhere;
     store_operand_run<B>(v, c.kk, op_r, off);
   } else {
-    fwd_store_dq<B>(v, c, dq, wg_first_run + wave_tid0, wg_end, lane, stage_all[wave_tid0 >> 6]);
+    fwd_store_dq<B>(v, c, dq, wg_first_run + wave_tid0, wg_end, lane, stage);
   }
 }
 
@@ -981,8 +996,9 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
     if (rows_per_wg < 1) rows_per_wg = 1;
     const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((quest_fwd_rows_kernel<In, LOGN, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
-                       stream, x, rows, runs_per_row, rows_per_wg, log2_exact(group), k, a.codes, a.scale, mask32,
+    constexpr int US = 2 * sizeof(In) > DqOut<Dq>::U ? 2 * sizeof(In) : DqOut<Dq>::U;
+    hipLaunchKernelGGL((quest_fwd_rows_kernel<In, LOGN, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads),
+                       rows_lds_bytes(threads, US), stream, x, rows, runs_per_row, rows_per_wg, log2_exact(group), k, a.codes, a.scale, mask32,
                        dq);
   }
   return hipGetLastError();

@@ -55,4 +55,24 @@ struct GemmLaunch {
 
 hipError_t launch_gemm_e2m3(const GemmLaunch& g, bool out_bf16);
 
+// Arguments of one forward onto the FP4 grid (sparse24 = 0) or the 2:4-sparse
+// b-bit grid (sparse24 = 1), already validated.
+struct GridLaunch {
+  int64_t rows, cols;
+  double alpha, trust;
+  int bits, sparse24;
+  uint8_t* codes;  // may be null
+  uint8_t* index;  // 2:4 positions, may be null
+  float* scale;
+  uint8_t* mask;
+  void* dq;  // dequantised output or null
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_grid(const void* x, int x_is_bf16, int log_block, int dq_kind, const GridLaunch& a);
+hipError_t launch_dequantize_fp4(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, void* out,
+                                 int out_is_bf16, hipStream_t stream);
+hipError_t launch_dequantize_sparse24(const uint8_t* codes, const uint8_t* index, const float* scale, int64_t rows,
+                                      int64_t cols, int bits, void* out, int out_is_bf16, hipStream_t stream);
+
 }  // namespace quest

@@ -127,3 +127,123 @@ def check_grad(got: np.ndarray, ref: np.ndarray, block: int, tol: float) -> floa
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(scale > 0, err / (tol * np.where(scale > 0, scale, 1)), 0.0)
     return float(ratio.max(initial=0.0))
+
+
+# ---------------------------------------------------------------------------
+# FP4 and 2:4-sparse grids: the same rule, with their own thresholds.
+# ---------------------------------------------------------------------------
+FP4_DECISIONS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])  # midpoints of the E2M1 magnitudes
+
+
+def exempt_fp4(y: np.ndarray, s: np.ndarray, band: float = BAND, trust: float = 1.0) -> np.ndarray:
+    """True where |y| lies within band * s_r of an FP4 decision threshold (the midpoints
+    between E2M1 levels, in units of s_r / 6) or of the trust threshold s_r (1 + trust / 6)."""
+    s = np.asarray(s, dtype=np.float64)[:, None]
+    a = np.abs(y)
+    near = np.zeros(y.shape, dtype=bool)
+    for t in FP4_DECISIONS:
+        near |= np.abs(a - t * s / 6.0) <= band * s
+    near |= np.abs(a - s * (1.0 + trust / 6.0)) <= band * s
+    near[(s == 0.0)[:, 0], :] = False
+    return near
+
+
+def check_fwd_fp4(x64: np.ndarray, block: int, codes, scale, mask, trust: float = 1.0,
+                  max_fraction: float | None = MAX_MISMATCH_FRACTION, ref=None) -> dict:
+    rows, cols = x64.shape
+    if ref is None:
+        ref = qo.quantize_fwd_fp4(x64, block, trust=trust)
+    code = qo.unpack_lsb_first(np.asarray(codes).reshape(rows, cols // 2), 4, cols)
+    m = qo.unpack_lsb_first(np.asarray(mask).reshape(rows, cols // 8), 1, cols).astype(bool)
+    ex = exempt_fp4(ref["y"], ref["scale"], trust=trust)
+    bad = (code != ref["u"]) | (m != ref["m"])
+    hard = bad & ~ex
+    if hard.any():
+        r, c = np.argwhere(hard)[0]
+        raise AssertionError(f"FP4 mismatch at ({r},{c}): gpu code={code[r, c]} m={m[r, c]} oracle "
+                             f"code={ref['u'][r, c]} m={ref['m'][r, c]} y={ref['y'][r, c]!r} s={ref['scale'][r]!r}; "
+                             f"{int(hard.sum())} outside the band")
+    if max_fraction is not None:
+        assert int(bad.sum()) <= math.ceil(max_fraction * bad.size), f"{int(bad.sum())} differing entries"
+    _check_scale(scale, ref["scale"])
+    return {"exempt": int(ex.sum()), "mismatched": int(bad.sum()), "elements": int(bad.size), "bad": bad, "ref": ref}
+
+
+def _check_scale(scale, s_ref) -> float:
+    scale = np.asarray(scale, dtype=np.float64).reshape(-1)
+    zero = s_ref == 0.0
+    assert np.all(scale[zero] == 0.0)
+    rel = np.abs(scale[~zero] - s_ref[~zero]) / s_ref[~zero] if (~zero).any() else np.zeros(1)
+    assert rel.max(initial=0.0) <= 2e-6, f"scale relative error {rel.max()}"
+    return float(rel.max(initial=0.0))
+
+
+def sparse24_tie_groups(y: np.ndarray, s: np.ndarray, band: float = BAND) -> np.ndarray:
+    """True for groups of 4 whose second and third largest |y| lie within band * s_r:
+    the kept pair there is decided by rounding (R x C/4)."""
+    rows, cols = y.shape
+    g = np.sort(np.abs(y).reshape(rows, cols // 4, 4), axis=2)
+    s = np.asarray(s, dtype=np.float64)[:, None]
+    tie = (g[:, :, 2] - g[:, :, 1]) <= band * s
+    tie[(s == 0.0)[:, 0], :] = False
+    return tie
+
+
+def check_fwd_sparse24(x64: np.ndarray, block: int, b: int, codes, index, scale, mask, trust: float = 1.0,
+                       max_fraction: float | None = MAX_MISMATCH_FRACTION, ref=None) -> dict:
+    """Kept positions, their codes and the mask against the oracle.
+
+    The share of differing decisions (kept pairs, codes, mask bits) is bounded as for
+    the dense forward.
+
+    Exempt: whole groups whose kept pair is a near tie; kept entries near a
+    decision or trust threshold of the dense rule (with the kept RMS); pruned
+    entries near Delta / 2.
+    """
+    rows, cols = x64.shape
+    if ref is None:
+        ref = qo.quantize_fwd_sparse24(x64, block, b, trust=trust)
+    u = qo.unpack_lsb_first(np.asarray(codes).reshape(rows, cols // 16 * b), b, cols // 2)
+    pos = qo.unpack_lsb_first(np.asarray(index).reshape(rows, cols // 8), 2, cols // 2)
+    m = qo.unpack_lsb_first(np.asarray(mask).reshape(rows, cols // 8), 1, cols).astype(bool)
+    y, s = ref["y"], ref["scale"]
+    ref_pos = qo.unpack_lsb_first(ref["index"], 2, cols // 2)
+    tie = sparse24_tie_groups(y, s)
+    tie_slot = np.repeat(tie, 2, axis=1)
+    tie_entry = np.repeat(tie, 4, axis=1)
+    kept_y = y[ref["keep"]].reshape(rows, cols // 2)
+    ex_slot = tie_slot | exempt_entries(kept_y, s, b, trust=trust)
+    big_l = 1 << b
+    half = np.asarray(s)[:, None] / (big_l - 1)
+    ex_entry = tie_entry.copy()
+    ex_entry[ref["keep"]] |= exempt_entries(kept_y, s, b, trust=trust).reshape(-1)
+    near_zero = np.abs(np.abs(y) - half) <= BAND * np.asarray(s)[:, None]
+    ex_entry |= ~ref["keep"] & near_zero
+    bad_slot = (u != ref["u"]) | (pos != ref_pos)
+    bad_entry = m != ref["m"]
+    hard_slot = bad_slot & ~ex_slot
+    hard_entry = bad_entry & ~ex_entry
+    if hard_slot.any():
+        r, k = np.argwhere(hard_slot)[0]
+        raise AssertionError(f"2:4 slot mismatch at ({r},{k}): gpu u={u[r, k]} pos={pos[r, k]} oracle "
+                             f"u={ref['u'][r, k]} pos={ref_pos[r, k]} group |y|={np.abs(y[r, 4 * (k // 2):4 * (k // 2) + 4])}; "
+                             f"{int(hard_slot.sum())} outside the band")
+    if hard_entry.any():
+        r, c = np.argwhere(hard_entry)[0]
+        raise AssertionError(f"2:4 mask mismatch at ({r},{c}): gpu {m[r, c]} oracle {ref['m'][r, c]} y={y[r, c]!r}")
+    if max_fraction is not None:
+        # Counted per decision: a group whose kept pair differs is one decision (it moves
+        # two entries and their mask bits); outside such groups, each differing code or
+        # mask bit is one.
+        rows_, groups = tie.shape
+        pair_bad = (pos != ref_pos).reshape(rows_, groups, 2).any(axis=2)
+        other_slot = bad_slot & ~np.repeat(pair_bad, 2, axis=1)
+        other_entry = bad_entry & ~np.repeat(pair_bad, 4, axis=1)
+        n_bad = int(pair_bad.sum()) + int(other_slot.sum()) + int(other_entry.sum())
+        assert n_bad <= math.ceil(max_fraction * bad_entry.size), (
+            f"{n_bad} differing decisions: {int(pair_bad.sum())} kept pairs, {int(other_slot.sum())} codes, "
+            f"{int(other_entry.sum())} mask bits")
+    _check_scale(scale, s)
+    return {"tie_groups": int(tie.sum()), "mismatched_slots": int(bad_slot.sum()),
+            "mismatched_mask": int(bad_entry.sum()), "elements": int(bad_entry.size), "ex_entry": ex_entry,
+            "ref": ref}

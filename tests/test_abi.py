@@ -364,3 +364,81 @@ def test_fwd_op_rejects(lib, kw, status):
 )
 def test_gemm_rejects(lib, kw, status):
     assert gemm(lib, **kw) == status
+
+
+# ---------------------------------------------------------------------------
+# FP4 and 2:4-sparse grids
+# ---------------------------------------------------------------------------
+
+def test_fit_alpha_fp4_matches_oracle(lib):
+    assert math.isclose(lib.quest_fit_alpha_fp4(), qo.fit_alpha_fp4(), rel_tol=1e-12)
+
+
+def test_sparse24_byte_counts(lib):
+    assert lib.quest_sparse24_codes_bytes(3, 256, 4) == 3 * 128 // 2
+    assert lib.quest_sparse24_codes_bytes(3, 256, 1) == 3 * 128 // 8
+    assert lib.quest_sparse24_codes_bytes(3, 256, 5) == 0
+    assert lib.quest_sparse24_index_bytes(3, 256) == 3 * 32
+    assert lib.quest_sparse24_index_bytes(3, 100) == 0
+
+
+def fwd_fp4(lib, x=A, dt=qa.QUEST_BF16, rows=4, cols=256, block=128, trust=1.0, codes=B_, scale=C_, mask=D_, dq=None,
+            dq_dt=qa.QUEST_BF16):
+    return lib.quest_quantize_fwd_fp4(x, dt, rows, cols, block, trust, codes, scale, mask, dq, dq_dt, None)
+
+
+def fwd_s24(lib, x=A, dt=qa.QUEST_BF16, rows=4, cols=256, block=128, b=4, trust=1.0, codes=B_, index=E_, scale=C_,
+            mask=D_, dq=None, dq_dt=qa.QUEST_BF16):
+    return lib.quest_quantize_fwd_sparse24(x, dt, rows, cols, block, b, trust, codes, index, scale, mask, dq, dq_dt,
+                                           None)
+
+
+def test_grid_forwards_empty_calls_are_noops(lib):
+    assert fwd_fp4(lib, x=None, codes=None, scale=None, mask=None, rows=0) == qa.QUEST_OK
+    assert fwd_s24(lib, x=None, codes=None, index=None, scale=None, mask=None, rows=0) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(block=32), qa.QUEST_EUNSUPPORTED),
+        (dict(cols=200), qa.QUEST_EINVAL),
+        (dict(trust=-1.0), qa.QUEST_EINVAL),
+        (dict(dt=3), qa.QUEST_EINVAL),
+        (dict(x=None), qa.QUEST_EINVAL),
+        (dict(mask=None), qa.QUEST_EINVAL),
+        (dict(scale=None), qa.QUEST_EINVAL),
+        (dict(codes=B_ + 4), qa.QUEST_EALIGN),
+        (dict(dq=E_, dq_dt=7), qa.QUEST_EINVAL),
+        (dict(codes=A), qa.QUEST_EINVAL),  # overlaps x
+        (dict(codes=C_ - 256), qa.QUEST_EINVAL),  # 512 code bytes run over scale
+    ],
+)
+def test_fwd_fp4_rejects(lib, kw, status):
+    assert fwd_fp4(lib, **kw) == status
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(b=5), qa.QUEST_EUNSUPPORTED),
+        (dict(b=0), qa.QUEST_EUNSUPPORTED),
+        (dict(block=512), qa.QUEST_EUNSUPPORTED),
+        (dict(x=None), qa.QUEST_EINVAL),
+        (dict(mask=None), qa.QUEST_EINVAL),
+        (dict(index=E_ + 8), qa.QUEST_EALIGN),
+        (dict(index=D_ + 64), qa.QUEST_EINVAL),  # index inside the mask
+        (dict(dq=C_), qa.QUEST_EINVAL),  # dq over scale
+    ],
+)
+def test_fwd_sparse24_rejects(lib, kw, status):
+    assert fwd_s24(lib, **kw) == status
+
+
+def test_grid_dequantize_rejects(lib):
+    assert lib.quest_dequantize_fp4(A, B_, 4, 256, C_, 9, None) == qa.QUEST_EINVAL
+    assert lib.quest_dequantize_fp4(A, B_, 4, 256, A, qa.QUEST_F32, None) == qa.QUEST_EINVAL
+    assert lib.quest_dequantize_fp4(A, B_, 0, 256, None, qa.QUEST_F32, None) == qa.QUEST_OK
+    assert lib.quest_dequantize_sparse24(A, D_, B_, 4, 256, 5, C_, qa.QUEST_F32, None) == qa.QUEST_EUNSUPPORTED
+    assert lib.quest_dequantize_sparse24(A, None, B_, 4, 256, 4, C_, qa.QUEST_F32, None) == qa.QUEST_EINVAL
+    assert lib.quest_dequantize_sparse24(A, D_ + 2, B_, 4, 256, 4, C_, qa.QUEST_F32, None) == qa.QUEST_EALIGN
