@@ -69,7 +69,11 @@ using lanes_t = unsigned long long;
 __device__ __forceinline__ lanes_t lanes(bool c) { return __builtin_amdgcn_ballot_w64(c); }
 __device__ __forceinline__ bool lane_in(lanes_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
 
-// w = 2 w + (this lane's bit of m): one add with carry-in.
+// w = 2 w + (this lane's bit of m): one add with carry-in.  gfx950 needs two
+// wait states between a vector write of an SGPR and a vector read of it,
+// which the compiler cannot see inside asm: m and the masks of select_lanes
+// must come from scalar ops (the callers pass combinations of compare
+// masks), never straight from a compare.
 __device__ __forceinline__ void push_lane_bit(uint32_t& w, lanes_t m) {
   asm volatile("v_addc_co_u32_e64 %0, %1, %0, %0, %1" : "+v"(w), "+s"(m));
 }
@@ -218,8 +222,9 @@ __global__ void __launch_bounds__(1024)
         for (int j = 0; j < 4; ++j) q[4 * g + j] = i0 == static_cast<uint32_t>(j) ? l0 : i1 == static_cast<uint32_t>(j) ? l1 : 0.f;
       }
     }
-#pragma unroll
-    for (int i = RUN - 1; i >= 0; --i) push_lane_bit(mw, lanes(e[i] <= thr));
+    // e >= 0, so |e| <= thr is e <= thr
+    push16_abs_le(mw, e + 16, thr);
+    push16_abs_le(mw, e, thr);
     const rsrc_t codes_r = window_at(codes, wg_first_run * 2 * B, codes ? total_runs * 2 * B : 0, wg_runs * 2 * B);
     const int coff = live ? tid * 2 * B : kNowhere;
     const uint32_t lo = static_cast<uint32_t>(packed), hi = static_cast<uint32_t>(packed >> 32);
