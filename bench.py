@@ -41,7 +41,7 @@ HBM_PEAK_GBPS = 8000.0
 ROWS, COLS, BLOCK, BITS = 16384, 2048, 128, 4
 N_SETS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_16384x2048.txt")
-KERNEL_SOURCES = ["quest_device.h", "quest_kernels.h"]
+KERNEL_SOURCES = ["quest_device.h", "quest_kernels.h", "quest_grids.hip"]
 
 
 def parse_args():
@@ -464,13 +464,16 @@ def main():
             "quest_quantize_fwd_dq (no codes, bf16 dequantised output; QAT training forward)": {
                 "avg_us": 1000 * fwd_dq_avg, "alg_bytes": fwd_dq_bytes,
                 "gbps": fwd_dq_bytes / (fwd_dq_avg * 1e6),
-                "frac_of_peak": round(fwd_dq_bytes / (fwd_dq_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+                "frac_of_peak": round(fwd_dq_bytes / (fwd_dq_avg * 1e6) / HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic("fwd_dq")},
             "quest_quantize_fwd_fp4 (FP4 codes, mask, scale)": {
                 "avg_us": 1000 * fp4_avg, "alg_bytes": fp4_bytes, "gbps": fp4_bytes / (fp4_avg * 1e6),
-                "frac_of_peak": round(fp4_bytes / (fp4_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+                "frac_of_peak": round(fp4_bytes / (fp4_avg * 1e6) / HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic("fp4")},
             "quest_quantize_fwd_sparse24 (b=4: kept codes, positions, mask, scale)": {
                 "avg_us": 1000 * s24_avg, "alg_bytes": s24_bytes, "gbps": s24_bytes / (s24_avg * 1e6),
-                "frac_of_peak": round(s24_bytes / (s24_avg * 1e6) / HBM_PEAK_GBPS, 4)},
+                "frac_of_peak": round(s24_bytes / (s24_avg * 1e6) / HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic("sparse24")},
         },
         "copy_reference": {"kernel": "torch.neg, 16384x2048 bf16", "bytes": copy_bytes, "avg_us": 1000 * copy_avg,
                            "gbps": copy_gbps, "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
