@@ -198,6 +198,32 @@ def test_gemm_matches_oracle(dev, m, n, k, ba, bb):
     log(f"gemm ok: max relative error fp32 {r32:.3g}, bf16 {r16:.3g}")
 
 
+def test_gemm_exact_at_the_largest_k(dev):
+    """k = 65536, the largest accepted, with every level at +-7.5 (the largest magnitude):
+    sums reach 65536 * 56.25 = 3686400 in quarter steps, which fp32 still holds exactly.
+    With clip scales 7.5 the steps are 1, so every fp32 output is the exact sum."""
+    m, n, k, b = 32, 24, 65536, 4
+    log(f"gemm {m}x{n}x{k}, every level +-7.5")
+    rng = np.random.default_rng(8400)
+    ua = np.where(rng.random((m, k)) < 0.5, 0, 15)
+    ub = np.where(rng.random((n, k)) < 0.5, 0, 15)
+    ua[0] = 15  # rows of one sign: the largest sums, +3686400 and -3686400
+    ub[0] = 15
+    ub[1] = 0
+    op_a = qo.tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ua, b), k, b), m, k)
+    op_b = qo.tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ub, b), k, b), n, k)
+    sa = np.full(m, 7.5, dtype=np.float32)
+    sb = np.full(n, 7.5, dtype=np.float32)
+    ref = qo.quest_gemm(qo.untile_operand(op_a, m, k), sa.astype(np.float64), b, qo.untile_operand(op_b, n, k),
+                        sb.astype(np.float64), b, k)
+    assert ref[0, 0] == 3686400.0 and ref[0, 1] == -3686400.0
+    y = qa.gemm(torch.from_numpy(op_a).to(dev), torch.from_numpy(sa).to(dev), m, b, torch.from_numpy(op_b).to(dev),
+                torch.from_numpy(sb).to(dev), n, b, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} outputs differ from the exact sums"
+
+
 def test_gemm_writes_nothing_outside_the_output(dev):
     m, n, k = 70, 36, 256
     xa = to_float64(make_tensor(TensorSpec("g.ga", m, k, "f32", "normal", 1.0, 8200), "cpu"))
