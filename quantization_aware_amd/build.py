@@ -28,8 +28,10 @@ SOURCES = [
     "quest_gemm.hip",
     "quest_grids.hip",
 ]
-# Sources whose matrix-core accumulators live in AGPRs: they are built without
-# the VGPR-only MFMA form.
+# Sources built without the VGPR-only MFMA form, leaving the placement of the
+# matrix-core accumulators to the register allocator (the product kernel, whose
+# 128 accumulator registers per wave share the 256-register budget of two
+# waves per SIMD: the VGPR-only form spilled there).
 AGPR_SOURCES = {"quest_gemm.hip"}
 ARCH = "gfx950"
 NOISE = "is not a recognized feature for this target"  # the host pass does not know the GPU feature below

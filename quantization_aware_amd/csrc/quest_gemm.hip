@@ -22,15 +22,15 @@
 // LSB-first -- exactly the register operand of one lane of the 32x32x64
 // instruction.
 //
-// Kernel: a workgroup (4 waves, one per SIMD) computes a 256 x 256 output
-// tile, each wave a 128 x 128 quadrant (16 accumulator tiles of 32 x 32 in
-// AGPRs).  Operand blocks stream from HBM/L2 straight into LDS (buffer loads
-// with the LDS-destination bit, 1 KB per wave instruction), three stages deep.
-// Per stage (k = 128) a wave runs 32 MFMAs in two halves; the fragment reads
-// of the next half and the loads of the stage after next are interleaved
-// with them, and one barrier per stage publishes the next stage.  The
-// epilogue scales by Delta_a Delta_b and writes whole row segments through
-// LDS.
+// Kernel: a workgroup of 8 waves (two per SIMD) computes a 256 x 256 output
+// tile, each wave 128 rows x 64 columns (8 accumulator tiles of 32 x 32).
+// Operand blocks stream from HBM/L2 straight into LDS (buffer loads with the
+// LDS-destination bit, 1 KB per wave instruction), three stages deep.  Per
+// stage (k = 128) a wave runs 16 MFMAs in two halves, reading the next half's
+// fragments from LDS meanwhile; one barrier per stage publishes the next
+// stage.  With two waves per SIMD one wave's fragment reads and waits overlap
+// the other's MFMAs.  The epilogue scales by Delta_a Delta_b and writes whole
+// row segments through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,7 +93,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <typename Out, bool kVec>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512, 1)
     quest_gemm_e2m3_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
                            const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k, float ka,
                            float kb, Out* __restrict__ out) {
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(256)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 8 waves: 2 x 4, each 128 rows x 64 columns
   const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
   // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
   // contiguous range of tiles, walked in groups of 8 tile rows, so that the
@@ -126,13 +126,13 @@ __global__ void __launch_bounds__(256)
   const i32x4 rb = raw_rsrc(b + static_cast<size_t>(tn) * 8 * rb_bytes, min(rb_b - tn * 8, 8) * rb_bytes);
 
   // Stage st into LDS: each operand's 8 blocks are 24 KB = 24 wave
-  // instructions; wave w issues t = w + 4 u, u < 6, for both operands.
+  // instructions; wave w issues t = w + 8 u, u < 3, for both operands.
   auto fetch = [&](int st, auto bi) {
     const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage_mem(bi)));
     const i32x4 qa = ra, qb = rb;
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int t = wave + 4 * u, blk = t / 3, part = t % 3;
+    for (int u = 0; u < 3; ++u) {
+      const int t = wave + 8 * u, blk = t / 3, part = t % 3;
       const int goff = blk * static_cast<int>(rb_bytes) + st * kBlock + part * 1024 + lane * 16;
       const uint32_t la = base + blk * kBlock + part * 1024;
       dma16(__builtin_amdgcn_readfirstlane(la), goff, qa);
@@ -150,68 +150,48 @@ __global__ void __launch_bounds__(256)
   // acc[j][i]: 32 x 32 tile of the product B A^T for B block j and A block i,
   // so lane l holds output row 32 i + l % 32 and four consecutive columns per
   // register quad.
-  v16f acc[4][4];
+  v16f acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int i = 0; i < 4; ++i) acc[j][i] = v16f{};
 
   const int stages = chunks;
   fetch(0, I0{});
   fetch(stages > 1 ? 1 : 0, I1{});
-  wait_vmcnt<12>();  // stage 0 has landed (stage 1 may be in flight)
+  wait_vmcnt<6>();  // stage 0 has landed (stage 1 may be in flight)
   __syncthreads();
-  v8i f0a[4], f0b[4], f1a[4], f1b[4];
+  v8i f0a[4], f0b[2], f1a[4], f1b[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
-    f0b[i] = frag(I0{}, 1, wn * 4 + i, 0);
-  }
+  for (int i = 0; i < 4; ++i) f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f0b[j] = frag(I0{}, 1, wn * 2 + j, 0);
   // One stage: bi holds stage s, bn stage s + 1, b2 receives stage s + 2.
   // b2 last held stage s - 1, whose reads every wave finished before the
   // previous barrier.
   auto step = [&](int s, auto bi, auto bn, auto b2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f1a[i] = frag(bi, 0, wm * 4 + i, 1);
-      f1b[i] = frag(bi, 1, wn * 4 + i, 1);
-    }
+    for (int i = 0; i < 4; ++i) f1a[i] = frag(bi, 0, wm * 4 + i, 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j) f1b[j] = frag(bi, 1, wn * 2 + j, 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0b[j], f0a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
     fetch(s + 2 < stages ? s + 2 : stages - 1, b2);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two vector-memory loads
-    }
-    wait_vmcnt<12>();                   // stage s + 1 has landed
+    wait_vmcnt<6>();                    // stage s + 1 has landed
     __builtin_amdgcn_s_waitcnt(0xC07F);  // and this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f0a[i] = frag(bn, 0, wm * 4 + i, 0);
-      f0b[i] = frag(bn, 1, wn * 4 + i, 0);
-    }
+    for (int i = 0; i < 4; ++i) f0a[i] = frag(bn, 0, wm * 4 + i, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j) f0b[j] = frag(bn, 1, wn * 2 + j, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1b[j], f1a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
   int s = 0;
   for (; s + 3 <= stages; s += 3) {
@@ -229,39 +209,40 @@ __global__ void __launch_bounds__(256)
   {
     const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
     const auto rsb = make_rsrc(sb + static_cast<size_t>(tn) * kTileN, min(n - tn * kTileN, kTileN) * 4);
-    const float va = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0));
-    const float vb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, tid * 4, 0, 0));
-    fac[tid] = va * ka;
-    fac[kTileM + tid] = vb * kb;
+    const bool row_side = tid < kTileM;
+    const float v = __builtin_bit_cast(
+        float, row_side ? __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0)
+                        : __builtin_amdgcn_raw_buffer_load_b32(rsb, (tid - kTileM) * 4, 0, 0));
+    fac[tid] = v * (row_side ? ka : kb);
   }
   __syncthreads();
-  // Each wave stages a 32 x 128 slab of its quadrant in its own LDS region
-  // and writes it as whole 128-column row segments.
+  // Each wave stages a 32 x 64 slab of its part in its own LDS region and
+  // writes it as whole 64-column row segments.
   constexpr int kOut = static_cast<int>(sizeof(Out));
-  constexpr int kPitch = 128 * kOut + 16;      // slab row pitch in bytes
+  constexpr int kPitch = 64 * kOut + 16;       // slab row pitch in bytes
   constexpr int kPer = 16 / kOut;              // outputs per 16-byte chunk
-  constexpr int kLanesPerRow = 128 / kPer;
-  static_assert(4 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
+  constexpr int kLanesPerRow = 64 / kPer;
+  static_assert(8 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
   uint8_t* slab = lds + kStage + wave * 32 * kPitch;  // the factors stay in the first
   const int rows_left = m - tm * kTileM;
   const auto rout = make_rsrc(out + static_cast<size_t>(tm) * kTileM * n,
                               static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
   const int r32 = lane & 31, h = lane >> 5;
   // column factors of the lane's 64 columns: 32 j + 8 q + 4 h + (0..3)
-  float4 fbs[4][4];
+  float4 fbs[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 128 + 32 * j + 8 * q + 4 * h]);
+      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 64 + 32 * j + 8 * q + 4 * h]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float fa = fac[wm * 128 + 32 * i + r32];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 128
+        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 64
         const float4 fb = fbs[j][q];
         const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
         const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
@@ -281,7 +262,7 @@ __global__ void __launch_bounds__(256)
     for (int t = 0; t < 32 * kLanesPerRow / 64; ++t) {
       const int sr = t * (64 / kLanesPerRow) + lane / kLanesPerRow, sc = (lane % kLanesPerRow) * kPer;
       const int row = wm * 128 + 32 * i + sr;  // within the tile
-      const int col = tn * kTileN + wn * 128 + sc;
+      const int col = tn * kTileN + wn * 64 + sc;
       const uint8_t* src = slab + sr * kPitch + sc * kOut;
       if constexpr (kVec) {
         // n is a multiple of kPer: a chunk is wholly inside or wholly past the row
@@ -309,7 +290,7 @@ __global__ void __launch_bounds__(256)
 template <typename Out, bool kVec>
 hipError_t launch(const GemmLaunch& g) {
   const int tiles = ((g.m + kTileM - 1) / kTileM) * ((g.n + kTileN - 1) / kTileN);
-  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec>), dim3(tiles), dim3(256), 0,
+  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec>), dim3(tiles), dim3(512), 0,
                      static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
                      static_cast<Out*>(g.out));
   return hipGetLastError();
