@@ -156,6 +156,17 @@ __global__ void __launch_bounds__(512, 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = v16f{};
 
+  // This tile's row (threads 0..255) and column (256..511) clip scales,
+  // loaded now so that the epilogue does not wait for them.
+  const bool row_side = tid < kTileM;
+  float my_scale;
+  {
+    const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
+    const auto rsb = make_rsrc(sb + static_cast<size_t>(tn) * kTileN, min(n - tn * kTileN, kTileN) * 4);
+    my_scale = __builtin_bit_cast(float, row_side ? __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0)
+                                                  : __builtin_amdgcn_raw_buffer_load_b32(rsb, (tid - kTileM) * 4, 0, 0));
+  }
+
   const int stages = chunks;
   fetch(0, I0{});
   fetch(stages > 1 ? 1 : 0, I1{});
@@ -206,15 +217,7 @@ __global__ void __launch_bounds__(512, 1)
 
   // Epilogue.  Row and column factors Delta = s * 2 / (L - 1) go to LDS.
   float* fac = reinterpret_cast<float*>(lds);  // [0, 256): rows, [256, 512): columns
-  {
-    const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
-    const auto rsb = make_rsrc(sb + static_cast<size_t>(tn) * kTileN, min(n - tn * kTileN, kTileN) * 4);
-    const bool row_side = tid < kTileM;
-    const float v = __builtin_bit_cast(
-        float, row_side ? __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0)
-                        : __builtin_amdgcn_raw_buffer_load_b32(rsb, (tid - kTileM) * 4, 0, 0));
-    fac[tid] = v * (row_side ? ka : kb);
-  }
+  fac[tid] = my_scale * (row_side ? ka : kb);
   __syncthreads();
   // Each wave stages a 32 x 64 slab of its part in its own LDS region and
   // writes it as whole 64-column row segments.
