@@ -620,8 +620,10 @@ __global__ void __launch_bounds__(256)
       }
     }
     const int64_t run0 = t * 64;
-    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
-                           window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
+    // An operand call that asks for neither codes nor mask skips them.
+    if (!kIsOperand<Dq> || codes || mask)
+      mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
+                             window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
     if constexpr (kIsOperand<Dq>) {
       // After the transpose lane l holds run l of the tile.  The workgroup's
       // four tiles are 4 ROWS consecutive rows of one 32-row block.
@@ -738,6 +740,8 @@ __global__ void __launch_bounds__(1024)
   // belong to the next workgroup.
   const int64_t run0 = wg_first_run + 64 * wave;
   const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
+  // (Skipping this for operand calls without codes and mask, as the tiles
+  // kernel does, measured 5% slower here.)
   mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
                          window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
   if constexpr (kIsOperand<Dq>) {
