@@ -12,16 +12,23 @@ by its operand's trust mask and transformed back (pith.science review,
 "What carries the argument" and the Figure 2 caption).
 
 Quantisation, masking and both transforms run in libquest's kernels
-(quest_quantize_fwd_dq, quest_trust_bwd).  The two matrix products are plain
-library GEMMs through torch.
+(quest_quantize_fwd_dq, quest_trust_bwd).  The two training products are
+plain library GEMMs through torch.
+
+Inference (``QuestLinear.freeze``, then eval mode): the weight is quantised
+once into the FP6 matrix-core operand, each activation by
+quest_quantize_fwd_op, and the product is libquest's FP6 GEMM (quest_gemm):
+the 4-bit layer product whose speed the pages compare with BF16 (pith.science
+review, Figure 5 caption).
 """
 from __future__ import annotations
 
 import torch
 
-from . import quantize_fwd_ex, trust_bwd
+from . import gemm, quantize_fwd_ex, quantize_fwd_op, trust_bwd
 
-__all__ = ["QuestLinearFunction", "quest_linear", "QuestLinear", "default_trust", "ONE_BIT_OUTER_TRUST"]
+__all__ = ["QuestLinearFunction", "quest_linear", "quest_linear_operand", "QuestLinear", "default_trust",
+           "ONE_BIT_OUTER_TRUST"]
 
 
 ONE_BIT_OUTER_TRUST = 1.30  # pith.science review of QuEST, "Assumptions & free parameters" (s*)
@@ -79,6 +86,26 @@ def quest_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = N
     return y.reshape(*lead, w.shape[0])
 
 
+def quest_linear_operand(x: torch.Tensor, w_operand: torch.Tensor, w_scale: torch.Tensor, out_features: int,
+                         bits_w: int, bias: torch.Tensor | None = None, block: int = 128, bits_x: int = 4,
+                         out_dtype=torch.bfloat16) -> torch.Tensor:
+    """Inference product Q(x) Q(w)^T (+ bias) with w already in operand form.
+
+    x (..., K) bf16 or fp32 with K a multiple of 128; w_operand / w_scale as
+    returned by quantize_fwd_op for the (out_features x K) weight at bits_w.
+    The activation is quantised (b = bits_x <= 4) straight into its operand
+    and multiplied on the matrix cores; no gradient flows.
+    """
+    lead = x.shape[:-1]
+    k = x.shape[-1]
+    x2 = x.reshape(-1, k).contiguous()
+    _, x_scale, _, x_op = quantize_fwd_op(x2, block, bits_x)
+    y = gemm(x_op, x_scale, x2.shape[0], bits_x, w_operand, w_scale, out_features, bits_w, k, out_dtype=out_dtype)
+    if bias is not None:
+        y = y + bias.to(y.dtype)
+    return y.reshape(*lead, out_features)
+
+
 class QuestLinear(torch.nn.Module):
     """Drop-in linear layer trained with QuEST quantisation of weights and activations."""
 
@@ -94,7 +121,28 @@ class QuestLinear(torch.nn.Module):
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
         self.bias = torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=dtype)) if bias else None
         torch.nn.init.kaiming_uniform_(self.weight, a=5 ** 0.5)
+        self._w_operand = self._w_scale = None
+
+    def freeze(self) -> "QuestLinear":
+        """Quantise the weight once into the FP6 operand and switch to eval mode; eval-mode
+        forwards then run the matrix-core product.  Needs bits_x, bits_w <= 4 and
+        in_features a multiple of 128; training mode (``train()``) drops the operand."""
+        if max(self.bits_x, self.bits_w) > 4 or self.weight.shape[1] % 128:
+            raise ValueError("the FP6 product needs bits <= 4 and in_features a multiple of 128")
+        with torch.no_grad():
+            _, self._w_scale, _, self._w_operand = quantize_fwd_op(self.weight.detach().contiguous(), self.block,
+                                                                   self.bits_w)
+        return self.eval()
+
+    def train(self, mode: bool = True) -> "QuestLinear":
+        if mode:
+            self._w_operand = self._w_scale = None
+        return super().train(mode)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if not self.training and self._w_operand is not None:
+            out_dtype = torch.float32 if self.compute_dtype == torch.float32 else torch.bfloat16
+            return quest_linear_operand(x, self._w_operand, self._w_scale, self.weight.shape[0], self.bits_w,
+                                        self.bias, self.block, self.bits_x, out_dtype)
         return quest_linear(x, self.weight, self.bias, self.block, self.bits_x, self.bits_w, self.compute_dtype,
                             self.trust_x, self.trust_w)

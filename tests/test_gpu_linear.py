@@ -145,3 +145,39 @@ def test_linear_module_autograd_3d_input(dev):
     close(x.grad.reshape(128, 1024), dx_ref, "module dx", tols, skip_dx, 128)
     close(layer.weight.grad, dw_ref, "module dw", tols, skip_dw, 128)
     assert np.allclose(layer.bias.grad.float().cpu().numpy(), dy.sum(axis=0), rtol=2e-2, atol=1e-6)
+
+
+@pytest.mark.parametrize("compute_dtype", [torch.float32, torch.bfloat16])
+def test_linear_module_frozen_fp6_product(dev, compute_dtype):
+    """freeze(): the eval-mode forward runs the FP6 operand path (quest_quantize_fwd_op + quest_gemm) and
+    gives the oracle's Q(x) Q(w)^T + bias: the sum is exact, so fp32 output is within 1e-6 relative of
+    the oracle, bf16 within one rounding (the tolerance of the product tests); training mode drops the
+    operand again."""
+    torch.manual_seed(1)
+    layer = QuestLinear(2048, 384, bias=True, block=128, compute_dtype=compute_dtype, device=dev,
+                        dtype=torch.bfloat16)
+    with torch.no_grad():
+        layer.bias.copy_(torch.linspace(-1, 1, 384, device=dev).to(torch.bfloat16))
+    x = make_tensor(TensorSpec("frz.x", 3 * 40, 2048, "bf16", "student_t", 4, 9500, outlier_cols=20,
+                               outlier_scale=20.0), dev).reshape(3, 40, 2048)
+    log(f"frozen layer, input 3x40x2048, compute {compute_dtype}")
+    layer.freeze()
+    assert not layer.training and layer._w_operand is not None
+    with torch.no_grad():
+        y = layer(x)
+    torch.cuda.synchronize()
+    assert y.shape == (3, 40, 384)
+    f = qo.qat_linear_fwd(to_float64(x.reshape(120, 2048)), to_float64(layer.weight.detach()), 128, 4, 4)
+    bias64 = to_float64(layer.bias.detach())[None, :]
+    skip_y, _, _ = band_reach(f, 4, 4, 128)
+    got = y.reshape(120, 384).float().cpu().numpy().astype(np.float64)
+    if compute_dtype == torch.float32:
+        # fp32 output: the product exact up to the scale roundings (1e-6 of it), then one fp32
+        # rounding of the sum with the bias (2^-24 of |product| + |bias|)
+        scale = np.abs(f["y"]) + np.abs(bias64)
+        err = np.abs(got - (f["y"] + bias64)) / scale
+        assert (err[~skip_y] <= 2e-6).all(), f"max error / (|product| + |bias|) {err[~skip_y].max()}"
+    else:
+        close(y.reshape(120, 384), f["y"] + bias64, "frozen y", (1e-2, 5e-3), skip_y)
+    layer.train()
+    assert layer._w_operand is None
