@@ -92,12 +92,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x3F70 | N);
 }
 
-template <typename Out, bool kVec>
-__global__ void __launch_bounds__(512, 1)
-    quest_gemm_e2m3_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
-                           const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k, float ka,
-                           float kb, Out* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+// One output tile: rows 256 tm .. + 255, columns col0 .. col0 + 128 WNB - 1
+// (WNB B blocks of 32 per wave: 2 for a full 256-column tile, 1 for a half
+// tile).  8 waves: 2 x 4, each 128 rows x 32 WNB columns.
+template <typename Out, bool kVec, int WNB>
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
+                                          const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k,
+                                          float ka, float kb, Out* __restrict__ out, int tm, int col0, uint8_t* lds) {
+  constexpr int kTileW = 128 * WNB;  // columns of the tile
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -105,28 +107,24 @@ __global__ void __launch_bounds__(512, 1)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 8 waves: 2 x 4, each 128 rows x 64 columns
-  const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
-  // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
-  // contiguous range of tiles, walked in groups of 8 tile rows, so that the
-  // tiles sharing operand blocks share an L2.
-  const int grid = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  const int full = grid & ~7;
-  if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
-  const int group = 8 * tiles_n;
-  const int first_m = (pid / group) * 8;
-  const int gm = min(tiles_m - first_m, 8);
-  const int tm = first_m + (pid % group) % gm, tn = (pid % group) / gm;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int cb0 = col0 >> 5;  // first B block of the tile
 
   const int chunks = k >> 7;
   const uint32_t rb_bytes = static_cast<uint32_t>(chunks) * kBlock;  // one 32-row block, all of k
   const int rb_a = (m + 31) >> 5, rb_b = (n + 31) >> 5;
   const i32x4 ra = raw_rsrc(a + static_cast<size_t>(tm) * 8 * rb_bytes, min(rb_a - tm * 8, 8) * rb_bytes);
-  const i32x4 rb = raw_rsrc(b + static_cast<size_t>(tn) * 8 * rb_bytes, min(rb_b - tn * 8, 8) * rb_bytes);
+  // (a half tile can lie wholly past n: then its windows are empty and every
+  // load reads zeros)
+  const int b_blocks = __builtin_amdgcn_readfirstlane(max(min(rb_b - cb0, 4 * WNB), 0));
+  const i32x4 rb = raw_rsrc(b + static_cast<size_t>(cb0) * rb_bytes, b_blocks * rb_bytes);
 
-  // Stage st into LDS: each operand's 8 blocks are 24 KB = 24 wave
-  // instructions; wave w issues t = w + 8 u, u < 3, for both operands.
+  // Stage st into LDS: A's 8 blocks are 24 KB = 24 wave instructions, wave w
+  // issuing t = w + 8 u, u < 3.  B's 4 WNB blocks are 12 WNB instructions:
+  // for a full tile spread the same way; for a half tile (12) wave w issues
+  // t = (w + 8 u) % 12, u < 2, so waves 4..7 repeat four of them (the same
+  // bytes to the same place) and every wave issues the same number of loads.
+  constexpr int kLoads = WNB == 2 ? 6 : 5;  // loads one wave issues per stage
   auto fetch = [&](int st, auto bi) {
     const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage_mem(bi)));
     const i32x4 qa = ra, qb = rb;
@@ -136,9 +134,18 @@ __global__ void __launch_bounds__(512, 1)
       const int goff = blk * static_cast<int>(rb_bytes) + st * kBlock + part * 1024 + lane * 16;
       const uint32_t la = base + blk * kBlock + part * 1024;
       dma16(__builtin_amdgcn_readfirstlane(la), goff, qa);
-      dma16(__builtin_amdgcn_readfirstlane(la + kOpStage), goff, qb);
+      if constexpr (WNB == 2) {
+        dma16(__builtin_amdgcn_readfirstlane(la + kOpStage), goff, qb);
+      } else if (u < 2) {
+        const int tb = t % 12, bblk = tb / 3, bpart = tb % 3;
+        const int bgoff = bblk * static_cast<int>(rb_bytes) + st * kBlock + bpart * 1024 + lane * 16;
+        dma16(__builtin_amdgcn_readfirstlane(base + kOpStage + bblk * kBlock + bpart * 1024), bgoff, qb);
+      }
     }
   };
+  // Wait until at most one stage's loads of this wave are in flight.
+  auto wait_one_stage = [&]() { wait_vmcnt<kLoads>(); };
+
   // Fragment (block rbk, k-half ks) of operand op: this lane's 24 bytes.
   auto frag = [&](auto bi, int op, int rbk, int ks) -> v8i {
     const u32x2* s = reinterpret_cast<const u32x2*>(stage_mem(bi) + op * kOpStage + rbk * kBlock + ks * kFrag + lane * 24);
@@ -150,9 +157,9 @@ __global__ void __launch_bounds__(512, 1)
   // acc[j][i]: 32 x 32 tile of the product B A^T for B block j and A block i,
   // so lane l holds output row 32 i + l % 32 and four consecutive columns per
   // register quad.
-  v16f acc[2][4];
+  v16f acc[WNB][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < WNB; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = v16f{};
 
@@ -162,7 +169,7 @@ __global__ void __launch_bounds__(512, 1)
   float my_scale;
   {
     const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
-    const auto rsb = make_rsrc(sb + static_cast<size_t>(tn) * kTileN, min(n - tn * kTileN, kTileN) * 4);
+    const auto rsb = make_rsrc(sb + col0, max(min(n - col0, kTileW), 0) * 4);
     my_scale = __builtin_bit_cast(float, row_side ? __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0)
                                                   : __builtin_amdgcn_raw_buffer_load_b32(rsb, (tid - kTileM) * 4, 0, 0));
   }
@@ -170,13 +177,13 @@ __global__ void __launch_bounds__(512, 1)
   const int stages = chunks;
   fetch(0, I0{});
   fetch(stages > 1 ? 1 : 0, I1{});
-  wait_vmcnt<6>();  // stage 0 has landed (stage 1 may be in flight)
+  wait_one_stage();  // stage 0 has landed (stage 1 may be in flight)
   __syncthreads();
-  v8i f0a[4], f0b[2], f1a[4], f1b[2];
+  v8i f0a[4], f0b[WNB], f1a[4], f1b[WNB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) f0b[j] = frag(I0{}, 1, wn * 2 + j, 0);
+  for (int j = 0; j < WNB; ++j) f0b[j] = frag(I0{}, 1, wn * WNB + j, 0);
   // One stage: bi holds stage s, bn stage s + 1, b2 receives stage s + 2.
   // b2 last held stage s - 1, whose reads every wave finished before the
   // previous barrier.
@@ -184,22 +191,22 @@ __global__ void __launch_bounds__(512, 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) f1a[i] = frag(bi, 0, wm * 4 + i, 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f1b[j] = frag(bi, 1, wn * 2 + j, 1);
+    for (int j = 0; j < WNB; ++j) f1b[j] = frag(bi, 1, wn * WNB + j, 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WNB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0b[j], f0a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
     fetch(s + 2 < stages ? s + 2 : stages - 1, b2);
-    wait_vmcnt<6>();                    // stage s + 1 has landed
+    wait_one_stage();                   // stage s + 1 has landed
     __builtin_amdgcn_s_waitcnt(0xC07F);  // and this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i) f0a[i] = frag(bn, 0, wm * 4 + i, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f0b[j] = frag(bn, 1, wn * 2 + j, 0);
+    for (int j = 0; j < WNB; ++j) f0b[j] = frag(bn, 1, wn * WNB + j, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WNB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1b[j], f1a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
@@ -217,35 +224,35 @@ __global__ void __launch_bounds__(512, 1)
 
   // Epilogue.  Row and column factors Delta = s * 2 / (L - 1) go to LDS.
   float* fac = reinterpret_cast<float*>(lds);  // [0, 256): rows, [256, 512): columns
-  fac[tid] = my_scale * (row_side ? ka : kb);
+  if (tid < kTileM + kTileW) fac[tid] = my_scale * (row_side ? ka : kb);
   __syncthreads();
-  // Each wave stages a 32 x 64 slab of its part in its own LDS region and
-  // writes it as whole 64-column row segments.
+  // Each wave stages a 32 x 32 WNB slab of its part in its own LDS region and
+  // writes it as whole row segments.
   constexpr int kOut = static_cast<int>(sizeof(Out));
-  constexpr int kPitch = 64 * kOut + 16;       // slab row pitch in bytes
+  constexpr int kPitch = 32 * WNB * kOut + 16;  // slab row pitch in bytes
   constexpr int kPer = 16 / kOut;              // outputs per 16-byte chunk
-  constexpr int kLanesPerRow = 64 / kPer;
+  constexpr int kLanesPerRow = 32 * WNB / kPer;
   static_assert(8 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
   uint8_t* slab = lds + kStage + wave * 32 * kPitch;  // the factors stay in the first
   const int rows_left = m - tm * kTileM;
   const auto rout = make_rsrc(out + static_cast<size_t>(tm) * kTileM * n,
                               static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
   const int r32 = lane & 31, h = lane >> 5;
-  // column factors of the lane's 64 columns: 32 j + 8 q + 4 h + (0..3)
-  float4 fbs[2][4];
+  // column factors of the lane's columns: 32 j + 8 q + 4 h + (0..3) of the wave's 32 WNB
+  float4 fbs[WNB][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < WNB; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 64 + 32 * j + 8 * q + 4 * h]);
+      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 32 * WNB + 32 * j + 8 * q + 4 * h]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float fa = fac[wm * 128 + 32 * i + r32];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WNB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 64
+        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 32 WNB
         const float4 fb = fbs[j][q];
         const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
         const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
@@ -265,7 +272,7 @@ __global__ void __launch_bounds__(512, 1)
     for (int t = 0; t < 32 * kLanesPerRow / 64; ++t) {
       const int sr = t * (64 / kLanesPerRow) + lane / kLanesPerRow, sc = (lane % kLanesPerRow) * kPer;
       const int row = wm * 128 + 32 * i + sr;  // within the tile
-      const int col = tn * kTileN + wn * 64 + sc;
+      const int col = col0 + wn * 32 * WNB + sc;
       const uint8_t* src = slab + sr * kPitch + sc * kOut;
       if constexpr (kVec) {
         // n is a multiple of kPer: a chunk is wholly inside or wholly past the row
@@ -290,12 +297,74 @@ __global__ void __launch_bounds__(512, 1)
   }
 }
 
+// Tile index -> (tm, tn): groups of 8 tile rows, walked column by column.
+__device__ __forceinline__ void tile_at(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group = 8 * tiles_n;
+  const int first_m = (pid / group) * 8;
+  const int gm = min(tiles_m - first_m, 8);
+  tm = first_m + (pid % group) % gm;
+  tn = (pid % group) / gm;
+}
+
+// Full tiles (WNB = 2): workgroup w computes tile w of the first
+// `tile_count` tiles, after the XCD remap below.  Half tiles (WNB = 1):
+// workgroup w computes half w % 2 of tile first_tile + w / 2, for the tiles
+// of a last round that would hold at most half the compute units.
+template <typename Out, bool kVec, int WNB>
+__global__ void __launch_bounds__(512, 1)
+    quest_gemm_e2m3_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
+                           const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k, float ka,
+                           float kb, Out* __restrict__ out, int tile_count, int first_tile) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+  const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
+  int tm, tn;
+  if constexpr (WNB == 2) {
+    // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
+    // contiguous range of tiles, so that the tiles sharing operand blocks
+    // share an L2.
+    int pid = blockIdx.x;
+    const int full = tile_count & ~7;
+    if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
+    tile_at(pid, tiles_m, tiles_n, tm, tn);
+    gemm_tile<Out, kVec, 2>(a, sa, m, b, sb, n, k, ka, kb, out, tm, tn * kTileN, lds);
+  } else {
+    const int h = blockIdx.x;
+    tile_at(first_tile + (h >> 1), tiles_m, tiles_n, tm, tn);
+    gemm_tile<Out, kVec, 1>(a, sa, m, b, sb, n, k, ka, kb, out, tm, tn * kTileN + (h & 1) * (kTileN / 2), lds);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <typename Out, bool kVec>
 hipError_t launch(const GemmLaunch& g) {
   const int tiles = ((g.m + kTileM - 1) / kTileM) * ((g.n + kTileN - 1) / kTileN);
-  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec>), dim3(tiles), dim3(512), 0,
+  // One workgroup per compute unit at a time (LDS): if the last round would
+  // hold at most half the compute units, its tiles are split in halves.
+  const int cus = device_cus();
+  const int last = tiles % cus;
+  const int full_tiles = tiles > cus && last > 0 && 2 * last <= cus ? tiles - last : tiles;
+  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec, 2>), dim3(full_tiles), dim3(512), 0,
                      static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
-                     static_cast<Out*>(g.out));
+                     static_cast<Out*>(g.out), full_tiles, 0);
+  if (full_tiles < tiles) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec, 1>), dim3(2 * (tiles - full_tiles)), dim3(512), 0,
+                       static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
+                       static_cast<Out*>(g.out), tiles - full_tiles, full_tiles);
+  }
   return hipGetLastError();
 }
 

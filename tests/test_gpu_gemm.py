@@ -168,6 +168,7 @@ GEMM_CASES = [
     (97, 45, 640, 3, 4),  # odd n: element stores in both types; 5 stages
     (1024, 512, 2048, 4, 4),  # 8 tiles, 16 stages
     (40, 700, 1152, 1, 2),  # 9 stages
+    (33280, 300, 128, 4, 4),  # 260 tiles: the last round's 4 tiles run as 8 half tiles, 2 of them past n
 ]
 
 
