@@ -31,6 +31,7 @@
 // stage.  With two waves per SIMD one wave's fragment reads and waits overlap
 // the other's MFMAs.  The epilogue scales by Delta_a Delta_b and writes whole
 // row segments through LDS.
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -334,17 +335,18 @@ __global__ void __launch_bounds__(512, 1)
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent first
+// calls on one device may both query it and store the same value).
 int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 template <typename Out, bool kVec>
