@@ -681,7 +681,7 @@ __global__ void __launch_bounds__(256)
 // block of rows (no grid-stride loop): with a barrier per block, letting the
 // hardware refill compute units as workgroups finish hides latency better
 // than a resident loop.
-template <int LOGN, int B, typename Dq>
+template <int LOGN, int B, typename Dq, bool kQuant = true>
 __global__ void __launch_bounds__(1024)
     quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
                                FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
@@ -742,10 +742,9 @@ __global__ void __launch_bounds__(1024)
   // belong to the next workgroup.
   const int64_t run0 = wg_first_run + 64 * wave;
   const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
-  // (Skipping this for operand calls without codes and mask, as the tiles
-  // kernel does, measured 5% slower here.)
-  mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
-                         window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
+  if (kQuant)
+    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
+                           window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
   if constexpr (kIsOperand<Dq>) {
     // After the transpose lane l holds run 64 w + l of the workgroup.
     const int64_t row0 = wg * rows_per_wg;
@@ -965,8 +964,18 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
       if (rows_per_wg < 1) rows_per_wg = 1;
       const int threads = ((rows_per_wg * runs_per_row + 63) / 64) * 64;
       const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-      hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads),
-                         0, stream, x, rows, runs_per_row, rows_per_wg, k, a.codes, a.scale, mask32, dq);
+      // An operand call that asks for neither codes nor mask runs the build without them.
+      auto run = [&](auto quant) {
+        hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B, Dq, decltype(quant)::value>),
+                           dim3(static_cast<uint32_t>(grid)), dim3(threads), 0, stream, x, rows, runs_per_row,
+                           rows_per_wg, k, a.codes, a.scale, mask32, dq);
+      };
+      bool quant = true;
+      if constexpr (kIsOperand<Dq>) quant = a.codes || a.mask;
+      if (quant)
+        run(std::true_type{});
+      else if constexpr (kIsOperand<Dq>)
+        run(std::false_type{});
       return hipGetLastError();
     }
     if (a.allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
