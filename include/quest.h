@@ -260,7 +260,9 @@ quest_status quest_quantize_fwd_op(const void* x, quest_dtype x_dtype, int64_t r
  * times (Delta_a Delta_b, the product, and the output type).
  *   a, a_scale  device, quest_operand_bytes(m, k) bytes and m floats (s_r)
  *   b, b_scale  device, quest_operand_bytes(n, k) bytes and n floats
- *   m, n        >= 0 (0: nothing is done); m <= 2^30, n <= 2^20
+ *   m, n        >= 0 (0: nothing is done); m <= 2^30, n <= 2^20, and at
+ *               most 2^23 - 1 output tiles of 256 x 256, ceil(m / 256) *
+ *               ceil(n / 256) (QUEST_EUNSUPPORTED)
  *   a_bits, b_bits  1 .. 4: the bit widths the operands were quantised to
  *   k           the common number of columns: a positive multiple of 128,
  *               at most 65536 (QUEST_EUNSUPPORTED; above that the fp32 sum

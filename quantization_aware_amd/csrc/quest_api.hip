@@ -176,6 +176,7 @@ quest_status quantize_grid_common(const void* x, quest_dtype x_dtype, int64_t ro
 constexpr int64_t kGemmMaxK = 65536;
 constexpr int64_t kGemmMaxN = int64_t(1) << 20;
 constexpr int64_t kGemmMaxM = int64_t(1) << 30;
+constexpr int64_t kGemmMaxTiles = (int64_t(1) << 23) - 1;  // 256 x 256 output tiles
 
 }  // namespace
 
@@ -250,7 +251,8 @@ quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a
   if (!dtype_ok(out_dtype) || m < 0 || n < 0 || k <= 0) return QUEST_EINVAL;
   if (k % 128 != 0 || k > kGemmMaxK || n > kGemmMaxN || m > kGemmMaxM) return QUEST_EUNSUPPORTED;
   const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (tiles > INT32_MAX) return QUEST_EUNSUPPORTED;
+  // 512 work-items per tile: the launch's work-item count must fit 32 bits.
+  if (tiles > kGemmMaxTiles) return QUEST_EUNSUPPORTED;
   if (m == 0 || n == 0) return QUEST_OK;
   if (!a || !a_scale || !b || !b_scale || !out) return QUEST_EINVAL;
   if (!aligned16(a) || !aligned16(a_scale) || !aligned16(b) || !aligned16(b_scale) || !aligned16(out))

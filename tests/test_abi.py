@@ -348,6 +348,8 @@ def test_fwd_op_rejects(lib, kw, status):
         (dict(k=65536 + 128), qa.QUEST_EUNSUPPORTED),
         (dict(n=2 ** 20 + 1), qa.QUEST_EUNSUPPORTED),
         (dict(m=2 ** 30 + 1), qa.QUEST_EUNSUPPORTED),
+        (dict(m=2 ** 23, n=2 ** 16 + 1), qa.QUEST_EUNSUPPORTED),  # 2^23 tiles: 2^32 work-items
+        (dict(m=2 ** 30, n=512), qa.QUEST_EUNSUPPORTED),
         (dict(k=0), qa.QUEST_EINVAL),
         (dict(k=-128), qa.QUEST_EINVAL),
         (dict(m=-1), qa.QUEST_EINVAL),
