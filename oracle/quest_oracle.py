@@ -462,16 +462,29 @@ def trust_bwd(grad: np.ndarray, mask: np.ndarray, block: int) -> np.ndarray:
 # Hadamard-domain gradient with the trust mask and transforms it back).
 # ---------------------------------------------------------------------------
 def qat_linear_fwd(x: np.ndarray, w: np.ndarray, block: int, bits_x: int, bits_w: int, trust_x: float = 1.0,
-                   trust_w: float = 1.0) -> dict:
+                   trust_w: float = 1.0, grid: str = "int") -> dict:
     """y = Q(x) Q(w)^T with both operands quantised along their last axis.
 
     x is N x K (activations), w is M x K (weights); the Hadamard blocks run
     along K, the contraction axis.  Q(.) is the dequantised grid value in the
     Hadamard domain, so y = (x~ H)(w~ H)^T = x~ w~^T, where x~ and w~ are the
-    original-domain reconstructions.
+    original-domain reconstructions.  grid: "int" (b-bit midrise levels),
+    "fp4" (E2M1 levels; the bit widths are unused) or "sparse24" (2:4-sparse
+    b-bit levels): the formats the pages train with, each through its own
+    quantiser above.
     """
-    fx = quantize_fwd(np.asarray(x, dtype=np.float64), block, bits_x, trust=trust_x)
-    fw = quantize_fwd(np.asarray(w, dtype=np.float64), block, bits_w, trust=trust_w)
+    def quantise(t, bits, trust):
+        t = np.asarray(t, dtype=np.float64)
+        if grid == "int":
+            return quantize_fwd(t, block, bits, trust=trust)
+        if grid == "fp4":
+            return quantize_fwd_fp4(t, block, trust=trust)
+        if grid == "sparse24":
+            return quantize_fwd_sparse24(t, block, bits, trust=trust)
+        raise ValueError(f"unknown grid {grid!r}")
+
+    fx = quantise(x, bits_x, trust_x)
+    fw = quantise(w, bits_w, trust_w)
     qx = fx["q"]
     qw = fw["q"]
     return {"y": qx @ qw.T, "qx": qx, "qw": qw, "mask_x": fx["mask"], "mask_w": fw["mask"], "fx": fx, "fw": fw}

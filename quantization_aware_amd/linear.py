@@ -12,8 +12,14 @@ by its operand's trust mask and transformed back (pith.science review,
 "What carries the argument" and the Figure 2 caption).
 
 Quantisation, masking and both transforms run in libquest's kernels
-(quest_quantize_fwd_dq, quest_trust_bwd).  The two training products are
-plain library GEMMs through torch.
+(quest_quantize_fwd_ex, or the FP4 and 2:4-sparse forwards, and
+quest_trust_bwd).  The two training products are plain library GEMMs through
+torch.  ``grid`` picks the format the operands are quantised to: "int"
+(b-bit midrise levels), "fp4" (E2M1 levels, 4 bits whatever bits_x and
+bits_w say) or "sparse24" (2:4-sparse b-bit levels), the formats the pages
+train with (pith.science review of QuEST, the list of contributions and the
+captions of Figures 3 and 4); all three share the transform, the RMS scale
+and the trust rule.
 
 Inference (``QuestLinear.freeze``, then eval mode): the weight is quantised
 once into the FP6 matrix-core operand, each activation by
@@ -25,13 +31,30 @@ from __future__ import annotations
 
 import torch
 
-from . import gemm, quantize_fwd_ex, quantize_fwd_op, trust_bwd
+from . import gemm, quantize_fwd_ex, quantize_fwd_fp4, quantize_fwd_op, quantize_fwd_sparse24, trust_bwd
 
 __all__ = ["QuestLinearFunction", "quest_linear", "quest_linear_operand", "QuestLinear", "default_trust",
-           "ONE_BIT_OUTER_TRUST"]
+           "ONE_BIT_OUTER_TRUST", "GRIDS"]
 
 
 ONE_BIT_OUTER_TRUST = 1.30  # pith.science review of QuEST, "Assumptions & free parameters" (s*)
+GRIDS = ("int", "fp4", "sparse24")
+
+
+def _check_grid(grid: str) -> None:
+    if grid not in GRIDS:
+        raise ValueError(f"grid must be one of {GRIDS}, not {grid!r}")
+
+
+def _quantise(t: torch.Tensor, block: int, bits: int, trust: float, grid: str, dtype):
+    """(trust mask, dequantised Hadamard-domain values in dtype) of t on the chosen grid."""
+    if grid == "int":
+        _, _, mask, q = quantize_fwd_ex(t, block, bits, trust=trust, with_codes=False, dq_dtype=dtype)
+    elif grid == "fp4":
+        _, _, mask, q = quantize_fwd_fp4(t, block, trust, with_codes=False, dq_dtype=dtype)
+    else:
+        _, _, _, mask, q = quantize_fwd_sparse24(t, block, bits, trust, with_codes=False, dq_dtype=dtype)
+    return mask, q
 
 
 def default_trust(bits: int) -> float:
@@ -43,9 +66,9 @@ class QuestLinearFunction(torch.autograd.Function):
     """y = Q(x) Q(w)^T for 2-D x (N x K) and w (M x K), K a multiple of `block`."""
 
     @staticmethod
-    def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype, trust_x=1.0, trust_w=1.0):
-        _, _, mask_x, qx = quantize_fwd_ex(x, block, bits_x, trust=trust_x, with_codes=False, dq_dtype=compute_dtype)
-        _, _, mask_w, qw = quantize_fwd_ex(w, block, bits_w, trust=trust_w, with_codes=False, dq_dtype=compute_dtype)
+    def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype, trust_x=1.0, trust_w=1.0, grid="int"):
+        mask_x, qx = _quantise(x, block, bits_x, trust_x, grid, compute_dtype)
+        mask_w, qw = _quantise(w, block, bits_w, trust_w, grid, compute_dtype)
         y = torch.nn.functional.linear(qx, qw)
         ctx.save_for_backward(qx, qw, mask_x, mask_w)
         ctx.block = block
@@ -65,22 +88,24 @@ class QuestLinearFunction(torch.autograd.Function):
             # products with a transposed operand view are avoided)
             g = torch.mm(dy.t().contiguous(), qx)
             dw = trust_bwd(g, mask_w, ctx.block, out=g).to(ctx.w_dtype)
-        return dx, dw, None, None, None, None, None, None
+        return dx, dw, None, None, None, None, None, None, None
 
 
 def quest_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None, block: int = 128,
                  bits_x: int = 4, bits_w: int = 4, compute_dtype=torch.bfloat16, trust_x: float | None = None,
-                 trust_w: float | None = None) -> torch.Tensor:
+                 trust_w: float | None = None, grid: str = "int") -> torch.Tensor:
     """QuEST linear map of x (..., K) by w (M, K); leading axes of x are flattened.
 
     trust_x / trust_w: outer trust factors; by default 1.30 for 1-bit operands
-    (the factor the pages tune for their 1-bit runs) and 1 otherwise.
+    of the "int" grid (the factor the pages tune for their 1-bit runs) and 1
+    otherwise.  grid: "int", "fp4" or "sparse24".
     """
-    trust_x = default_trust(bits_x) if trust_x is None else trust_x
-    trust_w = default_trust(bits_w) if trust_w is None else trust_w
+    _check_grid(grid)
+    trust_x = (default_trust(bits_x) if grid == "int" else 1.0) if trust_x is None else trust_x
+    trust_w = (default_trust(bits_w) if grid == "int" else 1.0) if trust_w is None else trust_w
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1]).contiguous()
-    y = QuestLinearFunction.apply(x2, w.contiguous(), block, bits_x, bits_w, compute_dtype, trust_x, trust_w)
+    y = QuestLinearFunction.apply(x2, w.contiguous(), block, bits_x, bits_w, compute_dtype, trust_x, trust_w, grid)
     if bias is not None:
         y = y + bias.to(y.dtype)
     return y.reshape(*lead, w.shape[0])
@@ -111,13 +136,15 @@ class QuestLinear(torch.nn.Module):
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True, block: int = 128, bits_x: int = 4,
                  bits_w: int = 4, compute_dtype=torch.bfloat16, trust_x: float | None = None,
-                 trust_w: float | None = None, device=None, dtype=None):
+                 trust_w: float | None = None, grid: str = "int", device=None, dtype=None):
         super().__init__()
         if in_features % block:
             raise ValueError(f"in_features ({in_features}) must be a multiple of the Hadamard block ({block})")
+        _check_grid(grid)
         self.block, self.bits_x, self.bits_w, self.compute_dtype = block, bits_x, bits_w, compute_dtype
-        self.trust_x = default_trust(bits_x) if trust_x is None else trust_x
-        self.trust_w = default_trust(bits_w) if trust_w is None else trust_w
+        self.grid = grid
+        self.trust_x = (default_trust(bits_x) if grid == "int" else 1.0) if trust_x is None else trust_x
+        self.trust_w = (default_trust(bits_w) if grid == "int" else 1.0) if trust_w is None else trust_w
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
         self.bias = torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=dtype)) if bias else None
         torch.nn.init.kaiming_uniform_(self.weight, a=5 ** 0.5)
@@ -126,9 +153,9 @@ class QuestLinear(torch.nn.Module):
     def freeze(self) -> "QuestLinear":
         """Quantise the weight once into the FP6 operand and switch to eval mode; eval-mode
         forwards then run the matrix-core product.  Needs bits_x, bits_w <= 4 and
-        in_features a multiple of 128; training mode (``train()``) drops the operand."""
-        if max(self.bits_x, self.bits_w) > 4 or self.weight.shape[1] % 128:
-            raise ValueError("the FP6 product needs bits <= 4 and in_features a multiple of 128")
+        in_features a multiple of 128, on the "int" grid; training mode (``train()``) drops the operand."""
+        if self.grid != "int" or max(self.bits_x, self.bits_w) > 4 or self.weight.shape[1] % 128:
+            raise ValueError("the FP6 product needs the int grid, bits <= 4 and in_features a multiple of 128")
         with torch.no_grad():
             _, self._w_scale, _, self._w_operand = quantize_fwd_op(self.weight.detach().contiguous(), self.block,
                                                                    self.bits_w)
@@ -145,4 +172,4 @@ class QuestLinear(torch.nn.Module):
             return quest_linear_operand(x, self._w_operand, self._w_scale, self.weight.shape[0], self.bits_w,
                                         self.bias, self.block, self.bits_x, out_dtype)
         return quest_linear(x, self.weight, self.bias, self.block, self.bits_x, self.bits_w, self.compute_dtype,
-                            self.trust_x, self.trust_w)
+                            self.trust_x, self.trust_w, self.grid)

@@ -189,6 +189,21 @@ def sparse24_tie_groups(y: np.ndarray, s: np.ndarray, band: float = BAND) -> np.
     return tie
 
 
+def sparse24_exempt_entries(ref: dict, b: int, trust: float = 1.0) -> np.ndarray:
+    """Entries of a 2:4 forward (oracle result `ref`) whose value or mask bit may
+    correctly differ: every entry of a group whose kept pair is a near tie, kept
+    entries near a decision or trust threshold of the dense rule (with the kept
+    RMS), and pruned entries near Delta / 2 (R x C)."""
+    y, s = ref["y"], np.asarray(ref["scale"])
+    rows, cols = y.shape
+    ex = np.repeat(sparse24_tie_groups(y, s), 4, axis=1)
+    kept_y = y[ref["keep"]].reshape(rows, cols // 2)
+    ex[ref["keep"]] |= exempt_entries(kept_y, s, b, trust=trust).reshape(-1)
+    half = s[:, None] / ((1 << b) - 1)
+    ex |= ~ref["keep"] & (np.abs(np.abs(y) - half) <= BAND * s[:, None])
+    return ex
+
+
 def check_fwd_sparse24(x64: np.ndarray, block: int, b: int, codes, index, scale, mask, trust: float = 1.0,
                        max_fraction: float | None = MAX_MISMATCH_FRACTION, ref=None) -> dict:
     """Kept positions, their codes and the mask against the oracle.
@@ -210,15 +225,9 @@ def check_fwd_sparse24(x64: np.ndarray, block: int, b: int, codes, index, scale,
     ref_pos = qo.unpack_lsb_first(ref["index"], 2, cols // 2)
     tie = sparse24_tie_groups(y, s)
     tie_slot = np.repeat(tie, 2, axis=1)
-    tie_entry = np.repeat(tie, 4, axis=1)
     kept_y = y[ref["keep"]].reshape(rows, cols // 2)
     ex_slot = tie_slot | exempt_entries(kept_y, s, b, trust=trust)
-    big_l = 1 << b
-    half = np.asarray(s)[:, None] / (big_l - 1)
-    ex_entry = tie_entry.copy()
-    ex_entry[ref["keep"]] |= exempt_entries(kept_y, s, b, trust=trust).reshape(-1)
-    near_zero = np.abs(np.abs(y) - half) <= BAND * np.asarray(s)[:, None]
-    ex_entry |= ~ref["keep"] & near_zero
+    ex_entry = sparse24_exempt_entries(ref, b, trust=trust)
     bad_slot = (u != ref["u"]) | (pos != ref_pos)
     bad_entry = m != ref["m"]
     hard_slot = bad_slot & ~ex_slot

@@ -28,7 +28,7 @@ import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
 from quantization_aware_amd.linear import QuestLinear, default_trust, quest_linear
 from quest_inputs import TensorSpec, make_tensor, to_float64
-from parity import exempt_entries
+from parity import exempt_entries, exempt_fp4, sparse24_exempt_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,11 @@ def band_reach(f: dict, bx: int, bw: int, block: int, trust_x: float = 1.0, trus
     """
     bx_ = exempt_entries(f["fx"]["y"], f["fx"]["scale"], bx, trust=trust_x)
     bw_ = exempt_entries(f["fw"]["y"], f["fw"]["scale"], bw, trust=trust_w)
+    return reach_of(bx_, bw_, block)
+
+
+def reach_of(bx_: np.ndarray, bw_: np.ndarray, block: int):
+    """(skip_y, skip_dx, skip_dw) reached from the exempt entries bx_ of x and bw_ of w."""
     rx, rw = bx_.any(axis=1), bw_.any(axis=1)
     k = bx_.shape[1]
     blk_x = np.repeat(bx_.reshape(bx_.shape[0], k // block, block).any(axis=(0, 2)), block)
@@ -121,6 +126,45 @@ def test_linear_matches_oracle(dev, n, k, m, block, bx, bw, compute_dtype):
     close(y.detach(), f["y"], "y", tols, skip_y)
     close(xg.grad, dx_ref, "dx", tols, skip_dx, block)
     close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
+
+
+@pytest.mark.parametrize("compute_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("grid,bx,bw", [("fp4", 4, 4), ("sparse24", 4, 4), ("sparse24", 2, 3)])
+def test_linear_grids_match_oracle(dev, grid, bx, bw, compute_dtype):
+    """The layer on the FP4 and 2:4-sparse grids against the oracle's composition of the same
+    quantiser, a float64 product and the trust backward; exemptions as in the grid parity tests."""
+    n, k, m, block = 192, 1024, 256, 128
+    log(f"linear on the {grid} grid, {n}x{k} by {m}x{k}, bits x{bx} w{bw}, compute {compute_dtype}")
+    tols = TOLS[compute_dtype]
+    x = make_tensor(TensorSpec("lin.gx", n, k, "bf16", "student_t", 4, 9600 + bx, outlier_cols=k // 100,
+                               outlier_scale=20.0), dev)
+    w = make_tensor(TensorSpec("lin.gw", m, k, "bf16", "normal", 0.02, 9700 + bw), dev)
+    dy = make_tensor(TensorSpec("lin.gdy", n, m, "bf16", "normal", 1e-3, 9800), dev)
+    xg = x.to(compute_dtype).requires_grad_(True)
+    wg = w.to(compute_dtype).requires_grad_(True)
+    y = quest_linear(xg, wg, block=block, bits_x=bx, bits_w=bw, compute_dtype=compute_dtype, grid=grid)
+    y.backward(dy.to(compute_dtype))
+    torch.cuda.synchronize()
+    f = qo.qat_linear_fwd(to_float64(x), to_float64(w), block, bx, bw, grid=grid)
+    dx_ref, dw_ref = qo.qat_linear_bwd(to_float64(dy), f, block)
+    if grid == "fp4":
+        ex_x, ex_w = exempt_fp4(f["fx"]["y"], f["fx"]["scale"]), exempt_fp4(f["fw"]["y"], f["fw"]["scale"])
+    else:
+        ex_x, ex_w = sparse24_exempt_entries(f["fx"], bx), sparse24_exempt_entries(f["fw"], bw)
+    skip_y, skip_dx, skip_dw = reach_of(ex_x, ex_w, block)
+    log(f"band reach: {int(skip_y.sum())} of y, {int(skip_dx.sum())} of dx, {int(skip_dw.sum())} of dw")
+    close(y.detach(), f["y"], "y", tols, skip_y)
+    close(xg.grad, dx_ref, "dx", tols, skip_dx, block)
+    close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
+
+
+def test_linear_module_grid_option(dev):
+    layer = QuestLinear(512, 128, grid="sparse24", device=dev, dtype=torch.bfloat16)
+    assert layer.grid == "sparse24" and layer.trust_x == 1.0
+    with pytest.raises(ValueError):
+        layer.freeze()  # the FP6 product holds int-grid levels only
+    with pytest.raises(ValueError):
+        QuestLinear(512, 128, grid="int8")
 
 
 def test_linear_module_autograd_3d_input(dev):

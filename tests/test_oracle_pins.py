@@ -466,13 +466,15 @@ def _signs_through_hadamard(rng, rows, cols, block):
     return qo.blockwise_hadamard(signs, block)
 
 
-def test_qat_linear_product_equals_original_domain_product():
+@pytest.mark.parametrize("grid", ["int", "fp4", "sparse24"])
+def test_qat_linear_product_equals_original_domain_product(grid):
     # Orthogonality: the Hadamard-domain product equals the product of the
-    # original-domain reconstructions (x~ = H Q(x) blockwise, H an involution).
+    # original-domain reconstructions (x~ = H Q(x) blockwise, H an involution),
+    # whatever the grid.
     rng = np.random.default_rng(71)
     x = rng.standard_t(4, size=(24, 256))
     w = 0.02 * rng.standard_normal((40, 256))
-    f = qo.qat_linear_fwd(x, w, 64, 4, 3)
+    f = qo.qat_linear_fwd(x, w, 64, 4, 3, grid=grid)
     x_rec = qo.blockwise_hadamard(f["qx"], 64)
     w_rec = qo.blockwise_hadamard(f["qw"], 64)
     assert np.allclose(f["y"], x_rec @ w_rec.T, rtol=1e-12, atol=1e-12)
@@ -497,13 +499,14 @@ def test_qat_linear_all_trusted_gradients_are_straight_through(bx, bw):
     assert np.allclose(dw, dy.T @ x_rec, rtol=1e-12, atol=1e-12)
 
 
-def test_qat_linear_untrusted_entries_get_no_gradient():
+@pytest.mark.parametrize("grid", ["int", "fp4", "sparse24"])
+def test_qat_linear_untrusted_entries_get_no_gradient(grid):
     # In the Hadamard domain the gradient is zero exactly where an operand's
     # entry is untrusted, and equals the unmasked gradient elsewhere.
     rng = np.random.default_rng(73)
     x = rng.standard_t(3, size=(32, 512))
     w = rng.standard_t(3, size=(20, 512))
-    f = qo.qat_linear_fwd(x, w, 128, 2, 2)
+    f = qo.qat_linear_fwd(x, w, 128, 2, 2, grid=grid)
     assert (~f["fx"]["m"]).any() and (~f["fw"]["m"]).any()
     dy = rng.standard_normal((32, 20))
     dx, dw = qo.qat_linear_bwd(dy, f, 128)
