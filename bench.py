@@ -221,6 +221,53 @@ def block_products(lib, qa, torch, dev, reps):
     }
 
 
+def qat_linear_step(torch, dev, reps):
+    """One training step (forward and backward) of the QuEST linear layer against BF16.
+
+    The q projection of the block (16384 tokens x 2048 by 2048 x 2048), b = 4
+    for both operands, block 128, bf16 compute: quest_linear (two forwards with
+    the bf16 dequantised output, the product, then two trust-masked backwards
+    around the two gradient products) against torch's BF16 linear, each as
+    `reps` back-to-back forward + backward passes (torch.autograd.grad, so no
+    gradient accumulation) between events on the launch stream.
+    """
+    from quantization_aware_amd.linear import quest_linear
+    from quest_inputs import LAYER_ACT_2048, TensorSpec, layer_products, make_tensor
+
+    wt = [w for name, _, w in layer_products() if name == "q"][0]
+    x = make_tensor(LAYER_ACT_2048, dev).requires_grad_(True)
+    w = make_tensor(wt, dev).requires_grad_(True)
+    dy = make_tensor(TensorSpec("bench.qat.dy", x.shape[0], w.shape[0], "bf16", "normal", 1e-3, 9900), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def quest():
+        y = quest_linear(x, w, block=BLOCK, bits_x=4, bits_w=4, compute_dtype=torch.bfloat16)
+        torch.autograd.grad(y, (x, w), dy)
+
+    def bf16():
+        y = torch.nn.functional.linear(x, w)
+        torch.autograd.grad(y, (x, w), dy)
+
+    t_q, t_b = timed(quest), timed(bf16)
+    return {"layer": "q projection", "tokens": x.shape[0], "in_features": x.shape[1], "out_features": w.shape[0],
+            "bits": 4, "block": BLOCK, "compute_dtype": "bf16", "quest_step_us": 1000 * t_q,
+            "bf16_step_us": 1000 * t_b, "quest_over_bf16": t_q / t_b,
+            "note": "training step of the QuEST layer (quantisers, bf16 products, trust backwards) vs a plain "
+                    "BF16 linear layer; the quantisers' cost over the three products"}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -485,6 +532,7 @@ def main():
     }
     if not args.no_block_products:
         out["block_products"] = block_products(lib, qa, torch, dev, args.product_reps)
+        out["qat_linear_step"] = qat_linear_step(torch, dev, args.product_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x0, g0, args.cpu_seconds)
     print(json.dumps(out), flush=True)

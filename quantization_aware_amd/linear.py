@@ -84,9 +84,9 @@ class QuestLinearFunction(torch.autograd.Function):
             g = torch.mm(dy, qw)  # gradient reaching Q(x), Hadamard domain
             dx = trust_bwd(g, mask_x, ctx.block, out=g).to(ctx.x_dtype)
         if ctx.needs_input_grad[1]:
-            # gradient reaching Q(w), Hadamard domain (dy^T made contiguous: bf16
-            # products with a transposed operand view are avoided)
-            g = torch.mm(dy.t().contiguous(), qx)
+            # gradient reaching Q(w), Hadamard domain (a 2-D product with a
+            # transposed left operand, as torch's own linear backward computes it)
+            g = torch.mm(dy.t(), qx)
             dw = trust_bwd(g, mask_w, ctx.block, out=g).to(ctx.w_dtype)
         return dx, dw, None, None, None, None, None, None, None
 
