@@ -225,9 +225,10 @@ def qat_linear_step(torch, dev, reps):
     """One training step (forward and backward) of the QuEST linear layer against BF16.
 
     The q projection of the block (16384 tokens x 2048 by 2048 x 2048), b = 4
-    for both operands, block 128, bf16 compute: quest_linear (two forwards with
-    the bf16 dequantised output, the product, then two trust-masked backwards
-    around the two gradient products) against torch's BF16 linear, each as
+    for both operands, block 128, bf16 compute: quest_linear (two operand
+    forwards with codes and mask, the FP6 product; in the backward the two
+    operands rebuilt from their codes, the two BF16 gradient products and two
+    trust-masked backwards) against torch's BF16 linear, each as
     `reps` back-to-back forward + backward passes (torch.autograd.grad, so no
     gradient accumulation) between events on the launch stream.
     """
@@ -264,8 +265,8 @@ def qat_linear_step(torch, dev, reps):
     return {"layer": "q projection", "tokens": x.shape[0], "in_features": x.shape[1], "out_features": w.shape[0],
             "bits": 4, "block": BLOCK, "compute_dtype": "bf16", "quest_step_us": 1000 * t_q,
             "bf16_step_us": 1000 * t_b, "quest_over_bf16": t_q / t_b,
-            "note": "training step of the QuEST layer (quantisers, bf16 products, trust backwards) vs a plain "
-                    "BF16 linear layer; the quantisers' cost over the three products"}
+            "note": "training step of the QuEST layer (quantisers, FP6 forward product, BF16 gradient products, "
+                    "trust backwards) vs a plain BF16 linear layer"}
 
 
 def main():

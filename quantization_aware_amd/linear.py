@@ -13,8 +13,13 @@ by its operand's trust mask and transformed back (pith.science review,
 
 Quantisation, masking and both transforms run in libquest's kernels
 (quest_quantize_fwd_ex, or the FP4 and 2:4-sparse forwards, and
-quest_trust_bwd).  The two training products are plain library GEMMs through
-torch.  ``grid`` picks the format the operands are quantised to: "int"
+quest_trust_bwd).  On the int grid with b <= 4 and K a multiple of 128 the
+forward product is libquest's FP6 product of the two operands
+(quest_quantize_fwd_op with codes and mask, then quest_gemm: exact sums, one
+rounding to the compute dtype), and the backward rebuilds Q(x) and Q(w) from
+the saved codes (quest_dequantize, the same values as the dequantised
+forward output).  The two gradient products, and the forward product of the
+other configurations, are plain library GEMMs through torch.  ``grid`` picks the format the operands are quantised to: "int"
 (b-bit midrise levels), "fp4" (E2M1 levels, 4 bits whatever bits_x and
 bits_w say) or "sparse24" (2:4-sparse b-bit levels), the formats the pages
 train with (pith.science review of QuEST, the list of contributions and the
@@ -31,7 +36,7 @@ from __future__ import annotations
 
 import torch
 
-from . import gemm, quantize_fwd_ex, quantize_fwd_fp4, quantize_fwd_op, quantize_fwd_sparse24, trust_bwd
+from . import dequantize, gemm, quantize_fwd_ex, quantize_fwd_fp4, quantize_fwd_op, quantize_fwd_sparse24, trust_bwd
 
 __all__ = ["QuestLinearFunction", "quest_linear", "quest_linear_operand", "QuestLinear", "default_trust",
            "ONE_BIT_OUTER_TRUST", "GRIDS"]
@@ -67,18 +72,39 @@ class QuestLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, w, block, bits_x, bits_w, compute_dtype, trust_x=1.0, trust_w=1.0, grid="int"):
+        ctx.block = block
+        ctx.x_dtype, ctx.w_dtype = x.dtype, w.dtype
+        # the FP6 product's domain: midrise levels of at most 4 bits, k a multiple of 128 up to 65536
+        # (exact fp32 sums), at most 2^20 output features
+        ctx.fp6 = (grid == "int" and max(bits_x, bits_w) <= 4 and x.shape[1] % 128 == 0 and x.shape[1] <= 65536
+                   and 0 < w.shape[0] <= 2 ** 20 and 0 < x.shape[0] <= 2 ** 30)
+        if ctx.fp6:
+            cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, with_codes=True, with_mask=True)
+            cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, with_codes=True, with_mask=True)
+            out_dtype = torch.float32 if compute_dtype == torch.float32 else torch.bfloat16
+            y = gemm(ox, sx, x.shape[0], bits_x, ow, sw, w.shape[0], bits_w, x.shape[1], out_dtype=out_dtype)
+            y = y.to(compute_dtype)
+            ctx.save_for_backward(cx, sx, cw, sw, mask_x, mask_w)
+            ctx.dims = (x.shape[0], w.shape[0], x.shape[1], bits_x, bits_w, compute_dtype)
+            return y
         mask_x, qx = _quantise(x, block, bits_x, trust_x, grid, compute_dtype)
         mask_w, qw = _quantise(w, block, bits_w, trust_w, grid, compute_dtype)
         y = torch.nn.functional.linear(qx, qw)
         ctx.save_for_backward(qx, qw, mask_x, mask_w)
-        ctx.block = block
-        ctx.x_dtype, ctx.w_dtype = x.dtype, w.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        qx, qw, mask_x, mask_w = ctx.saved_tensors
-        dy = dy.to(qx.dtype).contiguous()
+        if ctx.fp6:
+            cx, sx, cw, sw, mask_x, mask_w = ctx.saved_tensors
+            n, m, k, bits_x, bits_w, compute_dtype = ctx.dims
+            # Q(w) for the input gradient, Q(x) for the weight gradient, rebuilt from the codes
+            qw = dequantize(cw, sw, m, k, bits_w, out_dtype=compute_dtype) if ctx.needs_input_grad[0] else None
+            qx = dequantize(cx, sx, n, k, bits_x, out_dtype=compute_dtype) if ctx.needs_input_grad[1] else None
+        else:
+            qx, qw, mask_x, mask_w = ctx.saved_tensors
+            compute_dtype = qx.dtype
+        dy = dy.to(compute_dtype).contiguous()
         dx = dw = None
         if ctx.needs_input_grad[0]:
             g = torch.mm(dy, qw)  # gradient reaching Q(x), Hadamard domain
