@@ -26,7 +26,7 @@ import torch
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
-from quantization_aware_amd.linear import QuestLinear, default_trust, quest_linear
+from quantization_aware_amd.linear import QuestLinear, QuestLinearFunction, default_trust, quest_linear
 from quest_inputs import TensorSpec, make_tensor, to_float64
 from parity import exempt_entries, exempt_fp4, sparse24_exempt_entries
 
@@ -156,6 +156,25 @@ def test_linear_grids_match_oracle(dev, grid, bx, bw, compute_dtype):
     close(y.detach(), f["y"], "y", tols, skip_y)
     close(xg.grad, dx_ref, "dx", tols, skip_dx, block)
     close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
+
+
+@pytest.mark.parametrize("bits,k,fp6", [(4, 1024, True), (3, 512, True), (5, 1024, False), (4, 192, False)])
+def test_linear_training_forward_path(dev, bits, k, fp6):
+    """The int-grid training forward takes the FP6 product exactly where its domain allows (b <= 4,
+    K a multiple of 128) and then saves the operands' codes, not their dequantised values."""
+    block = 64
+    x = make_tensor(TensorSpec("path.x", 64, k, "bf16", "normal", 1.0, 9950), dev).requires_grad_(True)
+    w = make_tensor(TensorSpec("path.w", 32, k, "bf16", "normal", 0.02, 9951), dev).requires_grad_(True)
+    log(f"training forward path: bits {bits}, k {k}")
+    y = QuestLinearFunction.apply(x, w, block, bits, bits, torch.bfloat16, 1.0, 1.0, "int")
+    saved = y.grad_fn.saved_tensors
+    if fp6:
+        assert len(saved) == 6 and saved[0].dtype == torch.uint8 and saved[0].shape == (64, k * bits // 8)
+    else:
+        assert len(saved) == 4 and saved[0].dtype == torch.bfloat16 and saved[0].shape == (64, k)
+    y.float().sum().backward()
+    torch.cuda.synchronize()
+    assert x.grad is not None and w.grad is not None
 
 
 def test_linear_module_grid_option(dev):
