@@ -509,7 +509,7 @@ def main():
         "step_roofline_frac": step_bytes / (ms_per_step * 1e6) / HBM_PEAK_GBPS,
         "kernels": kernels,
         "other_kernels": {
-            "quest_quantize_fwd_dq (no codes, bf16 dequantised output; QAT training forward)": {
+            "quest_quantize_fwd_dq (no codes, bf16 dequantised output; fake-quant training forward)": {
                 "avg_us": 1000 * fwd_dq_avg, "alg_bytes": fwd_dq_bytes,
                 "gbps": fwd_dq_bytes / (fwd_dq_avg * 1e6),
                 "frac_of_peak": round(fwd_dq_bytes / (fwd_dq_avg * 1e6) / HBM_PEAK_GBPS, 4),
