@@ -76,8 +76,6 @@ __all__ = [
     "operand_e2m3",
     "operand_step",
     "quest_gemm",
-    "tile_operand",
-    "untile_operand",
     "gaussian_mse_levels",
     "gaussian_mse_levels_derivative",
     "fit_alpha_levels",
@@ -580,51 +578,6 @@ def quest_gemm(a_op: np.ndarray, a_scale: np.ndarray, bits_a: int, b_op: np.ndar
     va = e2m3_value(unpack_lsb_first(a_op, 6, k)) * operand_step(a_scale, bits_a)[:, None]
     vb = e2m3_value(unpack_lsb_first(b_op, 6, k)) * operand_step(b_scale, bits_b)[:, None]
     return va @ vb.T
-
-
-def tile_operand(op: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """Tiled storage of a row-major E2M3 operand (R x C*6/8 bytes), C a multiple of 128.
-
-    A storage layout, the one the matrix cores read: rows form blocks of 32
-    (the last padded with zero bytes), each row block is C/128 blocks of 3072
-    bytes, a block is two halves of 64 columns, each 64 slots of 24 bytes;
-    slot l of half e of block c of row block R holds the 24 bytes of row
-    32 R + l % 32 that cover columns 128 c + 64 e + 32 (l // 32) .. + 31.
-    Returns a flat uint8 array of ceil(R / 32) * 32 * C * 6 / 8 bytes.
-    """
-    op = np.asarray(op, dtype=np.uint8)
-    if cols % 128 != 0 or op.shape != (rows, cols * 6 // 8):
-        raise ValueError("operand must be rows x cols*3/4 bytes with cols a multiple of 128")
-    rblocks = (rows + 31) // 32
-    chunks = cols // 128
-    padded = np.zeros((rblocks * 32, cols * 6 // 8), dtype=np.uint8)
-    padded[:rows] = op
-    out = np.zeros((rblocks, chunks, 2, 64, 24), dtype=np.uint8)
-    for rb in range(rblocks):
-        for c in range(chunks):
-            for e in range(2):
-                for lane in range(64):
-                    row = 32 * rb + lane % 32
-                    first_col = 128 * c + 64 * e + 32 * (lane // 32)
-                    out[rb, c, e, lane] = padded[row, first_col * 6 // 8:(first_col + 32) * 6 // 8]
-    return out.reshape(-1)
-
-
-def untile_operand(tiled: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """Inverse of ``tile_operand``: the row-major R x C*6/8 operand (padding dropped)."""
-    tiled = np.asarray(tiled, dtype=np.uint8).reshape(-1)
-    rblocks = (rows + 31) // 32
-    chunks = cols // 128
-    blocks = tiled[:rblocks * chunks * 3072].reshape(rblocks, chunks, 2, 64, 24)
-    out = np.zeros((rblocks * 32, cols * 6 // 8), dtype=np.uint8)
-    for rb in range(rblocks):
-        for c in range(chunks):
-            for e in range(2):
-                for lane in range(64):
-                    row = 32 * rb + lane % 32
-                    first_col = 128 * c + 64 * e + 32 * (lane // 32)
-                    out[row, first_col * 6 // 8:(first_col + 32) * 6 // 8] = blocks[rb, c, e, lane]
-    return out[:rows]
 
 
 # ---------------------------------------------------------------------------

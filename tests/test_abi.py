@@ -14,6 +14,7 @@ import pytest
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
+from operand_layout import tile_operand
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "quest.h")
@@ -307,7 +308,7 @@ def test_operand_bytes(lib):
     assert lib.quest_operand_bytes(-1, 128) == 0
     rng = np.random.default_rng(0)
     op = rng.integers(0, 256, size=(45, 384 * 3 // 4), dtype=np.uint8)
-    assert qo.tile_operand(op, 45, 384).size == lib.quest_operand_bytes(45, 384)
+    assert tile_operand(op, 45, 384).size == lib.quest_operand_bytes(45, 384)
 
 
 def test_fwd_op_and_gemm_empty_calls_are_noops(lib):

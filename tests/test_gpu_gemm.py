@@ -24,6 +24,7 @@ import torch
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
+from operand_layout import tile_operand, untile_operand
 from parity import check_fwd, exempt_entries
 from quest_inputs import TensorSpec, layer_products, make_tensor, to_float64
 
@@ -49,7 +50,7 @@ def halves_e2m3(u: np.ndarray, b: int) -> np.ndarray:
 def gpu_fields(op: torch.Tensor, rows: int, cols: int) -> np.ndarray:
     """6-bit fields of a GPU operand, rows x cols, read back through the layout's definition."""
     flat = op.cpu().numpy()[: qa.operand_bytes(rows, cols)]
-    return qo.unpack_lsb_first(qo.untile_operand(flat, rows, cols), 6, cols)
+    return qo.unpack_lsb_first(untile_operand(flat, rows, cols), 6, cols)
 
 
 # ---------------------------------------------------------------------------
@@ -127,14 +128,14 @@ def test_fwd_op_leaves_bytes_outside_the_operand_alone(dev):
 def oracle_operand(x64: np.ndarray, block: int, b: int):
     rows, cols = x64.shape
     f = qo.quantize_fwd(x64, block, b)
-    tiled = qo.tile_operand(qo.operand_e2m3(f["codes"], cols, b), rows, cols)
+    tiled = tile_operand(qo.operand_e2m3(f["codes"], cols, b), rows, cols)
     return f, tiled, f["scale"].astype(np.float32)
 
 
 def gemm_reference(op_a, sa32, ba, op_b, sb32, bb, m, n, k):
     """The oracle's product and the float64 sum of |products| (which bounds its own rounding)."""
-    a_rows = qo.untile_operand(op_a, m, k)
-    b_rows = qo.untile_operand(op_b, n, k)
+    a_rows = untile_operand(op_a, m, k)
+    b_rows = untile_operand(op_b, n, k)
     ref = qo.quest_gemm(a_rows, sa32.astype(np.float64), ba, b_rows, sb32.astype(np.float64), bb, k)
     va = np.abs(qo.e2m3_value(qo.unpack_lsb_first(a_rows, 6, k))) * qo.operand_step(sa32, ba)[:, None]
     vb = np.abs(qo.e2m3_value(qo.unpack_lsb_first(b_rows, 6, k))) * qo.operand_step(sb32, bb)[:, None]
@@ -211,11 +212,11 @@ def test_gemm_exact_at_the_largest_k(dev):
     ua[0] = 15  # rows of one sign: the largest sums, +3686400 and -3686400
     ub[0] = 15
     ub[1] = 0
-    op_a = qo.tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ua, b), k, b), m, k)
-    op_b = qo.tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ub, b), k, b), n, k)
+    op_a = tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ua, b), k, b), m, k)
+    op_b = tile_operand(qo.operand_e2m3(qo.pack_lsb_first(ub, b), k, b), n, k)
     sa = np.full(m, 7.5, dtype=np.float32)
     sb = np.full(n, 7.5, dtype=np.float32)
-    ref = qo.quest_gemm(qo.untile_operand(op_a, m, k), sa.astype(np.float64), b, qo.untile_operand(op_b, n, k),
+    ref = qo.quest_gemm(untile_operand(op_a, m, k), sa.astype(np.float64), b, untile_operand(op_b, n, k),
                         sb.astype(np.float64), b, k)
     assert ref[0, 0] == 3686400.0 and ref[0, 1] == -3686400.0
     y = qa.gemm(torch.from_numpy(op_a).to(dev), torch.from_numpy(sa).to(dev), m, b, torch.from_numpy(op_b).to(dev),

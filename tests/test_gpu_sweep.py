@@ -14,6 +14,7 @@ import torch
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
+from operand_layout import tile_operand, untile_operand
 from parity import (TOL_BF16, TOL_F32, check_fwd, check_fwd_fp4, check_fwd_sparse24, check_grad, check_values,
                     exempt_entries)
 from quest_inputs import TensorSpec, make_tensor, to_float64
@@ -127,13 +128,13 @@ def test_sweep_gemm(dev, case):
                                            outlier_scale=10.0), "cpu"))
     xb = to_float64(make_tensor(TensorSpec("sw.b", n, k, "f32", "normal", 0.02, 29000 + case), "cpu"))
     fa, fb = qo.quantize_fwd(xa, 128, ba), qo.quantize_fwd(xb, 128, bb)
-    op_a = qo.tile_operand(qo.operand_e2m3(fa["codes"], k, ba), m, k)
-    op_b = qo.tile_operand(qo.operand_e2m3(fb["codes"], k, bb), n, k)
+    op_a = tile_operand(qo.operand_e2m3(fa["codes"], k, ba), m, k)
+    op_b = tile_operand(qo.operand_e2m3(fb["codes"], k, bb), n, k)
     sa, sb = fa["scale"].astype(np.float32), fb["scale"].astype(np.float32)
-    ref = qo.quest_gemm(qo.untile_operand(op_a, m, k), sa.astype(np.float64), ba, qo.untile_operand(op_b, n, k),
+    ref = qo.quest_gemm(untile_operand(op_a, m, k), sa.astype(np.float64), ba, untile_operand(op_b, n, k),
                         sb.astype(np.float64), bb, k)
-    va = np.abs(qo.e2m3_value(qo.unpack_lsb_first(qo.untile_operand(op_a, m, k), 6, k))) * qo.operand_step(sa, ba)[:, None]
-    vb = np.abs(qo.e2m3_value(qo.unpack_lsb_first(qo.untile_operand(op_b, n, k), 6, k))) * qo.operand_step(sb, bb)[:, None]
+    va = np.abs(qo.e2m3_value(qo.unpack_lsb_first(untile_operand(op_a, m, k), 6, k))) * qo.operand_step(sa, ba)[:, None]
+    vb = np.abs(qo.e2m3_value(qo.unpack_lsb_first(untile_operand(op_b, n, k), 6, k))) * qo.operand_step(sb, bb)[:, None]
     slack = 2.0 * k * 2.0 ** -53 * (va @ vb.T)
     out_dtype = torch.float32 if case % 2 == 0 else torch.bfloat16
     y = qa.gemm(torch.from_numpy(op_a).to(dev), torch.from_numpy(sa).to(dev), m, ba, torch.from_numpy(op_b).to(dev),
