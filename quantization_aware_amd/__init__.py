@@ -35,7 +35,9 @@ __all__ = [
     "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquest.so")
+# The library next to this file; QUEST_LIBRARY names another build of it (the
+# sanitizer build the CPU tests make, for instance).
+LIB_PATH = os.environ.get("QUEST_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquest.so")
 
 QUEST_OK, QUEST_EINVAL, QUEST_EUNSUPPORTED, QUEST_EALIGN, QUEST_EHIP = range(5)
 QUEST_F32, QUEST_BF16 = 0, 1
@@ -150,6 +152,26 @@ def _device_tensor(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _buffer(name: str, t, dtype, need: int) -> None:
+    """A caller-supplied buffer: a tensor of `dtype` holding at least `need` elements.  The C ABI takes raw
+    pointers and cannot see sizes, so a short buffer would be read or written past its end; it is rejected
+    here instead.  (Device and contiguity are checked by _on_device once every size has been.)"""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < need:
+        raise ValueError(f"{name} too small: {t.numel()} elements, the call needs {need}")
+
+
+def _on_device(device, **tensors) -> None:
+    """Every tensor contiguous on the GPU, on `device`."""
+    for name, t in tensors.items():
+        _device_tensor(name, t)
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
 
 
 def _stream_handle(device: torch.device, stream) -> int:
@@ -287,9 +309,8 @@ def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
     flat uint8 tensor of operand_bytes(rows, cols) bytes.
     """
     lib = load_library()
-    _device_tensor("x", x)
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D (rows x cols)")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor (rows x cols)")
     rows, cols = x.shape
     dev = x.device
     codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev) if with_codes else None
@@ -298,6 +319,9 @@ def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
     mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev) if with_mask else None
     if operand is None:
         operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=dev)
+    _buffer("scale", scale, torch.float32, rows)
+    _buffer("operand", operand, torch.uint8, operand_bytes(rows, cols))
+    _on_device(dev, x=x, scale=scale, operand=operand)
     st = lib.quest_quantize_fwd_op(
         x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),
         codes.data_ptr() if codes is not None else None, scale.data_ptr(),
@@ -311,12 +335,18 @@ def gemm(a: torch.Tensor, a_scale: torch.Tensor, m: int, a_bits: int, b: torch.T
          n: int, b_bits: int, k: int, out_dtype=torch.bfloat16, out=None, stream=None) -> torch.Tensor:
     """Product of two matrix-core operands (quest_gemm): an m x n tensor of out_dtype."""
     lib = load_library()
-    for name, t in (("a", a), ("a_scale", a_scale), ("b", b), ("b_scale", b_scale)):
-        _device_tensor(name, t)
+    m, n, k = int(m), int(n), int(k)
+    _buffer("a", a, torch.uint8, operand_bytes(m, k))
+    _buffer("a_scale", a_scale, torch.float32, m)
+    _buffer("b", b, torch.uint8, operand_bytes(n, k))
+    _buffer("b_scale", b_scale, torch.float32, n)
     dev = a.device
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
-    _device_tensor("out", out)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"out must be a float32 or bfloat16 tensor, got {getattr(out, 'dtype', type(out))}")
+    _buffer("out", out, out.dtype, m * n)
+    _on_device(dev, a=a, a_scale=a_scale, b=b, b_scale=b_scale, out=out)
     st = lib.quest_gemm(a.data_ptr(), a_scale.data_ptr(), m, int(a_bits), b.data_ptr(), b_scale.data_ptr(), n,
                         int(b_bits), k, out.data_ptr(), _dtype_code(out), _stream_handle(dev, stream))
     _check("quest_gemm", st)
@@ -377,8 +407,10 @@ def dequantize_fp4(codes: torch.Tensor, scale: torch.Tensor, rows: int, cols: in
                    stream=None) -> torch.Tensor:
     """FP4 codes back to their levels (quest_dequantize_fp4)."""
     lib = load_library()
-    _device_tensor("codes", codes)
-    _device_tensor("scale", scale)
+    rows, cols = int(rows), int(cols)
+    _buffer("codes", codes, torch.uint8, max(rows, 0) * max(cols, 0) // 2)
+    _buffer("scale", scale, torch.float32, rows)
+    _on_device(codes.device, codes=codes, scale=scale)
     out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
     st = lib.quest_dequantize_fp4(codes.data_ptr(), scale.data_ptr(), rows, cols, out.data_ptr(), _dtype_code(out),
                                   _stream_handle(codes.device, stream))
@@ -390,8 +422,11 @@ def dequantize_sparse24(codes: torch.Tensor, index: torch.Tensor, scale: torch.T
                         out_dtype=torch.float32, stream=None) -> torch.Tensor:
     """2:4-sparse codes back to the dense reconstruction (quest_dequantize_sparse24)."""
     lib = load_library()
-    for name, t in (("codes", codes), ("index", index), ("scale", scale)):
-        _device_tensor(name, t)
+    rows, cols, b = int(rows), int(cols), int(b)
+    _buffer("codes", codes, torch.uint8, int(lib.quest_sparse24_codes_bytes(rows, cols, b)))
+    _buffer("index", index, torch.uint8, int(lib.quest_sparse24_index_bytes(rows, cols)))
+    _buffer("scale", scale, torch.float32, rows)
+    _on_device(codes.device, codes=codes, index=index, scale=scale)
     out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
     st = lib.quest_dequantize_sparse24(codes.data_ptr(), index.data_ptr(), scale.data_ptr(), rows, cols, int(b),
                                        out.data_ptr(), _dtype_code(out), _stream_handle(codes.device, stream))
