@@ -555,10 +555,12 @@ __device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float
 // block (runs of one block are neighbouring n).  Codes and mask bits are
 // packed per slot (8 entries) and a transpose between lane quarters and
 // slots hands lane l all four quarters of run l, which it stores as in the
-// run-per-lane kernels.  Loads run two tiles ahead of the arithmetic.
+// run-per-lane kernels.  Each wave takes one tile and the launch covers every
+// tile: short-lived waves of few registers (50 at b = 4), eight per SIMD,
+// which the hardware refills as they finish, kept more loads in flight than
+// a grid-stride loop with its loads one to three tiles ahead.
 // kQuant = false (operand calls without codes and mask) leaves the codes and
-// mask work out of the build: 100 registers instead of 188, four waves per
-// SIMD instead of two.
+// mask work out of the build.
 template <int LOGN, int B, int LOGR, typename Dq, bool kQuant = true>
 __global__ void __launch_bounds__(256)
     quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
@@ -570,13 +572,11 @@ __global__ void __launch_bounds__(256)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t rows = total_runs >> LOGR;
   const int64_t tiles = (total_runs + 63) >> 6;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
-  // The operand is staged per workgroup step (a barrier per tile), so the
-  // four waves then run the same steps: a wave past the last tile computes
-  // on zeros and every store it makes is dropped or lands in padding.
-  const int64_t tile_end = kIsOperand<Dq> ? tiles + wave : tiles;
-  if (tile >= tile_end) return;
+  const int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
+  // The operand is staged per workgroup (a barrier), so all four waves of
+  // the last workgroup run: a wave past the last tile computes on zeros and
+  // every store it makes is dropped or lands in padding.
+  if (!kIsOperand<Dq> && tile >= tiles) return;
   __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
@@ -651,23 +651,9 @@ __global__ void __launch_bounds__(256)
                                           window_at(scale, t * ROWS * 4, rows * 4, ROWS * 4), scale_off, 0, 0);
   };
 
-  u32x4 a[4], b[4], c[4];
-  fetch(tile, a);
-  fetch(tile + stride, b);
-  for (;;) {
-    fetch(tile + 2 * stride, c);
-    process(tile, a);
-    tile += stride;
-    if (tile >= tile_end) break;
-    fetch(tile + 2 * stride, a);
-    process(tile, b);
-    tile += stride;
-    if (tile >= tile_end) break;
-    fetch(tile + 2 * stride, b);
-    process(tile, c);
-    tile += stride;
-    if (tile >= tile_end) break;
-  }
+  u32x4 f[4];
+  fetch(tile, f);
+  process(tile, f);
 }
 
 // bf16 rows of 16 m runs (m > 4: more than 2048 columns, a multiple of 512)
@@ -935,7 +921,7 @@ inline int log2_exact(int v) {
   return l;
 }
 
-// Workgroups (of four waves) launched for the tiled forward kernel: two per
+// Workgroups (of four waves) launched for the tiled forward kernels: two per
 // compute unit on the 256-CU MI355X, so each wave walks several tiles and its
 // loads run ahead of the arithmetic.
 constexpr int64_t kFwdTileWorkgroups = 512;
@@ -981,9 +967,7 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
     if (a.allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
       const int64_t total_runs = rows * runs_per_row;
       const int64_t tiles = (total_runs + 63) / 64;
-      int64_t wgs = (tiles + 3) / 4;
-      if (wgs > kFwdTileWorkgroups) wgs = kFwdTileWorkgroups;
-      const dim3 grid(static_cast<uint32_t>(wgs));
+      const dim3 grid(static_cast<uint32_t>((tiles + 3) / 4));  // one tile per wave
       // An operand call that asks for neither codes nor mask runs the build without them.
       auto run = [&](auto logr, auto quant) {
         hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, B, decltype(logr)::value, Dq, decltype(quant)::value>), grid,
