@@ -10,10 +10,13 @@ several buffer sets so that no step finds its data in the 256 MB last-level
 cache.
 
 Timing, all with HIP events on the stream the kernels are launched on:
-  * the step: K steps between two events, bracketed by device
-    synchronisation.  Steps are independent batches: each step's backward
-    runs on a second stream after an event from its own forward, so it
-    overlaps the next step's forward (the one-stream time is reported too);
+  * the step: K steps bracketed by device synchronisation.  Steps are
+    independent batches on two streams, step i on stream i % 2 with its
+    backward after its forward in that stream's order, so consecutive steps
+    overlap (the one-stream time is reported too).  Each stream records a
+    start and an end event; the event time is the span from the earlier
+    start to the later end, and ms_per_step is the larger of that and the
+    wall clock between the two synchronisations, over K;
   * each kernel: K back-to-back launches of that kernel alone between two
     events (events between every kernel would add their own gaps);
   * a plain copy kernel (elementwise negation) moving as many bytes as the
@@ -56,6 +59,10 @@ def parse_args():
     p.add_argument("--product-reps", type=int, default=50, help="back-to-back launches per product timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain elementwise copy of known size (for counter calibration)")
+    p.add_argument("--configs", default="C2,C3,C4,C5",
+                   help="comma-separated full-size configurations to time beside the headline ('none': skip)")
+    p.add_argument("--only-configs", action="store_true",
+                   help="time only the --configs (no headline step, products or CPU baseline; for profiling)")
     return p.parse_args()
 
 
@@ -131,7 +138,162 @@ def cpu_baseline(x_dev, g_dev, target_seconds):
         "sample": f"{done} rows ({done * COLS} elements; {done / ROWS:.2f} passes over the 16384x2048 workload, "
         f"in {chunk}-row chunks), fwd then bwd, {elapsed:.1f} s of oracle time",
         "cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "blas_threads": int(threads),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+CONFIG_TARGET_FRAC = 0.70  # the bar: 70% of the HBM roofline
+COLD_BYTES = 640 << 20  # buffer sets rotate until this much lies between two uses of one set
+
+
+def config_runs(lib, qa, torch, dev, reps, names):
+    """Full-size configurations C2-C5, each pass timed cache-cold against 70% of the HBM roofline.
+
+    Every timing is `reps` back-to-back repetitions between HIP events on the
+    launch stream, rotating over enough copies of the inputs and outputs that
+    more than 512 MiB is touched between two uses of one copy (the 256 MB
+    last-level cache then serves no repetition from an earlier one).
+    C2: 16384x512 bf16 Student-t(4) activation, forward at b = 1..4;
+    C3: the seven weight tensors of a 1.6B-scale block, forward at b = 4, one
+        repetition quantising all seven;
+    C4: trust backward of a 65536x2048 bf16 gradient with the mask of a
+        Student-t(4) activation's forward;
+    C5: 131072x5632 bf16 Student-t(3) activation, forward at b = 1 then the
+        backward of a gradient of that shape, one step.
+    """
+    from quest_inputs import WORKLOADS, make_tensor
+
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    vp = ctypes.c_void_p
+    f_fwd, f_bwd = lib.quest_quantize_fwd, lib.quest_trust_bwd
+
+    def check(name, st):
+        if st:
+            raise qa.QuestError(name, st, lib.quest_status_string(st).decode())
+
+    def timed(launch, nsets):
+        for i in range(min(nsets, 3)):
+            launch(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            launch(i % nsets)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * a.elapsed_time(b) / reps
+
+    def sets_for(set_bytes):
+        return max(2, -(-COLD_BYTES // set_bytes) + 1)
+
+    def entry(us, alg_bytes, elements):
+        gbps = alg_bytes / (us * 1e3)
+        return {"us": round(us, 3), "alg_bytes": alg_bytes, "gbps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "elements_per_s": elements / (us * 1e-6),
+                "target_us_at_70pct": round(alg_bytes / (CONFIG_TARGET_FRAC * HBM_PEAK_GBPS * 1e3), 3)}
+
+    def fwd_set(x, bits):
+        r, c = x.shape
+        return (x, torch.empty((r, c * bits // 8), dtype=torch.uint8, device=dev),
+                torch.empty((r,), dtype=torch.float32, device=dev),
+                torch.empty((r, c // 8), dtype=torch.uint8, device=dev))
+
+    def fwd_call(st_, block, bits):
+        x, cd, sc, mk = st_
+        return lambda: check("quest_quantize_fwd", f_fwd(vp(x.data_ptr()), qa.QUEST_BF16, x.shape[0], x.shape[1],
+                                                         block, bits, vp(cd.data_ptr()), vp(sc.data_ptr()),
+                                                         vp(mk.data_ptr()), sh))
+
+    def bwd_call(g, mk, out, block):
+        return lambda: check("quest_trust_bwd", f_bwd(vp(g.data_ptr()), qa.QUEST_BF16, vp(mk.data_ptr()), g.shape[0],
+                                                      g.shape[1], block, vp(out.data_ptr()), sh))
+
+    res = {}
+    if "C2" in names:
+        wl = WORKLOADS["C2"]
+        spec = wl.fwd[0]
+        x0 = make_tensor(spec, dev)
+        rec = {"workload": wl.description}
+        for bits in wl.bits:
+            alg = alg_bytes_fwd(spec.rows, spec.cols, 2, bits)
+            n = sets_for(alg)
+            sets = [fwd_set(x0 if i == 0 else x0.clone(), bits) for i in range(n)]
+            calls = [fwd_call(st_, wl.block, bits) for st_ in sets]
+            rec[f"b{bits}"] = entry(timed(lambda i: calls[i](), n), alg, spec.elements)
+            rec[f"b{bits}"]["buffer_sets"] = n
+            del sets, calls
+        res["C2"] = rec
+        del x0
+    if "C3" in names:
+        wl = WORKLOADS["C3"]
+        ws = [make_tensor(spec, dev) for spec in wl.fwd]
+        alg = sum(alg_bytes_fwd(w.shape[0], w.shape[1], 2, 4) for w in ws)
+        n = sets_for(alg)
+        sets = [[fwd_set(w if i == 0 else w.clone(), 4) for w in ws] for i in range(n)]
+        calls = [[fwd_call(st_, wl.block, 4) for st_ in one] for one in sets]
+
+        def all_seven(i):
+            for c in calls[i]:
+                c()
+
+        rec = {"workload": wl.description, "all_seven": entry(timed(all_seven, n), alg, sum(w.numel() for w in ws)),
+               "buffer_sets": n, "per_tensor_us": {}}
+        for j, spec in enumerate(wl.fwd):
+            rec["per_tensor_us"][spec.name.split(".")[1]] = round(timed(lambda i: calls[i][j](), n), 3)
+        res["C3"] = rec
+        del ws, sets, calls
+    if "C4" in names:
+        wl = WORKLOADS["C4"]
+        act, gspec = wl.fwd[0], wl.grad[0]
+        _, _, mask = qa.quantize_fwd(make_tensor(act, dev), wl.block, 4)
+        g0 = make_tensor(gspec, dev)
+        alg = alg_bytes_bwd(gspec.rows, gspec.cols, 2)
+        n = sets_for(alg)
+        sets = [(g0 if i == 0 else g0.clone(), mask if i == 0 else mask.clone(), torch.empty_like(g0))
+                for i in range(n)]
+        calls = [bwd_call(g, mk, o, wl.block) for g, mk, o in sets]
+        res["C4"] = {"workload": wl.description, "bwd": entry(timed(lambda i: calls[i](), n), alg, gspec.elements),
+                     "buffer_sets": n}
+        del sets, calls, g0, mask
+    if "C5" in names:
+        wl = WORKLOADS["C5"]
+        act, gspec = wl.fwd[0], wl.grad[0]
+        x0, g0 = make_tensor(act, dev), make_tensor(gspec, dev)
+        fwd_b = alg_bytes_fwd(act.rows, act.cols, 2, 1)
+        bwd_b = alg_bytes_bwd(gspec.rows, gspec.cols, 2)
+        sets = []
+        for i in range(2):
+            fs = fwd_set(x0 if i == 0 else x0.clone(), 1)
+            sets.append((fs, g0 if i == 0 else g0.clone(), torch.empty_like(g0)))
+        fcalls = [fwd_call(fs, wl.block, 1) for fs, _, _ in sets]
+        bcalls = [bwd_call(g, fs[3], o, wl.block) for fs, g, o in sets]
+
+        def step(i):
+            fcalls[i]()
+            bcalls[i]()
+
+        res["C5"] = {"workload": wl.description,
+                     "step": entry(timed(step, 2), fwd_b + bwd_b, act.elements),
+                     "fwd": entry(timed(lambda i: fcalls[i](), 2), fwd_b, act.elements),
+                     "bwd": entry(timed(lambda i: bcalls[i](), 2), bwd_b, gspec.elements),
+                     "buffer_sets": 2, "schedule": "forward then backward on one stream, back to back"}
+        del sets, fcalls, bcalls, x0, g0
+    torch.cuda.synchronize()
+    return res
 
 
 FP6_PEAK_TFLOPS = 10100.0  # MI355X dense FP6/FP4 matrix peak
@@ -287,6 +449,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lib = qa.load_library()
     dev = torch.device("cuda", 0)
+    config_names = [] if args.configs.strip().lower() == "none" else [c.strip() for c in args.configs.split(",")]
+    unknown = [c for c in config_names if c not in ("C2", "C3", "C4", "C5")]
+    if unknown:
+        sys.exit(f"unknown --configs {unknown}; the full-size configurations are C2, C3, C4, C5")
+    if args.only_configs:
+        print(json.dumps({"configs": config_runs(lib, qa, torch, dev, args.product_reps, config_names)}), flush=True)
+        return
     wl = WORKLOADS["T"]
     x0 = make_tensor(wl.fwd[0], dev)
     g0 = make_tensor(wl.grad[0], dev)
@@ -299,13 +468,9 @@ def main():
     dqs = [torch.empty_like(x0) for _ in range(N_SETS)]  # fake-quantised outputs of the fused forward
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    # Steps are independent batches: step i's backward runs on a second stream
-    # (default priority) after an event from step i's forward, so it overlaps
-    # step i+1's forward; a forward waits for the backward that last read its
-    # buffer set.
-    # Both are streams created here with hipStreamCreate (default priority):
-    # the null stream would synchronise with the other stream and serialise
-    # the two passes.
+    # Two streams created here with hipStreamCreate (default priority): the
+    # null stream would synchronise with the other stream and serialise the
+    # two.
     def hip_stream():
         st = ctypes.c_void_p()
         if lib.hipStreamCreate(ctypes.byref(st)):
@@ -327,16 +492,9 @@ def main():
     ]
     f_fwd, f_bwd = lib.quest_quantize_fwd, lib.quest_trust_bwd
     # Events of the HIP runtime that libquest (and torch) use, called
-    # directly: they bracket the timed region across both streams.
-    hip_record, hip_wait = lib.hipEventRecord, lib.hipStreamWaitEvent
+    # directly: they bracket the timed region on both streams.
+    hip_record = lib.hipEventRecord
     hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    hip_wait.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
-
-    def hip_event():
-        ev = ctypes.c_void_p()
-        if lib.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(2)):  # hipEventDisableTiming
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        return ev
 
     # Steps are independent batches.  Step i runs on stream i % 2, its
     # backward after its forward in that stream's order; steps on the two
@@ -371,29 +529,37 @@ def main():
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps.  The start event is on the forward stream
-    # (the backward stream waits for it); the end event follows both streams.
+    # Timed region: exactly K steps between two device synchronisations.  A
+    # start and an end event on each stream (no stream waits on the other:
+    # a cross-stream wait costs microseconds at both ends of a short region);
+    # the event time is the span from the earlier start to the later end.
     K = args.steps
-    e0, e1, e_join = ctypes.c_void_p(), ctypes.c_void_p(), hip_event()
-    for e in (e0, e1):
+
+    def timing_event():
+        e = ctypes.c_void_p()
         if lib.hipEventCreate(ctypes.byref(e)):
             raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(a, b):
+        t = ctypes.c_float()
+        if lib.hipEventElapsedTime(ctypes.byref(t), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    starts = [timing_event() for _ in streams]
+    ends = [timing_event() for _ in streams]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    hip_record(e0, sh_a)
-    hip_wait(sh_b, e0, 0)
+    for e, st in zip(starts, streams):
+        hip_record(e, st)
     run_steps(args.warmup, K)
-    hip_record(e_join, sh_b)
-    hip_wait(sh_a, e_join, 0)
-    hip_record(e1, sh_a)
+    for e, st in zip(ends, streams):
+        hip_record(e, st)
     enqueue = time.perf_counter() - t0
-    lib.hipEventSynchronize(e1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    elapsed = ctypes.c_float()
-    if lib.hipEventElapsedTime(ctypes.byref(elapsed), e0, e1):
-        raise RuntimeError("hipEventElapsedTime failed")
-    step_ms = elapsed.value
+    step_ms = max(elapsed_ms(a, b) for a in starts for b in ends)
     ms_per_step = max(step_ms, 1000.0 * wall) / K
     elements = ROWS * COLS
     value = elements / (ms_per_step / 1000.0)
@@ -479,8 +645,10 @@ def main():
         "frac": round(dom["gbps"] / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
         "kernel": dom_name,
+        "scope": "the dominant kernel alone, K back-to-back launches; the whole step's fraction is step_frac",
     }
     step_bytes = fwd_bytes + bwd_bytes
+    roofline["step_frac"] = round(step_bytes / (ms_per_step * 1e6) / HBM_PEAK_GBPS, 4)
     out = {
         "metric": METRIC,
         "value": value,
@@ -527,10 +695,12 @@ def main():
                            "gbps": copy_gbps, "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "timing": {"step_events_ms": step_ms, "step_wall_s": wall,
                    "schedule": "step i on stream i % 2 (forward then backward in stream order); "
-                               "consecutive steps overlap",
+                               "consecutive steps overlap; start and end events on both streams",
                    "one_stream_ms_per_step": one_stream_ms,
                    "host_enqueue_s": enqueue, "one_stream_host_enqueue_s": enqueue_one},
     }
+    if config_names:
+        out["configs"] = config_runs(lib, qa, torch, dev, args.product_reps, config_names)
     if not args.no_block_products:
         out["block_products"] = block_products(lib, qa, torch, dev, args.product_reps)
         out["qat_linear_step"] = qat_linear_step(torch, dev, args.product_reps)
