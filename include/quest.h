@@ -62,10 +62,15 @@ typedef enum {
   QUEST_EINVAL = 1,       /* bad pointer, size, dtype or forbidden aliasing */
   QUEST_EUNSUPPORTED = 2, /* block, bit width or row width outside what is built */
   QUEST_EALIGN = 3,       /* a buffer is not 16-byte aligned */
-  QUEST_EHIP = 4          /* the HIP runtime reported an error at launch */
+  QUEST_EHIP = 4,         /* the HIP runtime reported an error at launch */
+  QUEST_STATUS_INT_RANGE_ = 0x7FFFFFFF /* not a status: gives the type int's range of values */
 } quest_status;
 
-typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1 } quest_dtype;
+/* Element types.  The last enumerator is not a type: it gives quest_dtype the
+   whole range of int, so that any value a caller passes can be received and
+   rejected with QUEST_EINVAL (in C++ a value outside an enumeration's range
+   could not even be loaded). */
+typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1, QUEST_DTYPE_INT_RANGE_ = 0x7FFFFFFF } quest_dtype;
 
 /* Largest row width handled in one pass (a row is reduced by one workgroup). */
 #define QUEST_MAX_COLS 32768
