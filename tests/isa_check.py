@@ -15,7 +15,7 @@ import re
 import subprocess
 import tempfile
 
-from . import build
+from quantization_aware_amd import build
 
 _PAIR = re.compile(r"s\[(\d+):(\d+)\]|\b(vcc)\b")
 _FUNC = re.compile(r"^(_Z\S+):")

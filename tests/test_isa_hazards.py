@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
-from quantization_aware_amd import isa_check
+import isa_check
 
 SNIPPET = """_Zkernel:
 \tv_cmp_le_f32_e64 s[0:1], v1, v2
