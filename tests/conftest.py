@@ -8,3 +8,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libquest")
+
+
+def pytest_terminal_summary(terminalreporter):
+    parity = sys.modules.get("parity")
+    cases = getattr(parity, "RATE_READING_CASES", [])
+    if cases:
+        terminalreporter.write_line("in-band differences allowed by the rate reading of the 1e-5 mismatch bound:")
+        for c in cases:
+            terminalreporter.write_line(f"  {c}")

@@ -16,10 +16,15 @@ cancel to almost zero.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 
 from oracle import quest_oracle as qo
+
+# In-band differences that the plain fraction (count <= 1e-5 * entries) would
+# not allow and the rate reading does; tests/conftest.py lists them at the end.
+RATE_READING_CASES: list[str] = []
 
 BAND = 1e-6
 MAX_MISMATCH_FRACTION = 1e-5
@@ -79,6 +84,13 @@ def check_fwd(x64: np.ndarray, block: int, b: int, codes, scale, mask, ref=None,
         allowed = math.ceil(max_fraction * bad_u.size)
         count = int((bad_u | bad_m).sum())
         assert count <= allowed, f"{count} differing entries (fraction {frac}) above {allowed} allowed"
+        if count > max_fraction * bad_u.size:
+            # the case the rate reading exists for, listed at the end of the test run
+            rr, cc = np.argwhere(bad_u | bad_m)[0]
+            RATE_READING_CASES.append(
+                f"{os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]}: {count} of {bad_u.size} entries "
+                f"(b={b}, block={block}, trust={trust}), first at ({rr},{cc}) y={ref['y'][rr, cc]!r} "
+                f"s={ref['scale'][rr]!r}")
     s_ref = ref["scale"]
     zero = s_ref == 0.0
     assert np.all(scale[zero] == 0.0)

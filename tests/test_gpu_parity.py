@@ -3,9 +3,9 @@
 Every GPU input comes from the seeded generators in quest_inputs; the oracle
 receives the same bits widened to float64.  Small workloads are compared in
 full; the full-size workloads run on the GPU in the launch configuration the
-benchmark times, and a seeded sample of rows (always including the first and
-the last) is recomputed by the oracle, which is exact because every row is
-independent.  The backward pass is always fed the oracle's own mask on the
+benchmark times and are recomputed by the oracle row chunk by row chunk
+(every row of T, C3 and C4; a seeded eighth of C5's rows), which is exact
+because every row is independent.  The backward pass is always fed the oracle's own mask on the
 rows it checks, so the comparison has no boundary exemptions.
 """
 from __future__ import annotations
@@ -16,7 +16,7 @@ import torch
 
 import quantization_aware_amd as qa
 from oracle import quest_oracle as qo
-from parity import TOL_BF16, TOL_F32, check_fwd, check_grad, check_values, exempt_entries
+from parity import MAX_MISMATCH_FRACTION, TOL_BF16, TOL_F32, check_fwd, check_grad, check_values, exempt_entries
 from quest_inputs import WORKLOADS, TensorSpec, make_tensor, to_float64
 
 pytestmark = pytest.mark.gpu
@@ -126,57 +126,93 @@ def test_c2_fwd_full(dev, b):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads, sampled rows.
+# Full-size workloads: every row (C5: a seeded eighth of its rows), compared
+# in chunks of rows.  The GPU runs each pass once on the whole tensor, in the
+# launch configuration the benchmark times.
 # ---------------------------------------------------------------------------
+CHUNK_ROWS = 2048
 
-def _fwd_bwd_sampled(dev, wl, act_spec, grad_spec, b, n_rows, seed):
+
+def _chunks(rows: np.ndarray):
+    for i in range(0, len(rows), CHUNK_ROWS):
+        yield rows[i:i + CHUNK_ROWS]
+
+
+def _take(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    """Rows of a GPU tensor as float64 (bf16 widened exactly) or as raw bytes."""
+    sel = t.index_select(0, torch.as_tensor(rows, device=t.device))
+    if sel.dtype == torch.bfloat16:
+        return to_float64(sel)
+    if sel.dtype == torch.float32:
+        return sel.cpu().numpy().astype(np.float64)
+    return sel.cpu().numpy()
+
+
+def _fwd_bwd_rows(dev, wl, act_spec, grad_spec, b, rows=None):
+    """Forward of act_spec on the GPU, checked against the oracle on `rows` (all rows when None); then
+    the trust backward of grad_spec fed the oracle's mask on those rows, checked on the same rows."""
     block = wl.block
-    log(f"{wl.name} fwd {act_spec.rows}x{act_spec.cols} b={b} (full size)")
+    n = act_spec.rows
+    rows = np.arange(n) if rows is None else rows
+    what = f"{len(rows)} of {n} rows"
+    log(f"{wl.name} fwd {act_spec.rows}x{act_spec.cols} b={b} (full size), checking {what}")
     x = make_tensor(act_spec, dev)
     codes, scale, mask = fwd_gpu(x, block, b)
-    rows = sample_rows(act_spec.rows, n_rows, seed)
-    x64 = np_rows(x, rows).astype(np.float64) if x.dtype == torch.float32 else to_float64(
-        x.index_select(0, torch.as_tensor(rows, device=dev))
-    )
-    ref = qo.quantize_fwd(x64, block, b)
-    st = check_fwd(x64, block, b, np_rows(codes, rows), np_rows(scale, rows), np_rows(mask, rows), ref=ref)
-    log(f"{wl.name} fwd sampled {len(rows)} rows ok {st}")
+    omask = torch.empty_like(mask) if grad_spec is not None else None
+    totals = {"exempt": 0, "mismatched": 0, "elements": 0, "scale_max_rel": 0.0}
+    for part in _chunks(rows):
+        x64 = _take(x, part)
+        ref = qo.quantize_fwd(x64, block, b)
+        st = check_fwd(x64, block, b, _take(codes, part), _take(scale, part), _take(mask, part), ref=ref,
+                       max_fraction=None)
+        for key in ("exempt", "mismatched", "elements"):
+            totals[key] += st[key]
+        totals["scale_max_rel"] = max(totals["scale_max_rel"], st["scale_max_rel"])
+        if omask is not None:
+            omask[torch.as_tensor(part, device=dev)] = torch.from_numpy(ref["mask"]).to(dev)
+    allowed = int(np.ceil(MAX_MISMATCH_FRACTION * totals["elements"]))
+    assert totals["mismatched"] <= allowed, f"{totals['mismatched']} in-band differences, {allowed} allowed"
+    log(f"{wl.name} fwd ok on {what}: {totals}")
     if grad_spec is None:
         return
-    del x, codes, scale
+    del x, codes, scale, mask
     g = make_tensor(grad_spec, dev)
-    # Oracle mask on the sampled rows, the GPU's own elsewhere (those rows are not compared).
-    mask[torch.as_tensor(rows, device=dev)] = torch.from_numpy(ref["mask"]).to(dev)
-    log(f"{wl.name} trust_bwd {grad_spec.rows}x{grad_spec.cols} (full size)")
-    out = qa.trust_bwd(g, mask, block)
+    if len(rows) < n:  # rows not compared keep a mask of their own (all ones)
+        keep = np.ones(n, dtype=bool)
+        keep[rows] = False
+        omask[torch.as_tensor(np.flatnonzero(keep), device=dev)] = 0xFF
+    log(f"{wl.name} trust_bwd {grad_spec.rows}x{grad_spec.cols} (full size), checking {what}")
+    out = qa.trust_bwd(g, omask, block)
     torch.cuda.synchronize()
-    g64 = to_float64(g.index_select(0, torch.as_tensor(rows, device=dev)))
-    expect = qo.trust_bwd(g64, ref["mask"], block)
     tol = TOL_BF16 if g.dtype == torch.bfloat16 else TOL_F32
-    ratio = check_grad(np_rows(out, rows).astype(np.float64) if out.dtype == torch.float32
-                       else to_float64(out.index_select(0, torch.as_tensor(rows, device=dev))), expect, block, tol)
-    log(f"{wl.name} trust_bwd sampled ok, max error / tolerance = {ratio:.3g}")
+    worst = 0.0
+    for part in _chunks(rows):
+        expect = qo.trust_bwd(_take(g, part), _take(omask, part), block)
+        worst = max(worst, check_grad(_take(out, part), expect, block, tol))
+    log(f"{wl.name} trust_bwd ok on {what}, max error / tolerance = {worst:.3g}")
 
 
 def test_headline_16384x2048_fwd_bwd(dev):
     wl = WORKLOADS["T"]
-    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 4, 384, 606)
+    _fwd_bwd_rows(dev, wl, wl.fwd[0], wl.grad[0], 4)
 
 
 def test_c3_weights_fwd(dev):
     wl = WORKLOADS["C3"]
-    for i, spec in enumerate(wl.fwd):
-        _fwd_bwd_sampled(dev, wl, spec, None, 4, 96, 300 + i)
+    for spec in wl.fwd:
+        _fwd_bwd_rows(dev, wl, spec, None, 4)
 
 
 def test_c4_trust_bwd(dev):
     wl = WORKLOADS["C4"]
-    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 4, 128, 404)
+    _fwd_bwd_rows(dev, wl, wl.fwd[0], wl.grad[0], 4)
 
 
 def test_c5_fwd_bwd(dev):
+    """131072 x 5632: 738 M entries, several minutes of oracle time in full, so a seeded eighth of
+    the rows (always including the first and the last) is checked."""
     wl = WORKLOADS["C5"]
-    _fwd_bwd_sampled(dev, wl, wl.fwd[0], wl.grad[0], 1, 48, 505)
+    _fwd_bwd_rows(dev, wl, wl.fwd[0], wl.grad[0], 1, sample_rows(wl.fwd[0].rows, 16384, 505))
 
 
 # ---------------------------------------------------------------------------
