@@ -107,15 +107,22 @@ void fill_alpha_table() {
   g_alpha_fp4 = solve_alpha_fp4();
 }
 
-// Forward kernel selection, read once per process: QUEST_FWD_KERNEL=valu keeps
-// bf16 rows of 512..2048 columns on the vector-ALU transform instead of the
-// matrix cores (same results up to fp32 rounding order; for A/B timing).
+// Kernel selection, read once per process: QUEST_FWD_KERNEL=valu keeps bf16
+// forwards of 512 or more columns, QUEST_BWD_KERNEL=valu bf16 backwards, on
+// the vector-ALU transform instead of the matrix cores (same results up to
+// fp32 rounding order; for A/B timing).
 std::once_flag g_env_once;
 bool g_allow_mfma = true;
+bool g_allow_mfma_bwd = true;
+
+bool env_is(const char* name, const char* value) {
+  const char* v = std::getenv(name);
+  return v && std::strcmp(v, value) == 0;
+}
 
 void read_env() {
-  const char* v = std::getenv("QUEST_FWD_KERNEL");
-  g_allow_mfma = !(v && std::strcmp(v, "valu") == 0);
+  g_allow_mfma = !env_is("QUEST_FWD_KERNEL", "valu");
+  g_allow_mfma_bwd = !env_is("QUEST_BWD_KERNEL", "valu");
 }
 
 // ----------------------------------------------------------------------------
@@ -371,8 +378,9 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
   const size_t nm = quest_mask_bytes(rows, cols);
   if (grad_out != grad && overlaps(grad, ng, grad_out, ng)) return QUEST_EINVAL;
   if (overlaps(grad_out, ng, mask, nm) || overlaps(grad, ng, mask, nm)) return QUEST_EINVAL;
+  std::call_once(g_env_once, read_env);
   return from_hip(quest::launch_trust_bwd(grad, g_dtype == QUEST_BF16, mask, rows, cols, lb, grad_out,
-                                          static_cast<hipStream_t>(stream)));
+                                          g_allow_mfma_bwd, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

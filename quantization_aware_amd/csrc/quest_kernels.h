@@ -873,6 +873,65 @@ __global__ void __launch_bounds__(256)
   wave_store_runs<U>(grad_out, run0 * U, total_runs * U, lane, stage, raw);
 }
 
+// The same for bf16 gradients on the matrix cores, in the layout of
+// quest_fwd_mfma_kernel: a wave's tile is 64 runs held as four 16-run groups,
+// lane (g, n) loading the 16 bytes at 64 n + 16 g of each group (elements
+// 8 g .. 8 g + 7 of run 16 j + n in slot j; one contiguous kilobyte per load
+// instruction).  Each lane loads the mask dword of run l, and the transpose
+// between lane quarters and slots hands slot j the mask of run 16 j + n.  The
+// untrusted entries are zeroed in the bf16 fragment (each bit sign-extended
+// over its half of a dword), H_32 is applied by two matrix instructions per
+// group and the cross-run stages by DPP; the outputs, scaled by tau/sqrt(n)
+// and narrowed to bf16, are stored in the pattern of the loads.  No LDS and
+// no in-lane butterflies.  Tiles may straddle rows (the transform is per
+// block, a block never straddles a 16-run group); a tile past the end of the
+// tensor reads zeros and its stores are dropped.  In place is allowed: each
+// tile is read and written by one wave, its loads before its stores.
+template <int LOGN>
+__global__ void __launch_bounds__(256)
+    quest_bwd_mfma_kernel(const uint16_t* grad, const uint32_t* mask, int64_t total_runs, uint16_t* grad_out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (tile * 64 >= total_runs) return;
+  const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
+  const rsrc_t g_r = window_at(grad, tile * 4096, total_runs * 64, 4096);
+  u32x4 f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(g_r, in_off + 1024 * j, 0, kNonTemporal);
+  const uint32_t m = __builtin_amdgcn_raw_buffer_load_b32(window_at(mask, tile * 256, total_runs * 4, 256), lane * 4,
+                                                          0, kNonTemporal);
+  const bf16x8_t h0 = hadamard_fragment(lane, 0);
+  const bf16x8_t h1 = hadamard_fragment(lane, 1);
+  uint32_t mq[4] = {m, m, m, m};
+  transpose_quarters(mq);  // slot j: the mask of run 16 j + n
+  const int shift = 8 * (lane >> 4);
+  float v[RUN];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bits = static_cast<int>(mq[j] >> shift);  // bit e: element 8 g + e of the run
+    const uint32_t d[4] = {f[j].x, f[j].y, f[j].z, f[j].w};
+    uint32_t md[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t keep_lo = static_cast<uint32_t>(__builtin_amdgcn_sbfe(bits, 2 * i, 1));
+      const uint32_t keep_hi = static_cast<uint32_t>(__builtin_amdgcn_sbfe(bits, 2 * i + 1, 1));
+      md[i] = d[i] & ((keep_lo & 0xFFFFu) | (keep_hi & 0xFFFF0000u));
+    }
+    mfma_run_outputs(h0, h1, u32x4{md[0], md[1], md[2], md[3]}, v + 8 * j);
+  }
+  const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
+  const float k = tau * BlockConst<LOGN>::rsqrt_n;
+  const rsrc_t o_r = window_at(grad_out, tile * 4096, total_runs * 64, 4096);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* w = v + 8 * j;
+    const u32x4 o = {pack_bf16x2(w[0] * k, w[1] * k), pack_bf16x2(w[2] * k, w[3] * k),
+                     pack_bf16x2(w[4] * k, w[5] * k), pack_bf16x2(w[6] * k, w[7] * k)};
+    __builtin_amdgcn_raw_buffer_store_b128(o, o_r, in_off + 1024 * j, 0, kNonTemporal);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Dequantise: one lane per run.
 // ----------------------------------------------------------------------------
@@ -1046,10 +1105,29 @@ hipError_t fwd_dispatch_block(const In* x, int log_block, int bits, const FwdLau
 
 template <typename G>
 hipError_t bwd_dispatch(const G* grad, const uint8_t* mask, int64_t rows, int64_t cols, int log_block, G* out,
-                        hipStream_t stream) {
+                        bool allow_mfma, hipStream_t stream) {
   const int64_t total_runs = rows * (cols / RUN);
   const int64_t grid = (total_runs + 255) / 256;
   const uint32_t* mask32 = reinterpret_cast<const uint32_t*>(mask);
+  if constexpr (sizeof(G) == 2) {
+    if (allow_mfma) {  // bf16: one 64-run tile per wave, four waves per workgroup
+      switch (log_block) {
+        case 6:
+          hipLaunchKernelGGL((quest_bwd_mfma_kernel<6>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                             grad, mask32, total_runs, out);
+          break;
+        case 7:
+          hipLaunchKernelGGL((quest_bwd_mfma_kernel<7>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                             grad, mask32, total_runs, out);
+          break;
+        default:
+          hipLaunchKernelGGL((quest_bwd_mfma_kernel<8>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                             grad, mask32, total_runs, out);
+          break;
+      }
+      return hipGetLastError();
+    }
+  }
   switch (log_block) {
     case 6:
       hipLaunchKernelGGL((quest_bwd_kernel<G, 6>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, grad,

@@ -34,8 +34,10 @@ hipError_t launch_fwd_op(const void* x, int x_is_bf16, int log_block, int bits, 
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
                              void* out, int out_is_bf16, hipStream_t stream);
 
+// allow_mfma: bf16 gradients use the matrix-core transform (fp32 ones always
+// the vector-ALU one).
 hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
-                            int log_block, void* grad_out, hipStream_t stream);
+                            int log_block, void* grad_out, bool allow_mfma, hipStream_t stream);
 
 // Arguments of one product of two matrix-core operands, already validated:
 // out (m x n, row-major) = Delta_a Delta_b * (A B^T) with Delta = scale * k*.

@@ -21,12 +21,12 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t r
 }
 
 hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
-                            int log_block, void* grad_out, hipStream_t stream) {
+                            int log_block, void* grad_out, bool allow_mfma, hipStream_t stream) {
   if (g_is_bf16)
     return bwd_dispatch(static_cast<const uint16_t*>(grad), mask, rows, cols, log_block,
-                        static_cast<uint16_t*>(grad_out), stream);
+                        static_cast<uint16_t*>(grad_out), allow_mfma, stream);
   return bwd_dispatch(static_cast<const float*>(grad), mask, rows, cols, log_block, static_cast<float*>(grad_out),
-                      stream);
+                      false, stream);
 }
 
 }  // namespace quest
