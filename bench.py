@@ -629,7 +629,7 @@ def main():
     kernels = {
         "quest_fwd_mfma_kernel<7,4,6>": {"avg_us": 1000 * fwd_avg, "alg_bytes": fwd_bytes,
                                          "gbps": fwd_bytes / (fwd_avg * 1e6)},
-        "quest_bwd_kernel<bf16,7>": {"avg_us": 1000 * bwd_avg, "alg_bytes": bwd_bytes,
+        "quest_bwd_mfma_kernel<7>": {"avg_us": 1000 * bwd_avg, "alg_bytes": bwd_bytes,
                                      "gbps": bwd_bytes / (bwd_avg * 1e6)},
     }
     for v in kernels.values():

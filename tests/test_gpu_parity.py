@@ -451,6 +451,48 @@ def test_valu_switch_matches_oracle_and_mfma(dev, tmp_path, cols, block, b):
     assert np.array_equal(u_valu[~ex], u_mfma[~ex])
 
 
+_VALU_BWD_CHILD = r"""
+import sys
+import numpy as np
+import torch
+sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
+import quantization_aware_amd as qa
+from quest_inputs import TensorSpec, make_tensor
+dev = torch.device("cuda", 0)
+rows, cols, block = int(sys.argv[2]), int(sys.argv[3]), int(sys.argv[4])
+g = make_tensor(TensorSpec("valu.g", rows, cols, "bf16", "normal", 1e-3, 8200), dev)
+mask = torch.from_numpy(np.load(sys.argv[5])).to(dev)
+out = qa.trust_bwd(g, mask, block)
+torch.cuda.synchronize()
+np.save(sys.argv[6], out.float().cpu().numpy())
+"""
+
+
+@pytest.mark.parametrize("rows,cols,block", [(96, 2048, 128), (33, 512, 64), (17, 5632, 256)])
+def test_valu_bwd_switch_matches_oracle_and_mfma(dev, tmp_path, rows, cols, block):
+    """QUEST_BWD_KERNEL=valu keeps bf16 gradients on the run-per-lane kernel: it matches the oracle,
+    and the matrix-core kernel's result to bf16 rounding of the same sums."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    rng = np.random.default_rng(8300 + cols)
+    mask = rng.integers(0, 256, size=(rows, cols // 8), dtype=np.uint8)
+    np.save(tmp_path / "mask.npy", mask)
+    log(f"vector-ALU backward in a child process, {rows}x{cols} bf16 block {block}")
+    subprocess.run([sys.executable, "-c", _VALU_BWD_CHILD, root, str(rows), str(cols), str(block),
+                    str(tmp_path / "mask.npy"), str(tmp_path / "out.npy")],
+                   env=dict(os.environ, QUEST_BWD_KERNEL="valu"), check=True, timeout=300)
+    got_valu = np.load(tmp_path / "out.npy").astype(np.float64)
+    g = make_tensor(TensorSpec("valu.g", rows, cols, "bf16", "normal", 1e-3, 8200), dev)
+    expect = qo.trust_bwd(to_float64(g), mask, block)
+    check_grad(got_valu, expect, block, TOL_BF16)
+    got_mfma = to_float64(qa.trust_bwd(g, torch.from_numpy(mask).to(dev), block))
+    check_grad(got_mfma, expect, block, TOL_BF16)
+    check_grad(got_mfma, got_valu, block, 2.0 ** -7)  # two bf16 roundings of fp32 sums apart at most
+
+
 # ---------------------------------------------------------------------------
 # Forward that also writes the dequantised tensor (quest_quantize_fwd_dq):
 # codes, scale and mask equal quest_quantize_fwd's bit for bit, dq equals
