@@ -250,7 +250,23 @@ def config_runs(lib, qa, torch, dev, reps, names):
             for c in calls[i]:
                 c()
 
-        rec = {"workload": wl.description, "all_seven": entry(timed(all_seven, n), alg, sum(w.numel() for w in ws)),
+        descs = []
+        for one in sets:
+            d = (qa._FwdTensor * len(one))()
+            for j, (x, cd, sc, mk) in enumerate(one):
+                d[j] = qa._FwdTensor(x.data_ptr(), x.shape[0], x.shape[1], cd.data_ptr(), sc.data_ptr(), mk.data_ptr())
+            descs.append(d)
+        f_group = lib.quest_quantize_fwd_group
+
+        def grouped(i):
+            check("quest_quantize_fwd_group", f_group(descs[i], len(ws), qa.QUEST_BF16, wl.block, 4, sh))
+
+        elements = sum(w.numel() for w in ws)
+        rec = {"workload": wl.description,
+               "grouped": entry(timed(grouped, n), alg, elements),
+               "all_seven": entry(timed(all_seven, n), alg, elements),
+               "note": "grouped: one quest_quantize_fwd_group call (q, k, v, o, gate, up share one launch; down, "
+                       "5632 columns, its own); all_seven: seven quest_quantize_fwd calls",
                "buffer_sets": n, "per_tensor_us": {}}
         for j, spec in enumerate(wl.fwd):
             rec["per_tensor_us"][spec.name.split(".")[1]] = round(timed(lambda i: calls[i][j](), n), 3)

@@ -119,6 +119,40 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
                                 int b, uint8_t* codes, float* scale, uint8_t* mask, void* stream);
 
 /*
+ * The forward of quest_quantize_fwd on several tensors in one call: the
+ * outputs are those of calling quest_quantize_fwd on each tensor in turn
+ * (same block, bit width and input dtype), bit for bit.  A quantisation-aware
+ * training step quantises every weight of a model (pith.science review of
+ * QuEST, "What carries the argument": the quantiser is applied to weights and
+ * activations in every forward pass); the library launches the bf16 tensors
+ * whose rows have 512, 1024 or 2048 entries (b <= 4) together, one launch
+ * per width for up to eight tensors, and the others one by one.
+ *
+ *   tensors  host array of `count` descriptors, read during the call only;
+ *            each names x, rows, cols, codes, scale and mask as the
+ *            arguments of quest_quantize_fwd (a tensor with rows == 0 is
+ *            skipped and its pointers are not read)
+ *   count    >= 0 (0: nothing is done)
+ *   x_dtype, block, b, stream: as for quest_quantize_fwd, for every tensor
+ * Errors: everything quest_quantize_fwd rejects for any tensor, with the
+ * same status; count < 0 or tensors NULL with count > 0 is QUEST_EINVAL; an
+ * output of one tensor overlapping an input or output of another is
+ * QUEST_EINVAL (inputs may overlap each other).  Validation covers every
+ * tensor before the first launch, so on error nothing is written.
+ */
+typedef struct {
+  const void* x;
+  int64_t rows;
+  int64_t cols;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* mask;
+} quest_fwd_tensor;
+
+quest_status quest_quantize_fwd_group(const quest_fwd_tensor* tensors, int count, quest_dtype x_dtype, int block,
+                                      int b, void* stream);
+
+/*
  * Forward quantisation that also writes the dequantised ("fake-quantised")
  * tensor, in one pass over x: everything quest_quantize_fwd computes, plus
  *   dq[r, c] = (2 u[r, c] - L + 1) * s_r / (L - 1)   (Hadamard domain),

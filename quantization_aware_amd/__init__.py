@@ -21,6 +21,7 @@ __all__ = [
     "codes_bytes",
     "mask_bytes",
     "quantize_fwd",
+    "quantize_fwd_group",
     "quantize_fwd_dq",
     "quantize_fwd_ex",
     "quantize_fwd_op",
@@ -45,6 +46,7 @@ QUEST_F32, QUEST_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "quest_fit_alpha",
     "quest_quantize_fwd",
+    "quest_quantize_fwd_group",
     "quest_quantize_fwd_dq",
     "quest_quantize_fwd_ex",
     "quest_quantize_fwd_op",
@@ -76,6 +78,13 @@ class QuestError(RuntimeError):
 _lib = None
 
 
+class _FwdTensor(ctypes.Structure):
+    """quest_fwd_tensor of include/quest.h."""
+
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libquest.so (once) and declare the C signatures."""
     global _lib
@@ -92,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_fit_alpha.restype = ctypes.c_double
     lib.quest_quantize_fwd.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp]
     lib.quest_quantize_fwd.restype = c_int
+    lib.quest_quantize_fwd_group.argtypes = [ctypes.POINTER(_FwdTensor), c_int, c_int, c_int, c_int, vp]
+    lib.quest_quantize_fwd_group.restype = c_int
     lib.quest_quantize_fwd_dq.argtypes = [vp, c_int, i64, i64, c_int, c_int, vp, vp, vp, vp, c_int, vp]
     lib.quest_quantize_fwd_dq.restype = c_int
     lib.quest_quantize_fwd_ex.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp, c_int, vp]
@@ -223,6 +234,36 @@ def quantize_fwd(x: torch.Tensor, block: int, b: int, codes=None, scale=None, ma
     )
     _check("quest_quantize_fwd", st)
     return codes, scale, mask
+
+
+def quantize_fwd_group(xs, block: int, b: int, stream=None):
+    """quantize_fwd of several 2-D tensors of one dtype and device in one call (quest_quantize_fwd_group).
+
+    Returns a list of (codes, scale, mask), one per tensor, equal to what
+    quantize_fwd returns for each.  Tensors of 512, 1024 or 2048 bf16 columns
+    (b <= 4) share launches.
+    """
+    lib = load_library()
+    xs = list(xs)
+    if not xs:
+        return []
+    outs, descs = [], (_FwdTensor * len(xs))()
+    for i, x in enumerate(xs):
+        _device_tensor(f"xs[{i}]", x)
+        if x.dim() != 2:
+            raise ValueError(f"xs[{i}] must be 2-D (rows x cols)")
+        if x.dtype != xs[0].dtype or x.device != xs[0].device:
+            raise ValueError("every tensor of a group must share the first one's dtype and device")
+        rows, cols = x.shape
+        codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=x.device)
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+        mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=x.device)
+        outs.append((codes, scale, mask))
+        descs[i] = _FwdTensor(x.data_ptr(), rows, cols, codes.data_ptr(), scale.data_ptr(), mask.data_ptr())
+    st = lib.quest_quantize_fwd_group(descs, len(xs), _dtype_code(xs[0]), int(block), int(b),
+                                      _stream_handle(xs[0].device, stream))
+    _check("quest_quantize_fwd_group", st)
+    return outs
 
 
 def quantize_fwd_dq(x: torch.Tensor, block: int, b: int, dq_dtype=torch.bfloat16, with_codes: bool = True,

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <limits>
 #include <mutex>
+#include <vector>
 
 #include "../../include/quest.h"
 #include "quest_launch.h"
@@ -162,6 +163,10 @@ quest_status check_shape(int64_t rows, int64_t cols, int multiple_of) {
 
 quest_status from_hip(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_EHIP; }
 
+// The argument checks of quantize_fwd_common, without the launch.
+quest_status check_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b, double trust,
+                       uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, bool mask_required, void* dq,
+                       quest_dtype dq_dtype, bool dq_required, uint8_t* operand);
 // Forward with codes (null allowed unless codes_required), an optional
 // dequantised output (null allowed unless dq_required; dq_dtype is checked
 // only when dq is given) and the outer trust factor.  Checks every argument
@@ -222,6 +227,65 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
                                 uint8_t* codes, float* scale, uint8_t* mask, void* stream) {
   return quantize_fwd_common(x, x_dtype, rows, cols, block, b, 1.0, codes, true, scale, mask, true, nullptr,
                              QUEST_BF16, false, nullptr, stream);
+}
+
+quest_status quest_quantize_fwd_group(const quest_fwd_tensor* tensors, int count, quest_dtype x_dtype, int block,
+                                      int b, void* stream) {
+  if (count < 0 || (count > 0 && !tensors)) return QUEST_EINVAL;
+  // Every tensor as quest_quantize_fwd would check it ...
+  for (int i = 0; i < count; ++i) {
+    const quest_fwd_tensor& t = tensors[i];
+    const quest_status st = check_fwd(t.x, x_dtype, t.rows, t.cols, block, b, 1.0, t.codes, true, t.scale, t.mask,
+                                      true, nullptr, QUEST_BF16, false, nullptr);
+    if (st != QUEST_OK) return st;
+  }
+  // ... and no output of one tensor on an input or output of another.
+  auto spans = [&](const quest_fwd_tensor& t, size_t (&n)[4]) {
+    n[0] = static_cast<size_t>(t.rows * t.cols) * dtype_size(x_dtype);
+    n[1] = quest_codes_bytes(t.rows, t.cols, b);
+    n[2] = static_cast<size_t>(t.rows) * sizeof(float);
+    n[3] = quest_mask_bytes(t.rows, t.cols);
+  };
+  for (int i = 0; i < count; ++i) {
+    if (tensors[i].rows == 0) continue;
+    size_t ni[4];
+    spans(tensors[i], ni);
+    const void* bi[4] = {tensors[i].x, tensors[i].codes, tensors[i].scale, tensors[i].mask};
+    for (int j = i + 1; j < count; ++j) {
+      if (tensors[j].rows == 0) continue;
+      size_t nj[4];
+      spans(tensors[j], nj);
+      const void* bj[4] = {tensors[j].x, tensors[j].codes, tensors[j].scale, tensors[j].mask};
+      for (int p = 0; p < 4; ++p)
+        for (int q = 0; q < 4; ++q)
+          if ((p > 0 || q > 0) && overlaps(bi[p], ni[p], bj[q], nj[q])) return QUEST_EINVAL;
+    }
+  }
+  std::call_once(g_env_once, read_env);
+  const int lb = log2_block(block);
+  const double alpha = quest_fit_alpha(b);
+  // bf16 rows of 512, 1024 or 2048 entries (b <= 4) go in grouped launches,
+  // one per width; everything else as quest_quantize_fwd.
+  std::vector<quest::FwdGroupItem> group[3];
+  for (int i = 0; i < count; ++i) {
+    const quest_fwd_tensor& t = tensors[i];
+    if (t.rows == 0) continue;
+    const int w = t.cols == 512 ? 0 : t.cols == 1024 ? 1 : t.cols == 2048 ? 2 : -1;
+    if (x_dtype == QUEST_BF16 && b <= 4 && g_allow_mfma && w >= 0) {
+      group[w].push_back({t.x, t.rows, t.codes, t.scale, t.mask});
+    } else {
+      const quest_status st = quantize_fwd_common(t.x, x_dtype, t.rows, t.cols, block, b, 1.0, t.codes, true, t.scale,
+                                                  t.mask, true, nullptr, QUEST_BF16, false, nullptr, stream);
+      if (st != QUEST_OK) return st;
+    }
+  }
+  for (int w = 0; w < 3; ++w) {
+    if (group[w].empty()) continue;
+    const hipError_t e = quest::launch_fwd_group(group[w].data(), static_cast<int>(group[w].size()), 512 << w, lb, b,
+                                                 alpha, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return QUEST_EHIP;
+  }
+  return QUEST_OK;
 }
 
 quest_status quest_quantize_fwd_dq(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
@@ -387,10 +451,11 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
 
 namespace {
 
-quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
-                                 double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
-                                 bool mask_required, void* dq, quest_dtype dq_dtype, bool dq_required,
-                                 uint8_t* operand, void* stream) {
+// The argument checks of the forward entry points (QUEST_OK also for rows == 0,
+// which launches nothing).
+quest_status check_fwd(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b, double trust,
+                       uint8_t* codes, bool codes_required, float* scale, uint8_t* mask, bool mask_required, void* dq,
+                       quest_dtype dq_dtype, bool dq_required, uint8_t* operand) {
   const int lb = log2_block(block);
   if (lb < 0 || b < 1 || b > kMaxBits) return QUEST_EUNSUPPORTED;
   if (operand && (b > 4 || cols % 128 != 0)) return QUEST_EUNSUPPORTED;
@@ -416,6 +481,17 @@ quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t row
       overlaps(dq, nd, mask, nm) || overlaps(operand, no, x, nx) || overlaps(operand, no, codes, nc) ||
       overlaps(operand, no, scale, ns) || overlaps(operand, no, mask, nm))
     return QUEST_EINVAL;
+  return QUEST_OK;
+}
+
+quest_status quantize_fwd_common(const void* x, quest_dtype x_dtype, int64_t rows, int64_t cols, int block, int b,
+                                 double trust, uint8_t* codes, bool codes_required, float* scale, uint8_t* mask,
+                                 bool mask_required, void* dq, quest_dtype dq_dtype, bool dq_required,
+                                 uint8_t* operand, void* stream) {
+  const quest_status st = check_fwd(x, x_dtype, rows, cols, block, b, trust, codes, codes_required, scale, mask,
+                                    mask_required, dq, dq_dtype, dq_required, operand);
+  if (st != QUEST_OK || rows == 0) return st;
+  const int lb = log2_block(block);
   std::call_once(g_env_once, read_env);
   quest::FwdLaunch a;
   a.rows = rows;

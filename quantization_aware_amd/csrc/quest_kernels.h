@@ -561,23 +561,14 @@ __device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float
 // a grid-stride loop with its loads one to three tiles ahead.
 // kQuant = false (operand calls without codes and mask) leaves the codes and
 // mask work out of the build.
-template <int LOGN, int B, int LOGR, typename Dq, bool kQuant = true>
-__global__ void __launch_bounds__(256)
-    quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
-                          uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask,
-                          Dq* __restrict__ dq) {
+template <int LOGN, int B, int LOGR, typename Dq, bool kQuant>
+__device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, int64_t total_runs, const FwdConsts& k,
+                                              uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                              uint32_t* __restrict__ mask, Dq* __restrict__ dq, int64_t tile, int lane,
+                                              int wave, uint8_t* opstage) {
   static_assert(LOGR >= 4 && LOGR <= 6, "16, 32 or 64 runs per row");
   constexpr int ROWS = 64 >> LOGR;  // rows per tile
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t rows = total_runs >> LOGR;
-  const int64_t tiles = (total_runs + 63) >> 6;
-  const int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
-  // The operand is staged per workgroup (a barrier), so all four waves of
-  // the last workgroup run: a wave past the last tile computes on zeros and
-  // every store it makes is dropped or lands in padding.
-  if (!kIsOperand<Dq> && tile >= tiles) return;
-  __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
   const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
@@ -654,6 +645,69 @@ __global__ void __launch_bounds__(256)
   u32x4 f[4];
   fetch(tile, f);
   process(tile, f);
+}
+
+template <int LOGN, int B, int LOGR, typename Dq, bool kQuant = true>
+__global__ void __launch_bounds__(256)
+    quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
+                          uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask,
+                          Dq* __restrict__ dq) {
+  constexpr int ROWS = 64 >> LOGR;  // rows per tile
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t tiles = (total_runs + 63) >> 6;
+  const int64_t tile = fwd_wg_index<Dq>() * 4 + wave;
+  // The operand is staged per workgroup (a barrier), so all four waves of
+  // the last workgroup run: a wave past the last tile computes on zeros and
+  // every store it makes is dropped or lands in padding.
+  if (!kIsOperand<Dq> && tile >= tiles) return;
+  __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
+  fwd_mfma_tile<LOGN, B, LOGR, Dq, kQuant>(x, total_runs, k, codes, scale, mask, dq, tile, lane, wave, opstage);
+}
+
+// Several tensors of one width in one launch (quest_quantize_fwd_group):
+// each tensor's tiles follow the previous tensor's, and a wave finds its
+// tensor by comparing its tile with the running tile counts (a scan over
+// compile-time indices, so the table stays in scalar registers).  Per
+// tensor the work is quest_fwd_mfma_kernel's; a workgroup may span two
+// tensors (no barrier in this path).
+constexpr int kFwdGroupMax = 8;
+
+struct FwdGroup {
+  int count;                               // tensors in this launch, 1 .. kFwdGroupMax
+  int64_t first_tile[kFwdGroupMax + 1];    // running tile counts; first_tile[count] = all tiles
+  int64_t total_runs[kFwdGroupMax];
+  const uint16_t* x[kFwdGroupMax];
+  uint8_t* codes[kFwdGroupMax];
+  float* scale[kFwdGroupMax];
+  uint32_t* mask[kFwdGroupMax];
+};
+
+template <int LOGN, int B, int LOGR>
+__global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, FwdConsts k) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const uint16_t* x = g.x[0];
+  uint8_t* codes = g.codes[0];
+  float* scale = g.scale[0];
+  uint32_t* mask = g.mask[0];
+  int64_t runs = g.total_runs[0], first = 0, end = g.first_tile[1];
+#pragma unroll
+  for (int i = 1; i < kFwdGroupMax; ++i) {
+    if (i < g.count && tile >= g.first_tile[i]) {
+      x = g.x[i];
+      codes = g.codes[i];
+      scale = g.scale[i];
+      mask = g.mask[i];
+      runs = g.total_runs[i];
+      first = g.first_tile[i];
+      end = g.first_tile[i + 1];
+    }
+  }
+  if (tile >= end) return;
+  fwd_mfma_tile<LOGN, B, LOGR, void, true>(x, runs, k, codes, scale, mask, nullptr, tile - first, lane, wave,
+                                           nullptr);
 }
 
 // bf16 rows of 16 m runs (m > 4: more than 2048 columns, a multiple of 512)
@@ -987,18 +1041,45 @@ constexpr int64_t kFwdTileWorkgroups = 512;
 
 
 
+// Per-launch constants of the forward kernels for rows of `cols` entries.
+template <int LOGN, int B>
+FwdConsts fwd_consts(double alpha, double trust, int64_t cols) {
+  const double L = double(1 << B), sqrt_n = std::sqrt(double(1 << LOGN));
+  FwdConsts k;
+  k.alpha = static_cast<float>(alpha);
+  k.kk = static_cast<float>((L - 1.0) / (2.0 * alpha * sqrt_n));
+  // Trusted: |y| <= s + trust * Delta / 2, i.e. |v| <= alpha sqrt(n) (1 + trust / (L - 1)) RMS.
+  k.thr = static_cast<float>(alpha * sqrt_n * (1.0 + trust / (L - 1.0)));
+  k.inv_cols = static_cast<float>(1.0 / double(cols));
+  k.chunks = static_cast<int>(cols / 128);
+  return k;
+}
+
+// One grouped launch: every tensor of `g` has rows of `cols` entries, cols
+// 512, 1024 or 2048 (16, 32 or 64 runs), bf16, b <= 4.
+template <int LOGN, int B>
+hipError_t fwd_group_dispatch(const FwdGroup& g, int64_t cols, double alpha, hipStream_t stream) {
+  const FwdConsts k = fwd_consts<LOGN, B>(alpha, 1.0, cols);
+  const dim3 grid(static_cast<uint32_t>((g.first_tile[g.count] + 3) / 4));
+  switch (cols / RUN) {
+    case 16:
+      hipLaunchKernelGGL((quest_fwd_mfma_group_kernel<LOGN, B, 4>), grid, dim3(256), 0, stream, g, k);
+      break;
+    case 32:
+      hipLaunchKernelGGL((quest_fwd_mfma_group_kernel<LOGN, B, 5>), grid, dim3(256), 0, stream, g, k);
+      break;
+    default:
+      hipLaunchKernelGGL((quest_fwd_mfma_group_kernel<LOGN, B, 6>), grid, dim3(256), 0, stream, g, k);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <typename In, int LOGN, int B, typename Dq>
 hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
   const int64_t rows = a.rows;
   const int runs_per_row = static_cast<int>(a.cols / RUN);
-  const double L = double(1 << B), sqrt_n = std::sqrt(double(1 << LOGN));
-  FwdConsts k;
-  k.alpha = static_cast<float>(a.alpha);
-  k.kk = static_cast<float>((L - 1.0) / (2.0 * a.alpha * sqrt_n));
-  // Trusted: |y| <= s + trust * Delta / 2, i.e. |v| <= alpha sqrt(n) (1 + trust / (L - 1)) RMS.
-  k.thr = static_cast<float>(a.alpha * sqrt_n * (1.0 + a.trust / (L - 1.0)));
-  k.inv_cols = static_cast<float>(1.0 / double(a.cols));
-  k.chunks = static_cast<int>(a.cols / 128);
+  const FwdConsts k = fwd_consts<LOGN, B>(a.alpha, a.trust, a.cols);
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(a.mask);
   Dq* dq = static_cast<Dq*>(a.dq);
   hipStream_t stream = a.stream;

@@ -31,6 +31,21 @@ hipError_t launch_fwd_dq_bf16(const void* x, int x_is_bf16, int log_block, int b
 hipError_t launch_fwd_dq_f32(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 hipError_t launch_fwd_op(const void* x, int x_is_bf16, int log_block, int bits, const FwdLaunch& a);
 
+// One tensor of a grouped forward (quest_quantize_fwd_group).
+struct FwdGroupItem {
+  const void* x;  // bf16
+  int64_t rows;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* mask;
+};
+
+// The forward (trust 1) of `count` bf16 tensors whose rows all have `cols`
+// entries, cols 512, 1024 or 2048, bits <= 4, in launches of at most eight
+// tensors; rows >= 1 for every item.  All arguments already validated.
+hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, int log_block, int bits, double alpha,
+                            hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
                              void* out, int out_is_bf16, hipStream_t stream);
 

@@ -140,6 +140,67 @@ def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
 
 
+# A second tensor's buffers, apart from the first one's (fake addresses, never dereferenced).
+E_, F_, G_, H_ = 0x70000000, 0x78000000, 0x7C000000, 0x7E000000
+
+
+def group(lib, items, dt=qa.QUEST_BF16, block=128, b=4, count=None):
+    descs = (qa._FwdTensor * max(len(items), 1))()
+    for i, it in enumerate(items):
+        descs[i] = qa._FwdTensor(it.get("x"), it.get("rows", 4), it.get("cols", 256), it.get("codes"),
+                                 it.get("scale"), it.get("mask"))
+    return lib.quest_quantize_fwd_group(descs, len(items) if count is None else count, dt, block, b, None)
+
+
+GOOD = dict(x=E_, codes=F_, scale=G_, mask=H_)
+
+
+def test_group_empty_calls_are_noops(lib):
+    assert group(lib, []) == qa.QUEST_OK
+    assert lib.quest_quantize_fwd_group(None, 0, qa.QUEST_BF16, 128, 4, None) == qa.QUEST_OK
+    assert group(lib, [dict(rows=0), dict(rows=0, cols=2048)]) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize("kw,status", [(kw, st) for kw, st in test_fwd_rejects.pytestmark[0].args[1]
+                                       if not {"dt", "block", "b"} & set(kw)])
+def test_group_rejects_what_fwd_rejects(lib, kw, status):
+    """A bad tensor anywhere in a group gives quest_quantize_fwd's status for it; nothing launches."""
+    bad = dict(x=A, codes=B_, scale=C_, mask=D_, rows=4, cols=256)
+    bad.update(kw)
+    assert group(lib, [dict(GOOD), bad]) == status
+    assert group(lib, [bad, dict(GOOD)]) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(block=32), qa.QUEST_EUNSUPPORTED), (dict(b=9), qa.QUEST_EUNSUPPORTED),
+                                       (dict(dt=7), qa.QUEST_EINVAL)])
+def test_group_rejects_bad_common_arguments(lib, kw, status):
+    assert group(lib, [dict(GOOD)], **kw) == status
+
+
+def test_group_rejects_bad_counts(lib):
+    assert group(lib, [dict(GOOD)], count=-1) == qa.QUEST_EINVAL
+    assert lib.quest_quantize_fwd_group(None, 2, qa.QUEST_BF16, 128, 4, None) == qa.QUEST_EINVAL
+
+
+@pytest.mark.parametrize("second", [
+    dict(x=E_, codes=B_, scale=G_, mask=H_),  # codes of the second on the first's codes
+    dict(x=E_, codes=A, scale=G_, mask=H_),  # codes of the second inside the first's input
+    dict(x=E_, codes=F_, scale=D_, mask=H_),  # scale of the second on the first's mask
+    dict(x=B_, codes=F_, scale=G_, mask=H_),  # input of the second on the first's codes
+])
+def test_group_rejects_outputs_across_tensors(lib, second):
+    first = dict(x=A, codes=B_, scale=C_, mask=D_)
+    assert group(lib, [first, dict(second, rows=4, cols=256)]) == qa.QUEST_EINVAL
+
+
+def test_group_shared_input_and_rows_zero_pointers_unread(lib):
+    """Inputs may overlap; a rows == 0 tensor's pointers are not read, so a group whose other
+    tensor is invalid still fails on that one (and a misaligned pointer of a skipped tensor does not)."""
+    first = dict(x=A, codes=B_, scale=C_, mask=D_)
+    assert group(lib, [first, dict(x=A, codes=F_, scale=G_, mask=H_ + 1)]) == qa.QUEST_EALIGN
+    assert group(lib, [dict(x=A + 1, rows=0), dict(first, codes=None)]) == qa.QUEST_EINVAL
+
+
 def test_fwd_outputs_just_past_input_are_accepted_by_checks(lib):
     # x (4 x 256 bf16 = 2048 bytes) ends where codes begin: no overlap.  The call would then
     # launch, so only the overlap predicate is exercised here, through an invalid block size.

@@ -494,6 +494,50 @@ def test_valu_bwd_switch_matches_oracle_and_mfma(dev, tmp_path, rows, cols, bloc
 
 
 # ---------------------------------------------------------------------------
+# Grouped forward (quest_quantize_fwd_group): every tensor's codes, scale and
+# mask equal quest_quantize_fwd's bit for bit, whether it shares a launch
+# (bf16, 512 / 1024 / 2048 columns, b <= 4) or takes its own.
+# ---------------------------------------------------------------------------
+GROUP_SHAPES = [(2048, 2048), (77, 2048), (1, 2048), (300, 512), (5, 512), (129, 1024), (96, 5632), (33, 256),
+                (2048, 1024), (3, 2048), (64, 2048), (1000, 512), (0, 2048), (17, 640)]
+
+
+@pytest.mark.parametrize("dt,b,block", [("bf16", 4, 128), ("bf16", 1, 64), ("bf16", 3, 256), ("f32", 4, 128),
+                                        ("bf16", 6, 128)])
+def test_group_equals_single_calls(dev, dt, b, block):
+    shapes = [(r, c) for r, c in GROUP_SHAPES if c % block == 0]
+    xs = [make_tensor(TensorSpec(f"grp{i}", r, c, dt, "student_t", 4, 8500 + i, outlier_cols=min(4, c // 64),
+                                 outlier_scale=20.0), dev) for i, (r, c) in enumerate(shapes)]
+    log(f"group of {len(xs)} {dt} tensors, b={b}, block {block}")
+    got = qa.quantize_fwd_group(xs, block, b)
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        if x.shape[0] == 0:
+            continue
+        ref = qa.quantize_fwd(x, block, b)
+        torch.cuda.synchronize()
+        for name, g_, r_ in zip(("codes", "scale", "mask"), got[i], ref):
+            assert torch.equal(g_, r_), f"tensor {i} {tuple(x.shape)}: {name} differs from quest_quantize_fwd"
+    # and against the oracle on two of them
+    for i in (1, 3):
+        x64 = to_float64(xs[i]) if dt == "bf16" else xs[i].cpu().numpy().astype(np.float64)
+        c, sc, m = (t.cpu().numpy() for t in got[i])
+        check_fwd(x64, block, b, c, sc, m)
+
+
+def test_group_c3_weights_equal_single_calls(dev):
+    """The seven weight tensors of a 1.6B-scale block (C3) in one call: six share one launch, down
+    (5632 columns) takes its own; all equal the per-tensor forward bit for bit."""
+    wl = WORKLOADS["C3"]
+    ws = [make_tensor(spec, dev) for spec in wl.fwd]
+    got = qa.quantize_fwd_group(ws, wl.block, 4)
+    for w, g_ in zip(ws, got):
+        ref = qa.quantize_fwd(w, wl.block, 4)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(g_, ref))
+
+
+# ---------------------------------------------------------------------------
 # Forward that also writes the dequantised tensor (quest_quantize_fwd_dq):
 # codes, scale and mask equal quest_quantize_fwd's bit for bit, dq equals
 # quest_dequantize of those codes bit for bit, and both match the oracle.
