@@ -268,6 +268,26 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
 size_t quest_operand_bytes(int64_t rows, int64_t cols);
 
 /*
+ * The operand of stored codes: the tiled FP6 operand that
+ * quest_quantize_fwd_op writes for the same codes, built from packed b-bit
+ * codes (quest_quantize_fwd's layout), so that codes kept at b bits per
+ * entry (a frozen layer's weight, for instance) can feed quest_gemm.  The
+ * pages time QuEST's 4-bit layer products (pith.science review of QuEST,
+ * Figure 5 caption); gfx950 multiplies them as FP6 (see the operand above),
+ * and this is the step from the stored codes to that type.
+ *   codes    device, quest_codes_bytes(rows, cols, b) bytes
+ *   rows     >= 0;  cols a positive multiple of 128 (QUEST_EINVAL
+ *            otherwise), at most QUEST_MAX_COLS
+ *   b        1 .. 4 (QUEST_EUNSUPPORTED otherwise)
+ *   operand  device output, quest_operand_bytes(rows, cols) bytes; the
+ *            padding rows of the last 32-row block are not written
+ * 16-byte aligned pointers (QUEST_EALIGN); the operand may not overlap the
+ * codes (QUEST_EINVAL).  Asynchronous on `stream`.
+ */
+quest_status quest_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int b, uint8_t* operand,
+                                    void* stream);
+
+/*
  * Forward writing the matrix-core operand: the quantiser of
  * quest_quantize_fwd_ex, whose levels go to `operand` instead of a
  * dequantised tensor.  Codes and mask are optional (an inference forward

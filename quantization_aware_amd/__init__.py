@@ -26,6 +26,7 @@ __all__ = [
     "quantize_fwd_ex",
     "quantize_fwd_op",
     "operand_bytes",
+    "codes_to_operand",
     "gemm",
     "quantize_fwd_fp4",
     "quantize_fwd_sparse24",
@@ -52,6 +53,7 @@ EXPORTED_SYMBOLS = (
     "quest_quantize_fwd_op",
     "quest_gemm",
     "quest_operand_bytes",
+    "quest_codes_to_operand",
     "quest_fit_alpha_fp4",
     "quest_quantize_fwd_fp4",
     "quest_quantize_fwd_sparse24",
@@ -111,6 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_quantize_fwd_op.restype = c_int
     lib.quest_gemm.argtypes = [vp, vp, i64, c_int, vp, vp, i64, c_int, i64, vp, c_int, vp]
     lib.quest_gemm.restype = c_int
+    lib.quest_codes_to_operand.argtypes = [vp, i64, i64, c_int, vp, vp]
+    lib.quest_codes_to_operand.restype = c_int
     lib.quest_operand_bytes.argtypes = [i64, i64]
     lib.quest_operand_bytes.restype = ctypes.c_size_t
     lib.quest_fit_alpha_fp4.argtypes = []
@@ -370,6 +374,21 @@ def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
     )
     _check("quest_quantize_fwd_op", st)
     return codes, scale, mask, operand
+
+
+def codes_to_operand(codes: torch.Tensor, rows: int, cols: int, b: int, operand=None, stream=None) -> torch.Tensor:
+    """The matrix-core operand of packed b-bit codes (quest_codes_to_operand), b <= 4."""
+    lib = load_library()
+    rows, cols, b = int(rows), int(cols), int(b)
+    _buffer("codes", codes, torch.uint8, codes_bytes(rows, cols, b))
+    if operand is None:
+        operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=codes.device)
+    _buffer("operand", operand, torch.uint8, operand_bytes(rows, cols))
+    _on_device(codes.device, codes=codes, operand=operand)
+    st = lib.quest_codes_to_operand(codes.data_ptr(), rows, cols, b, operand.data_ptr(),
+                                    _stream_handle(codes.device, stream))
+    _check("quest_codes_to_operand", st)
+    return operand
 
 
 def gemm(a: torch.Tensor, a_scale: torch.Tensor, m: int, a_bits: int, b: torch.Tensor, b_scale: torch.Tensor,

@@ -428,6 +428,18 @@ quest_status quest_dequantize(const uint8_t* codes, const float* scale, int64_t 
                                            static_cast<hipStream_t>(stream)));
 }
 
+quest_status quest_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int b, uint8_t* operand,
+                                    void* stream) {
+  if (b < 1 || b > 4) return QUEST_EUNSUPPORTED;
+  const quest_status sh = check_shape(rows, cols, 128);
+  if (sh != QUEST_OK) return sh;
+  if (rows == 0) return QUEST_OK;
+  if (!codes || !operand) return QUEST_EINVAL;
+  if (!aligned16(codes) || !aligned16(operand)) return QUEST_EALIGN;
+  if (overlaps(operand, quest_operand_bytes(rows, cols), codes, quest_codes_bytes(rows, cols, b))) return QUEST_EINVAL;
+  return from_hip(quest::launch_codes_to_operand(codes, rows, cols, b, operand, static_cast<hipStream_t>(stream)));
+}
+
 quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_t* mask, int64_t rows, int64_t cols,
                              int block, void* grad_out, void* stream) {
   const int lb = log2_block(block);

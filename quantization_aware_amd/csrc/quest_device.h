@@ -649,26 +649,27 @@ __device__ __forceinline__ void put_code(CodeWords<B>& cw, int j, uint32_t code)
 
 // Store the codes of run `lane` of a window (4 B bytes per run): one access
 // of 4..16 bytes for b <= 4, a 16-byte access plus one of 4..16 bytes above.
-template <int B>
+// P: the stores' cache policy (non-temporal by default).
+template <int B, int P = kNonTemporal>
 __device__ __forceinline__ void store_codes(rsrc_t r, int lane, const CodeWords<B>& cw) {
   const int off = lane * 4 * B;
   if constexpr (B == 1) {
-    __builtin_amdgcn_raw_buffer_store_b32(cw.w[0], r, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b32(cw.w[0], r, off, 0, P);
   } else if constexpr (B == 2) {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[0], cw.w[1]}, r, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[0], cw.w[1]}, r, off, 0, P);
   } else if constexpr (B == 3) {
-    __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[0], cw.w[1], cw.w[2]}, r, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[0], cw.w[1], cw.w[2]}, r, off, 0, P);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[0], cw.w[1], cw.w[2], cw.w[3]}, r, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[0], cw.w[1], cw.w[2], cw.w[3]}, r, off, 0, P);
     if constexpr (B == 5) {
-      __builtin_amdgcn_raw_buffer_store_b32(cw.w[4], r, off + 16, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b32(cw.w[4], r, off + 16, 0, P);
     } else if constexpr (B == 6) {
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[4], cw.w[5]}, r, off + 16, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{cw.w[4], cw.w[5]}, r, off + 16, 0, P);
     } else if constexpr (B == 7) {
-      __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[4], cw.w[5], cw.w[6]}, r, off + 16, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b96(u32x3{cw.w[4], cw.w[5], cw.w[6]}, r, off + 16, 0, P);
     } else if constexpr (B == 8) {
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{cw.w[4], cw.w[5], cw.w[6], cw.w[7]}, r, off + 16, 0,
-                                             kNonTemporal);
+                                             P);
     }
   }
 }
@@ -683,10 +684,9 @@ __device__ __forceinline__ uint32_t get_code(const CodeWords<B>& cw, int j) {
   return c & ((1u << B) - 1u);
 }
 
-// Load the codes of run `lane` of a window (zeros past its end).
+// Load the codes of the run at byte offset `off` of a window (zeros past its end).
 template <int B>
-__device__ __forceinline__ CodeWords<B> load_codes(rsrc_t r, int lane) {
-  const int off = lane * 4 * B;
+__device__ __forceinline__ CodeWords<B> load_codes_at(rsrc_t r, int off) {
   CodeWords<B> cw;
   if constexpr (B == 1) {
     cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
@@ -725,6 +725,12 @@ __device__ __forceinline__ CodeWords<B> load_codes(rsrc_t r, int lane) {
     }
   }
   return cw;
+}
+
+// Load the codes of run `lane` of a window (zeros past its end).
+template <int B>
+__device__ __forceinline__ CodeWords<B> load_codes(rsrc_t r, int lane) {
+  return load_codes_at<B>(r, lane * 4 * B);
 }
 
 }  // namespace quest

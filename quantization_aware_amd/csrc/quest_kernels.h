@@ -516,8 +516,10 @@ __device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const
     cw.w[3] = cp[3];
   }
   const uint32_t mw = mp[0] | (mp[1] << 8) | (mp[2] << 16) | (mp[3] << 24);
-  store_codes<B>(codes_r, lane, cw);
-  __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, kNonTemporal);
+  // Default cache policy: measured 0.4 us faster than non-temporal stores at
+  // 16384 x 2048 (the loads stay non-temporal).
+  store_codes<B, 0>(codes_r, lane, cw);
+  __builtin_amdgcn_raw_buffer_store_b32(mw, mask_r, lane * 4, 0, 0);
 }
 
 // Dequantised values of the wave's four 16-run groups (layout of
@@ -1017,6 +1019,39 @@ __global__ void __launch_bounds__(256)
 }
 
 // ----------------------------------------------------------------------------
+// Packed b-bit codes (b <= 4) to the matrix-core operand: the levels
+// h = u - (L - 1)/2 that quest_quantize_fwd_op writes for the same codes.  A
+// workgroup takes one 32-row block and eight runs (two 128-column chunks):
+// thread t converts run 8 G + t / 32 of row 32 R + t % 32, so a wave's 64 runs
+// are 64 consecutive slots of the tiled layout (1536 contiguous bytes) and
+// the workgroup's loads cover 128 contiguous code bytes of each of its 32
+// rows.  Runs past the row and rows past the tensor are skipped (the
+// operand's padding rows are not written).
+// ----------------------------------------------------------------------------
+template <int B>
+__global__ void __launch_bounds__(256)
+    quest_codes_to_operand_kernel(const uint8_t* __restrict__ codes, int64_t rows, int runs_per_row, int run_groups,
+                                  uint8_t* __restrict__ operand) {
+  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
+  const int t = threadIdx.x;
+  const int64_t rb = blockIdx.x / run_groups;  // 32-row block
+  const int grp = static_cast<int>(blockIdx.x - rb * run_groups);
+  const int r = t & 31, j = 8 * grp + (t >> 5);
+  const bool live = rb * 32 + r < rows && j < runs_per_row;
+  const int64_t row_bytes = static_cast<int64_t>(runs_per_row) * 4 * B;
+  const rsrc_t codes_r = window_at(codes, rb * 32 * row_bytes, rows * row_bytes, static_cast<uint32_t>(32 * row_bytes));
+  const CodeWords<B> cw = load_codes_at<B>(codes_r, live ? static_cast<int>(r * row_bytes) + 4 * B * j : kNowhere);
+  float h[RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) h[i] = static_cast<float>(get_code<B>(cw, i)) - kHalf;
+  uint32_t w[6];
+  e2m3_pack32(h, w);
+  const int64_t rb_bytes = static_cast<int64_t>(runs_per_row / 4) * kOpBlockBytes;
+  const rsrc_t op_r = window_at(operand, rb * rb_bytes, ((rows + 31) >> 5) * rb_bytes, static_cast<uint32_t>(rb_bytes));
+  store_operand_words(w, op_r, live ? operand_slot(r, j) : kNowhere);
+}
+
+// ----------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------
 inline int gcd_int(int a, int b) {
@@ -1223,6 +1258,18 @@ hipError_t bwd_dispatch(const G* grad, const uint8_t* mask, int64_t rows, int64_
                          mask32, total_runs, out);
       break;
   }
+  return hipGetLastError();
+}
+
+// Codes to operand: one workgroup per 32-row block and eight runs.
+template <int B>
+hipError_t codes_to_operand_launch(const uint8_t* codes, int64_t rows, int64_t cols, uint8_t* operand,
+                                   hipStream_t stream) {
+  const int runs_per_row = static_cast<int>(cols / RUN);
+  const int run_groups = (runs_per_row + 7) / 8;
+  const int64_t grid = ((rows + 31) / 32) * run_groups;
+  hipLaunchKernelGGL((quest_codes_to_operand_kernel<B>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                     codes, rows, runs_per_row, run_groups, operand);
   return hipGetLastError();
 }
 

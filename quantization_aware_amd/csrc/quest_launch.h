@@ -46,6 +46,10 @@ struct FwdGroupItem {
 hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, int log_block, int bits, double alpha,
                             hipStream_t stream);
 
+// Packed codes (bits <= 4, cols a multiple of 128) to the tiled FP6 operand.
+hipError_t launch_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint8_t* operand,
+                                   hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t rows, int64_t cols, int bits,
                              void* out, int out_is_bf16, hipStream_t stream);
 

@@ -20,6 +20,16 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* scale, int64_t r
   return dequant_dispatch(codes, scale, rows, cols, bits, static_cast<float*>(out), stream);
 }
 
+hipError_t launch_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint8_t* operand,
+                                   hipStream_t stream) {
+  switch (bits) {
+    case 1: return codes_to_operand_launch<1>(codes, rows, cols, operand, stream);
+    case 2: return codes_to_operand_launch<2>(codes, rows, cols, operand, stream);
+    case 3: return codes_to_operand_launch<3>(codes, rows, cols, operand, stream);
+    default: return codes_to_operand_launch<4>(codes, rows, cols, operand, stream);
+  }
+}
+
 hipError_t launch_trust_bwd(const void* grad, int g_is_bf16, const uint8_t* mask, int64_t rows, int64_t cols,
                             int log_block, void* grad_out, bool allow_mfma, hipStream_t stream) {
   if (g_is_bf16)

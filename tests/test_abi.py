@@ -506,3 +506,18 @@ def test_grid_dequantize_rejects(lib):
     assert lib.quest_dequantize_sparse24(A, D_, B_, 4, 256, 5, C_, qa.QUEST_F32, None) == qa.QUEST_EUNSUPPORTED
     assert lib.quest_dequantize_sparse24(A, None, B_, 4, 256, 4, C_, qa.QUEST_F32, None) == qa.QUEST_EINVAL
     assert lib.quest_dequantize_sparse24(A, D_ + 2, B_, 4, 256, 4, C_, qa.QUEST_F32, None) == qa.QUEST_EALIGN
+
+
+def c2o(lib, codes=A, rows=4, cols=256, b=4, op=B_):
+    return lib.quest_codes_to_operand(codes, rows, cols, b, op, None)
+
+
+def test_codes_to_operand_checks(lib):
+    assert c2o(lib, codes=None, op=None, rows=0) == qa.QUEST_OK
+    for kw, status in [(dict(b=0), qa.QUEST_EUNSUPPORTED), (dict(b=5), qa.QUEST_EUNSUPPORTED),
+                       (dict(cols=192), qa.QUEST_EINVAL), (dict(cols=0), qa.QUEST_EINVAL),
+                       (dict(cols=65536), qa.QUEST_EUNSUPPORTED), (dict(rows=-1), qa.QUEST_EINVAL),
+                       (dict(codes=None), qa.QUEST_EINVAL), (dict(op=None), qa.QUEST_EINVAL),
+                       (dict(codes=A + 8), qa.QUEST_EALIGN), (dict(op=B_ + 4), qa.QUEST_EALIGN),
+                       (dict(op=A + 256), qa.QUEST_EINVAL)]:  # the operand starts inside the codes
+        assert c2o(lib, **kw) == status, kw

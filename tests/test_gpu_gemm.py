@@ -297,3 +297,50 @@ def test_block_products_full_size_sampled(dev, name, act, wt):
     got = y.index_select(0, torch.as_tensor(ri, device=dev)).index_select(1, torch.as_tensor(rj, device=dev))
     ratio = check_product(got, f["y"], 4e-3 + 1e-5, skip, abs_sum=np.abs(f["qx"]) @ np.abs(f["qw"]).T, k=k)
     log(f"{name} ok: {len(ri)}x{len(rj)} sampled outputs, {int(skip.sum())} in band reach, max rel {ratio:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# Stored codes to the operand (quest_codes_to_operand): the same bytes as the
+# operand quest_quantize_fwd_op writes with those codes on every row of the
+# tensor (the padding rows of the last 32-row block are left alone by the
+# conversion, while the forward's spare waves may write them), and the same
+# product.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols,b", [(45, 384, 4), (64, 2048, 1), (64, 2048, 2), (33, 2048, 3), (33, 5632, 4),
+                                         (1000, 640, 2), (7, 128, 4), (96, 1152, 3)])
+def test_codes_to_operand_equals_forward_operand(dev, rows, cols, b):
+    log(f"codes to operand {rows}x{cols} b={b}")
+    x = make_tensor(TensorSpec("c2o.x", rows, cols, "bf16", "student_t", 4, 8700 + cols + b, outlier_cols=2,
+                               outlier_scale=20.0), dev)
+    nbytes = qa.operand_bytes(rows, cols)
+    op_fwd = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=dev)
+    codes, scale, _, _ = qa.quantize_fwd_op(x, 128, b, with_codes=True, operand=op_fwd)
+    op_c = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=dev)
+    qa.codes_to_operand(codes, rows, cols, b, operand=op_c)
+    torch.cuda.synchronize()
+    rows_c = untile_operand(op_c.cpu().numpy()[:nbytes], rows, cols)
+    rows_f = untile_operand(op_fwd.cpu().numpy()[:nbytes], rows, cols)
+    assert np.array_equal(rows_c, rows_f), f"{int((rows_c != rows_f).sum())} operand bytes differ"
+    # the conversion writes no padding row
+    pad = op_c.cpu().numpy()[:nbytes].copy()
+    pad_rows = untile_operand(pad, ((rows + 31) // 32) * 32, cols)[rows:]
+    assert (pad_rows == 0xA5).all()
+    # the fields decode to the codes' levels (read back through the layout helper)
+    u = qo.unpack_lsb_first(codes.cpu().numpy(), b, cols)
+    fields = gpu_fields(op_c, rows, cols)
+    assert np.array_equal(fields, halves_e2m3(u, b))
+
+
+def test_product_from_stored_codes(dev):
+    """A weight kept as 4-bit codes feeds the product through quest_codes_to_operand and gives the
+    product of the operand forward exactly."""
+    m, n, k = 300, 256, 2048
+    x = make_tensor(TensorSpec("c2o.a", m, k, "bf16", "student_t", 4, 8800, outlier_cols=20, outlier_scale=20.0), dev)
+    w = make_tensor(TensorSpec("c2o.w", n, k, "bf16", "normal", 0.02, 8801), dev)
+    _, sx, _, ox = qa.quantize_fwd_op(x, 128, 4)
+    cw, sw, _, ow = qa.quantize_fwd_op(w, 128, 4, with_codes=True)
+    ow_c = qa.codes_to_operand(cw, n, k, 4)
+    y_fwd = qa.gemm(ox, sx, m, 4, ow, sw, n, 4, k, out_dtype=torch.float32)
+    y_codes = qa.gemm(ox, sx, m, 4, ow_c, sw, n, 4, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd, y_codes)
