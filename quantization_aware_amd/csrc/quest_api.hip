@@ -557,6 +557,8 @@ quest_status quantize_grid_common(const void* x, quest_dtype x_dtype, int64_t ro
   a.trust = trust;
   a.bits = b == 0 ? 4 : b;
   a.sparse24 = b == 0 ? 0 : 1;
+  std::call_once(g_env_once, read_env);
+  a.allow_mfma = g_allow_mfma;
   a.codes = codes;
   a.index = index;
   a.scale = scale;

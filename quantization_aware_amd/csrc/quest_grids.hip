@@ -24,7 +24,9 @@
 //
 // Kernel layout as quest_fwd_rows_kernel: a workgroup holds whole rows, a
 // lane holds one 32-entry run (8 groups of 4), the row's sum of squares goes
-// through aligned lane groups and LDS in a fixed order.
+// through aligned lane groups and LDS in a fixed order.  FP4 of bf16 rows of
+// 512, 1024 or 2048 columns instead runs the dense matrix-core forward
+// (quest_fwd_mfma_kernel with FP4 codes).
 #include "quest_kernels.h"
 
 namespace quest {
@@ -40,25 +42,6 @@ struct GridConsts {
   float prune_ratio;  // 2:4: thr / (the pruned entries' threshold Delta / 2) = L - 1 + t
   float inv_count; // 1 / (entries the RMS runs over): 1 / C (FP4), 2 / C (2:4)
 };
-
-// FP4 codes of 8 entries (factor kz), one dword, entry i in bits [4 i, 4 i + 4).
-// The conversion keeps the sign of zero; the zero level gets the +0 code.
-__device__ __forceinline__ uint32_t fp4_codes8(const float* v, float kz) {
-  uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * kz, v[1] * kz, 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * kz, v[3] * kz, 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * kz, v[5] * kz, 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * kz, v[7] * kz, 1.0f, 3);
-  const uint32_t t = ~w;
-  const uint32_t neg_zero = (w >> 3) & (t >> 2) & (t >> 1) & t & 0x11111111u;  // nibbles equal to 8
-  return w ^ (neg_zero << 3);
-}
-
-// E2M1 magnitude of a 3-bit code.
-__device__ __forceinline__ float e2m1_mag(uint32_t c) {
-  const uint32_t e = c >> 1, m = c & 1u;
-  return e == 0 ? 0.5f * static_cast<float>(m) : (1.f + 0.5f * static_cast<float>(m)) * static_cast<float>(1u << (e - 1));
-}
 
 // Per-lane conditions of the 2:4 selection are kept as wave lane masks
 // (one bit per lane), so that their logic runs on the scalar unit: a compare
@@ -347,6 +330,32 @@ hipError_t grid_launch(const In* x, const GridLaunch& a) {
     k.thr = static_cast<float>(a.alpha * sqrt_n * (1.0 + a.trust / lm1));
     k.prune_ratio = static_cast<float>(lm1 + a.trust);
     k.inv_count = static_cast<float>(2.0 / double(a.cols));
+  }
+  if constexpr (G == Grid::kFp4 && sizeof(In) == 2) {
+    if (a.allow_mfma && (runs_per_row == 16 || runs_per_row == 32 || runs_per_row == 64)) {
+      // bf16 rows of 512, 1024 or 2048 columns: the dense matrix-core forward
+      // with FP4 codes (same transform, RMS from the inputs, nibble per entry).
+      FwdConsts kf;
+      kf.alpha = k.alpha;
+      kf.kk = k.kz;
+      kf.thr = k.thr;
+      kf.inv_cols = k.inv_count;
+      kf.chunks = static_cast<int>(a.cols / 128);
+      const int64_t total_runs = a.rows * runs_per_row;
+      const dim3 grid4(static_cast<uint32_t>((total_runs + 255) / 256));
+      auto run = [&](auto logr) {
+        hipLaunchKernelGGL((quest_fwd_mfma_kernel<LOGN, 4, decltype(logr)::value, Dq, true, true>), grid4, dim3(256),
+                           0, a.stream, x, total_runs, kf, a.codes, a.scale, reinterpret_cast<uint32_t*>(a.mask),
+                           static_cast<Dq*>(a.dq));
+      };
+      if (runs_per_row == 16)
+        run(std::integral_constant<int, 4>{});
+      else if (runs_per_row == 32)
+        run(std::integral_constant<int, 5>{});
+      else
+        run(std::integral_constant<int, 6>{});
+      return hipGetLastError();
+    }
   }
   constexpr int US = 2 * sizeof(In) > DqOut<Dq>::U ? 2 * sizeof(In) : DqOut<Dq>::U;
   hipLaunchKernelGGL((quest_fwd_grid_kernel<In, LOGN, G, B, Dq>), dim3(static_cast<uint32_t>(grid)), dim3(threads),

@@ -480,6 +480,25 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// FP4 codes of 8 entries (factor kz), one dword, entry i in bits [4 i, 4 i + 4).
+// The conversion keeps the sign of zero; the zero level gets the +0 code.
+__device__ __forceinline__ uint32_t fp4_codes8(const float* v, float kz) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * kz, v[1] * kz, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * kz, v[3] * kz, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * kz, v[5] * kz, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * kz, v[7] * kz, 1.0f, 3);
+  const uint32_t t = ~w;
+  const uint32_t neg_zero = (w >> 3) & (t >> 2) & (t >> 1) & t & 0x11111111u;  // nibbles equal to 8
+  return w ^ (neg_zero << 3);
+}
+
+// E2M1 magnitude of a 3-bit code.
+__device__ __forceinline__ float e2m1_mag(uint32_t c) {
+  const uint32_t e = c >> 1, m = c & 1u;
+  return e == 0 ? 0.5f * static_cast<float>(m) : (1.f + 0.5f * static_cast<float>(m)) * static_cast<float>(1u << (e - 1));
+}
+
 // Codes and mask of a wave's four 16-run groups after the matrix-core
 // transform: v[8 j .. 8 j + 7] of lane (g, n) are outputs 8 g .. 8 g + 7 of
 // run 16 j + n, quantised with kk[j] and tested against thr[j].  Codes and
@@ -487,13 +506,16 @@ __global__ void __launch_bounds__(256)
 // quarters and slots then hands lane l all four quarters of run l, stored at
 // run l of the windows `codes_r` (4 B bytes per run) and `mask_r` (a dword
 // per run).
-template <int B>
+// kFp4: FP4 codes (E2M1 patterns of the nearest level, B = 4) instead of the
+// midrise grid's.
+template <int B, bool kFp4 = false>
 __device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const float (&kk)[4],
                                                     const float (&thr)[4], int lane, rsrc_t codes_r, rsrc_t mask_r) {
+  static_assert(!kFp4 || B == 4, "FP4 codes are 4 bits");
   uint32_t cp[4], mp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cp[j] = quantise8<B>(v + 8 * j, kk[j]);
+    cp[j] = kFp4 ? fp4_codes8(v + 8 * j, kk[j]) : quantise8<B>(v + 8 * j, kk[j]);
     mp[j] = 0u;
     push8_abs_le(mp[j], v + 8 * j, thr[j]);
   }
@@ -527,7 +549,8 @@ __device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const
 // lane (g, n) holds entries 8 g .. 8 g + 7 of run 16 j + n in slot j, which
 // it stores as 16 (bf16) or 32 (fp32) contiguous bytes; each store
 // instruction covers one contiguous stretch, as the loads do.
-template <int B, typename Dq>
+// kFp4: FP4 levels, c = s / 6, as quest_dequantize_fp4 computes them.
+template <int B, typename Dq, bool kFp4 = false>
 __device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float (&kk)[4], const float (&c)[4],
                                               int lane, rsrc_t dq_r) {
   if constexpr (DqOut<Dq>::kOn) {
@@ -535,7 +558,17 @@ __device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float q[8];
-      grid_values<B, 8>(v + 8 * j, kk[j], c[j], q);
+      if constexpr (kFp4) {
+        const uint32_t w = fp4_codes8(v + 8 * j, kk[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t code = (w >> (4 * i)) & 15u;
+          const float mag = e2m1_mag(code & 7u) * c[j];
+          q[i] = (code & 8u) ? -mag : mag;
+        }
+      } else {
+        grid_values<B, 8>(v + 8 * j, kk[j], c[j], q);
+      }
       if constexpr (sizeof(Dq) == 2) {
         const u32x4 w = {pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]), pack_bf16x2(q[4], q[5]),
                          pack_bf16x2(q[6], q[7])};
@@ -563,7 +596,7 @@ __device__ __forceinline__ void mfma_store_dq(const float (&v)[RUN], const float
 // a grid-stride loop with its loads one to three tiles ahead.
 // kQuant = false (operand calls without codes and mask) leaves the codes and
 // mask work out of the build.
-template <int LOGN, int B, int LOGR, typename Dq, bool kQuant>
+template <int LOGN, int B, int LOGR, typename Dq, bool kQuant, bool kFp4 = false>
 __device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, int64_t total_runs, const FwdConsts& k,
                                               uint8_t* __restrict__ codes, float* __restrict__ scale,
                                               uint32_t* __restrict__ mask, Dq* __restrict__ dq, int64_t tile, int lane,
@@ -612,13 +645,13 @@ __device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, in
       for (int j = r * (4 / ROWS); j < (r + 1) * (4 / ROWS); ++j) {
         kk[j] = c.kk;
         thr[j] = c.thr;
-        ch[j] = grid_step_half<B>(c.scale);
+        ch[j] = kFp4 ? c.scale / 6.f : grid_step_half<B>(c.scale);
       }
     }
     const int64_t run0 = t * 64;
     if (kQuant)
-      mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
-                             window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
+      mfma_quantise_store<B, kFp4>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
+                                   window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
     if constexpr (kIsOperand<Dq>) {
       // After the transpose lane l holds run l of the tile.  The workgroup's
       // four tiles are 4 ROWS consecutive rows of one 32-row block.
@@ -635,7 +668,7 @@ __device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, in
       __syncthreads();
     } else if constexpr (DqOut<Dq>::kOn) {
       constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
-      mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, total_runs * RB, 64 * RB));
+      mfma_store_dq<B, Dq, kFp4>(v, kk, ch, lane, window_at(dq, run0 * RB, total_runs * RB, 64 * RB));
     }
     float my_scale = sc[0];
 #pragma unroll
@@ -649,7 +682,7 @@ __device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, in
   process(tile, f);
 }
 
-template <int LOGN, int B, int LOGR, typename Dq, bool kQuant = true>
+template <int LOGN, int B, int LOGR, typename Dq, bool kQuant = true, bool kFp4 = false>
 __global__ void __launch_bounds__(256)
     quest_fwd_mfma_kernel(const uint16_t* __restrict__ x, int64_t total_runs, FwdConsts k,
                           uint8_t* __restrict__ codes, float* __restrict__ scale, uint32_t* __restrict__ mask,
@@ -664,7 +697,8 @@ __global__ void __launch_bounds__(256)
   // every store it makes is dropped or lands in padding.
   if (!kIsOperand<Dq> && tile >= tiles) return;
   __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
-  fwd_mfma_tile<LOGN, B, LOGR, Dq, kQuant>(x, total_runs, k, codes, scale, mask, dq, tile, lane, wave, opstage);
+  fwd_mfma_tile<LOGN, B, LOGR, Dq, kQuant, kFp4>(x, total_runs, k, codes, scale, mask, dq, tile, lane, wave,
+                                                 opstage);
 }
 
 // Several tensors of one width in one launch (quest_quantize_fwd_group):

@@ -82,6 +82,7 @@ struct GridLaunch {
   int64_t rows, cols;
   double alpha, trust;
   int bits, sparse24;
+  bool allow_mfma;  // bf16 rows of 512, 1024 or 2048 columns: the matrix-core kernels
   uint8_t* codes;  // may be null
   uint8_t* index;  // 2:4 positions, may be null
   float* scale;

@@ -47,8 +47,11 @@ def np_rows(t: torch.Tensor, rows) -> np.ndarray:
 
 
 CASES = [
-    # rows, cols, dtype, block, trust
+    # rows, cols, dtype, block, trust (bf16 rows of 512, 1024 or 2048 columns take the matrix-core 2:4 kernel)
     (77, 2048, "bf16", 128, 1.0),
+    (130, 512, "bf16", 64, 1.0),
+    (45, 1024, "bf16", 256, 1.3),
+    (1, 2048, "bf16", 64, 0.0),
     (33, 1024, "f32", 64, 1.0),
     (21, 5632, "bf16", 128, 1.3),
     (19, 2560, "bf16", 256, 0.0),
@@ -145,6 +148,87 @@ def test_grids_degenerate_rows(dev):
             check_fwd_sparse24(x64, block, b, codes.cpu().numpy(), index.cpu().numpy(), scale.cpu().numpy(),
                                mask.cpu().numpy(), max_fraction=None, ref=ref)
             assert torch.all(scale[0] == 0) and torch.all(mask[0] == 0xFF)
+
+
+@pytest.mark.parametrize("cols", [512, 1024, 2048])
+def test_grids_degenerate_rows_bf16(dev, cols):
+    """bf16 rows with zeros and exact magnitude ties in the Hadamard domain, at the widths of the
+    matrix-core forwards: FP4 (zero row: code 0, scale 0, all trusted) and 2:4 (ties to the lower
+    index)."""
+    rows = 8
+    x = np.zeros((rows, cols), dtype=np.float32)
+    x[1] = 3.25
+    x[2, 77] = -5.0
+    x[3, :128] = 1.0
+    x[4] = np.arange(cols, dtype=np.float32) % 7 - 3
+    x[5, ::2] = 2.0
+    x[6, ::4] = -1.5
+    x[7] = np.where(np.arange(cols) % 3 == 0, 0.5, -0.25)
+    xt = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    x64 = to_float64(xt)
+    for block in (64, 128, 256):
+        log(f"fp4 degenerate bf16 {rows}x{cols} block {block}")
+        codes, scale, mask, dq = qa.quantize_fwd_fp4(xt, block, dq_dtype=torch.float32)
+        torch.cuda.synchronize()
+        check_fwd_fp4(x64, block, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), max_fraction=None)
+        assert torch.all(codes[0] == 0) and torch.all(scale[0] == 0) and torch.all(mask[0] == 0xFF)
+        assert torch.equal(dq, qa.dequantize_fp4(codes, scale, rows, cols, torch.float32))
+        for b in (1, 2, 3, 4):
+            log(f"2:4 ties bf16 {rows}x{cols} block {block} b={b}")
+            codes, index, scale, mask, dq = qa.quantize_fwd_sparse24(xt, block, b, dq_dtype=torch.float32)
+            torch.cuda.synchronize()
+            ref = qo.quantize_fwd_sparse24(x64, block, b)
+            if block != 128:
+                # exact Hadamard entries on both sides: ties are exact, positions agree everywhere
+                assert np.array_equal(index.cpu().numpy(), ref["index"])
+            check_fwd_sparse24(x64, block, b, codes.cpu().numpy(), index.cpu().numpy(), scale.cpu().numpy(),
+                               mask.cpu().numpy(), max_fraction=None, ref=ref)
+            assert torch.all(scale[0] == 0) and torch.all(mask[0] == 0xFF) and torch.all(dq[0] == 0)
+            assert torch.equal(dq, qa.dequantize_sparse24(codes, index, scale, rows, cols, b, torch.float32))
+
+
+_VALU_FP4_CHILD = r"""
+import sys
+import numpy as np
+import torch
+sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
+import quantization_aware_amd as qa
+from quest_inputs import TensorSpec, make_tensor
+dev = torch.device("cuda", 0)
+x = make_tensor(TensorSpec("valu.fp4", 96, int(sys.argv[2]), "bf16", "student_t", 4, 8600, outlier_cols=20,
+                           outlier_scale=20.0), dev)
+codes, scale, mask, _ = qa.quantize_fwd_fp4(x, int(sys.argv[3]), float(sys.argv[4]))
+torch.cuda.synchronize()
+np.savez(sys.argv[5], codes=codes.cpu().numpy(), scale=scale.cpu().numpy(), mask=mask.cpu().numpy())
+"""
+
+
+@pytest.mark.parametrize("cols,block,trust", [(2048, 128, 1.0), (512, 64, 1.3)])
+def test_fp4_valu_switch_matches_oracle(dev, tmp_path, cols, block, trust):
+    """QUEST_FWD_KERNEL=valu keeps the FP4 forward of these widths on the run-per-lane kernel: it matches
+    the oracle, and so does the matrix-core kernel; they agree outside the exempt entries."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = tmp_path / "fp4.npz"
+    log(f"vector-ALU FP4 forward in a child process, 96x{cols} block {block} trust {trust}")
+    subprocess.run([sys.executable, "-c", _VALU_FP4_CHILD, root, str(cols), str(block), str(trust), str(out)],
+                   env=dict(os.environ, QUEST_FWD_KERNEL="valu"), check=True, timeout=300)
+    got = np.load(out)
+    x = make_tensor(TensorSpec("valu.fp4", 96, cols, "bf16", "student_t", 4, 8600, outlier_cols=20,
+                               outlier_scale=20.0), dev)
+    x64 = to_float64(x)
+    st = check_fwd_fp4(x64, block, got["codes"], got["scale"], got["mask"], trust=trust)
+    codes, scale, mask, _ = qa.quantize_fwd_fp4(x, block, trust)
+    torch.cuda.synchronize()
+    st2 = check_fwd_fp4(x64, block, codes.cpu().numpy(), scale.cpu().numpy(), mask.cpu().numpy(), trust=trust,
+                        ref=st["ref"])
+    ok = ~(st["bad"] | st2["bad"])
+    c_valu = qo.unpack_lsb_first(got["codes"], 4, cols)
+    c_mfma = qo.unpack_lsb_first(codes.cpu().numpy(), 4, cols)
+    assert np.array_equal(c_valu[ok], c_mfma[ok])
 
 
 def test_grids_empty(dev):
