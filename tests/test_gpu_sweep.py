@@ -144,3 +144,53 @@ def test_sweep_gemm(dev, case):
     tol = 1e-6 if out_dtype == torch.float32 else 4e-3
     bad = np.abs(got - ref) > tol * np.abs(ref) + slack
     assert not bad.any(), f"{int(bad.sum())} outputs off, first at {np.argwhere(bad)[0]}"
+
+
+N_GROUP, N_C2O = 16, 16
+
+
+@pytest.mark.parametrize("case", range(N_GROUP))
+def test_sweep_group(dev, case):
+    """Random groups (1..12 tensors, mixed widths incl. the grouped ones, ragged rows, empty tensors):
+    each tensor equal to its own quest_quantize_fwd bit for bit, and one checked against the oracle."""
+    rng = np.random.default_rng(30000 + case)
+    block = int(rng.choice([64, 128, 256]))
+    b = int(rng.integers(1, 9))
+    dt = "bf16" if rng.random() < 0.8 else "f32"
+    widths = [c for c in (512, 1024, 2048, 256, 640, 5632, 1536) if c % block == 0]
+    count = int(rng.integers(1, 13))
+    shapes = [(int(rng.integers(0, 300)) if rng.random() < 0.9 else 0, int(rng.choice(widths))) for _ in range(count)]
+    log(f"group case {case}: {count} {dt} tensors, block {block}, b={b}: {shapes}")
+    xs = [draw_input(rng, r, c, dt, 31000 + 16 * case + i, dev) if r else
+          torch.empty((0, c), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev)
+          for i, (r, c) in enumerate(shapes)]
+    got = qa.quantize_fwd_group(xs, block, b)
+    for i, x in enumerate(xs):
+        if x.shape[0] == 0:
+            continue
+        ref = qa.quantize_fwd(x, block, b)
+        torch.cuda.synchronize()
+        assert all(torch.equal(g_, r_) for g_, r_ in zip(got[i], ref)), f"tensor {i} {tuple(x.shape)}"
+    live = [i for i, x in enumerate(xs) if x.shape[0]]
+    if live:
+        i = live[0]
+        c_, s_, m_ = (t.cpu().numpy() for t in got[i])
+        check_fwd(x64_of(xs[i]), block, b, c_, s_, m_)
+
+
+@pytest.mark.parametrize("case", range(N_C2O))
+def test_sweep_codes_to_operand(dev, case):
+    """Random shapes and widths: the operand of the stored codes equals the operand forward's on every row."""
+    rng = np.random.default_rng(32000 + case)
+    rows = int(rng.integers(1, 300))
+    cols = 128 * int(rng.integers(1, 45))
+    b = int(rng.integers(1, 5))
+    dt = "bf16" if rng.random() < 0.7 else "f32"
+    log(f"codes to operand case {case}: {rows}x{cols} {dt} b={b}")
+    x = draw_input(rng, rows, cols, dt, 33000 + case, dev)
+    codes, _, _, op = qa.quantize_fwd_op(x, 128, b, with_codes=True)
+    op_c = qa.codes_to_operand(codes, rows, cols, b)
+    torch.cuda.synchronize()
+    n = qa.operand_bytes(rows, cols)
+    assert np.array_equal(untile_operand(op_c.cpu().numpy()[:n], rows, cols),
+                          untile_operand(op.cpu().numpy()[:n], rows, cols))
