@@ -49,6 +49,22 @@ def exempt_entries(y: np.ndarray, s: np.ndarray, b: int, band: float = BAND, tru
     return ex
 
 
+def check_rate(count: int, entries: int, what: str, first: str | None = None,
+               max_fraction: float = MAX_MISMATCH_FRACTION) -> None:
+    """At most ceil(max_fraction * entries) in-band differences among `entries` decisions.
+
+    A rate, so that a call of fewer than 1 / max_fraction entries may hold one; the
+    entries are those of one call (all tensors of a grouped call together).  Counts
+    above the plain fraction are listed at the end of the test run.
+    """
+    allowed = math.ceil(max_fraction * entries)
+    assert count <= allowed, f"{count} differing entries (fraction {count / max(entries, 1)}) above {allowed} allowed"
+    if count > max_fraction * entries:
+        RATE_READING_CASES.append(
+            f"{os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]}: {count} of {entries} entries ({what})"
+            + (f", {first}" if first else ""))
+
+
 def check_fwd(x64: np.ndarray, block: int, b: int, codes, scale, mask, ref=None,
               max_fraction: float | None = MAX_MISMATCH_FRACTION, trust: float = 1.0) -> dict:
     """Assert GPU forward outputs (numpy uint8 / float32 arrays) match the oracle on x64.
@@ -79,18 +95,12 @@ def check_fwd(x64: np.ndarray, block: int, b: int, codes, scale, mask, ref=None,
         )
     frac = float((bad_u | bad_m).mean()) if bad_u.size else 0.0
     if max_fraction is not None:
-        # A rate: at most ceil(max_fraction * entries) differing entries, so that
-        # a tensor of fewer than 1 / max_fraction entries may hold one.
-        allowed = math.ceil(max_fraction * bad_u.size)
-        count = int((bad_u | bad_m).sum())
-        assert count <= allowed, f"{count} differing entries (fraction {frac}) above {allowed} allowed"
-        if count > max_fraction * bad_u.size:
-            # the case the rate reading exists for, listed at the end of the test run
+        first = None
+        if (bad_u | bad_m).any():
             rr, cc = np.argwhere(bad_u | bad_m)[0]
-            RATE_READING_CASES.append(
-                f"{os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]}: {count} of {bad_u.size} entries "
-                f"(b={b}, block={block}, trust={trust}), first at ({rr},{cc}) y={ref['y'][rr, cc]!r} "
-                f"s={ref['scale'][rr]!r}")
+            first = f"first at ({rr},{cc}) y={ref['y'][rr, cc]!r} s={ref['scale'][rr]!r}"
+        check_rate(int((bad_u | bad_m).sum()), bad_u.size, f"b={b}, block={block}, trust={trust}", first,
+                   max_fraction)
     s_ref = ref["scale"]
     zero = s_ref == 0.0
     assert np.all(scale[zero] == 0.0)
