@@ -259,8 +259,10 @@ quest_status quest_trust_bwd(const void* grad, quest_dtype g_dtype, const uint8_
  *   8 t + j).  Run j (columns 32 j .. 32 j + 31) of row r therefore starts at
  *     (r / 32) * (cols / 128) * 3072 + (j / 4) * 3072 + (j / 2 % 2) * 1536
  *       + (32 (j % 2) + r % 32) * 24.
- *   The padding rows of the last row block are not written; a product only
- *   uses them for outputs it does not store.
+ *   The padding rows of the last row block may be written by
+ *   quest_quantize_fwd_op (their contents are unspecified) and are left alone
+ *   by quest_codes_to_operand; a product only uses them for outputs it does
+ *   not store.
  */
 
 /* Bytes of the operand: ceil(rows / 32) * 32 * cols * 3 / 4 (0 unless cols is a

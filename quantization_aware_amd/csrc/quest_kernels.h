@@ -268,6 +268,7 @@ __device__ __forceinline__ int64_t fwd_wg_index() {
 }
 
 constexpr int kOpBlockBytes = 3072;  // 32 rows x 128 columns at 6 bits
+constexpr int kOpStorePolicy = 0;    // cache policy of the staged operand stores
 
 // Offset of run j of a row inside its row block.
 __device__ __forceinline__ int operand_slot(int row_in_block, int j) {
@@ -347,11 +348,14 @@ __device__ __forceinline__ void store_operand_words(const uint32_t (&w)[6], rsrc
 // Operand staging in LDS for a workgroup that holds R consecutive rows of one
 // 32-row block (R divides 32, the first row a multiple of R): in the tiled
 // layout the R rows' slots of one run j are adjacent, 24 R contiguous bytes.
-// Run j of row r goes to LDS byte j (24 R + 8) + 24 r (the 8-byte pad spreads
-// the runs over the banks); the pieces are then written out by the whole
-// workgroup as 8-byte stores that cover whole pieces, not 24-byte slots.
+// Run j of row r goes to LDS byte j (24 R + 16) + 24 r (the 16-byte pad
+// spreads the runs over the banks and keeps pieces 16-byte aligned); the
+// pieces are then written out by the whole workgroup as 16-byte stores (8-byte
+// ones when R is odd) that cover whole pieces, not 24-byte slots.
+constexpr int kOpStagePad = 16;
+
 __device__ __forceinline__ void stage_operand_words(uint8_t* st, int j, int r, int R, const uint32_t (&w)[6]) {
-  u32x2* d = reinterpret_cast<u32x2*>(st + j * (24 * R + 8) + 24 * r);
+  u32x2* d = reinterpret_cast<u32x2*>(st + j * (24 * R + kOpStagePad) + 24 * r);
   d[0] = u32x2{w[0], w[1]};
   d[1] = u32x2{w[2], w[3]};
   d[2] = u32x2{w[4], w[5]};
@@ -359,15 +363,26 @@ __device__ __forceinline__ void stage_operand_words(uint8_t* st, int j, int r, i
 
 // Write the staged pieces of runs 0 .. runs - 1 (R rows from row r0 of its
 // block) through `op_r`, the window of that row block.  Thread t of n takes
-// the 8-byte words t, t + n, ...
+// the words t, t + n, ...
 __device__ __forceinline__ void flush_operand(const uint8_t* st, int R, int runs, int r0_in_block, rsrc_t op_r, int t,
                                               int n) {
-  const int per = 3 * R;  // words per piece
-  const int words = runs * per;
-  for (int q = t; q < words; q += n) {
-    const int j = q / per, within = q - j * per;
-    const u32x2 v = *reinterpret_cast<const u32x2*>(st + j * (24 * R + 8) + 8 * within);
-    __builtin_amdgcn_raw_buffer_store_b64(v, op_r, operand_slot(r0_in_block, j) + 8 * within, 0, 0);
+  const int stride = 24 * R + kOpStagePad;
+  if ((R & 1) == 0) {
+    const int per = 3 * R / 2;  // 16-byte words per piece
+    const int words = runs * per;
+    for (int q = t; q < words; q += n) {
+      const int j = q / per, within = q - j * per;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + j * stride + 16 * within);
+      __builtin_amdgcn_raw_buffer_store_b128(v, op_r, operand_slot(r0_in_block, j) + 16 * within, 0, kOpStorePolicy);
+    }
+  } else {
+    const int per = 3 * R;  // 8-byte words per piece
+    const int words = runs * per;
+    for (int q = t; q < words; q += n) {
+      const int j = q / per, within = q - j * per;
+      const u32x2 v = *reinterpret_cast<const u32x2*>(st + j * stride + 8 * within);
+      __builtin_amdgcn_raw_buffer_store_b64(v, op_r, operand_slot(r0_in_block, j) + 8 * within, 0, kOpStorePolicy);
+    }
   }
 }
 
@@ -696,7 +711,7 @@ __global__ void __launch_bounds__(256)
   // the last workgroup run: a wave past the last tile computes on zeros and
   // every store it makes is dropped or lands in padding.
   if (!kIsOperand<Dq> && tile >= tiles) return;
-  __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + 8) : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t opstage[kIsOperand<Dq> ? 64 * (24 * 4 * ROWS + kOpStagePad) : 16];
   fwd_mfma_tile<LOGN, B, LOGR, Dq, kQuant, kFp4>(x, total_runs, k, codes, scale, mask, dq, tile, lane, wave,
                                                  opstage);
 }
@@ -745,6 +760,9 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
   fwd_mfma_tile<LOGN, B, LOGR, void, true>(x, runs, k, codes, scale, mask, nullptr, tile - first, lane, wave,
                                            nullptr);
 }
+
+// Dynamic LDS of the row-per-workgroup kernels (sized at launch).
+extern __shared__ u32x4 rows_lds[];
 
 // bf16 rows of 16 m runs (m > 4: more than 2048 columns, a multiple of 512)
 // on the matrix cores.  A workgroup holds rows_per_wg whole rows; wave w
@@ -822,23 +840,25 @@ __global__ void __launch_bounds__(1024)
     mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
                            window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
   if constexpr (kIsOperand<Dq>) {
-    // After the transpose lane l holds run 64 w + l of the workgroup.
+    // After the transpose lane l holds run 64 w + l of the workgroup.  The
+    // workgroup's rows lie in one 32-row block (rows_per_wg divides 32 and
+    // the first row is a multiple of it), where run j of its rows is one
+    // piece of 24 rows_per_wg bytes: the runs are staged in LDS and written
+    // as whole pieces.  In the last block rows past `rows` land in the
+    // padding rows.
     const int64_t row0 = wg * rows_per_wg;
-    const int64_t last = (row0 + rows_per_wg < rows ? row0 + rows_per_wg : rows) - 1;
     const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
-    const int64_t rb0 = row0 >> 5;
-    const rsrc_t op_r = window_at(dq, rb0 * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
-                                  static_cast<uint32_t>(((last >> 5) - rb0 + 1) * rb_bytes));
+    const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                  static_cast<uint32_t>(rb_bytes));
     const int wr = 64 * wave + lane;
     const int lrow = wr / runs_per_row;
-    const int64_t row = row0 + lrow;
-    const bool live = lrow < rows_per_wg && row < rows;
     uint32_t w[6];
     mfma_operand_words<B>(v, kk, w);
-    const int off = live ? static_cast<int>(((row >> 5) - rb0) * rb_bytes) +
-                               operand_slot(static_cast<int>(row & 31), wr - lrow * runs_per_row)
-                         : kNowhere;
-    store_operand_words(w, op_r, off);
+    uint8_t* st = reinterpret_cast<uint8_t*>(rows_lds);
+    if (lrow < rows_per_wg) stage_operand_words(st, wr - lrow * runs_per_row, lrow, rows_per_wg, w);
+    __syncthreads();
+    flush_operand(st, rows_per_wg, runs_per_row, static_cast<int>(row0 & 31), op_r, static_cast<int>(threadIdx.x),
+                  static_cast<int>(blockDim.x));
   } else if constexpr (DqOut<Dq>::kOn) {
     constexpr int64_t RB = 32 * sizeof(Dq);  // bytes per run
     mfma_store_dq<B, Dq>(v, kk, ch, lane, window_at(dq, run0 * RB, run_end * RB, 64 * RB));
@@ -856,7 +876,6 @@ __global__ void __launch_bounds__(1024)
 // LDS of the row-per-workgroup kernels, sized at launch by their wave count:
 // per wave a staging area of 64 * US 16-byte slots, then one float per lane
 // for the partial row sums.
-extern __shared__ u32x4 rows_lds[];
 
 inline size_t rows_lds_bytes(int threads, int us) {
   return static_cast<size_t>(threads / 64) * 64 * static_cast<size_t>(us) * 16 + static_cast<size_t>(threads) * 4;
@@ -1108,6 +1127,9 @@ inline int log2_exact(int v) {
 // loads run ahead of the arithmetic.
 constexpr int64_t kFwdTileWorkgroups = 512;
 
+// Rows per workgroup of the matrix-core row kernel when it writes the operand.
+constexpr int kOpRowsPerWorkgroup = 4;
+
 
 
 // Per-launch constants of the forward kernels for rows of `cols` entries.
@@ -1162,7 +1184,15 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
       // waves.
       const int padded = ((runs_per_row + 63) / 64) * 64;
       int rows_per_wg = 1;
-      if (8 * (padded - runs_per_row) > padded) {
+      size_t lds = 0;
+      if constexpr (kIsOperand<Dq>) {
+        // The operand: several rows of one 32-row block per workgroup (a
+        // power of two, at most kOpRowsPerWorkgroup and 1024 threads), so
+        // that its pieces are 24 rows_per_wg contiguous bytes.
+        rows_per_wg = kOpRowsPerWorkgroup;
+        while (rows_per_wg > 1 && rows_per_wg * runs_per_row > 1024) rows_per_wg >>= 1;
+        lds = static_cast<size_t>(runs_per_row) * (24 * rows_per_wg + kOpStagePad);
+      } else if (8 * (padded - runs_per_row) > padded) {
         rows_per_wg = 64 / gcd_int(runs_per_row, 64);
         if (rows_per_wg * runs_per_row > 1024) rows_per_wg = 1024 / runs_per_row;
         if (rows_per_wg < 1) rows_per_wg = 1;
@@ -1172,7 +1202,7 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
       // An operand call that asks for neither codes nor mask runs the build without them.
       auto run = [&](auto quant) {
         hipLaunchKernelGGL((quest_fwd_mfma_rows_kernel<LOGN, B, Dq, decltype(quant)::value>),
-                           dim3(static_cast<uint32_t>(grid)), dim3(threads), 0, stream, x, rows, runs_per_row,
+                           dim3(static_cast<uint32_t>(grid)), dim3(threads), lds, stream, x, rows, runs_per_row,
                            rows_per_wg, k, a.codes, a.scale, mask32, dq);
       };
       bool quant = true;
