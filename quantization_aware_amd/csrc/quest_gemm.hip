@@ -86,49 +86,117 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, int32_t voff, i32x4 rsr
                : "memory");
 }
 
-// s_waitcnt with only the vector-memory counter limited (lgkm and exp left open).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x3F70 | N);
+// 4 bytes from global memory into LDS at lds_base + 4 * lane (as dma16).
+__device__ __forceinline__ void dma4(uint32_t lds_base, int32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
 }
 
-// One output tile: rows 256 tm .. + 255, columns col0 .. col0 + 128 WNB - 1
-// (WNB B blocks of 32 per wave: 2 for a full 256-column tile, 1 for a half
-// tile).  8 waves: 2 x 4, each 128 rows x 32 WNB columns.
-template <typename Out, bool kVec, int WNB>
-__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
-                                          const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k,
-                                          float ka, float kb, Out* __restrict__ out, int tm, int col0, uint8_t* lds) {
+// s_waitcnt with only the vector-memory counter limited (lgkm and exp left
+// open); the count's low four bits go to bits 3..0, the high two to 15..14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x3F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// A workgroup barrier that waits for this wave's LDS accesses only (a
+// __syncthreads would also wait for every load and store in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Output tiles of one workgroup: rounds r = 0, 1, ... of tile_of(r, tm, col0)
+// until it returns false.  Each tile covers rows 256 tm .. + 255 and columns
+// col0 .. col0 + 128 WNB - 1 (WNB B blocks of 32 per wave: 2 for a full
+// 256-column tile, 1 for a half tile), 8 waves as 2 x 4, each 128 rows x
+// 32 WNB columns.  Between two tiles the next tile's first two stages are
+// requested before the finished tile's output is stored, so that the stores
+// drain while the next tile's operands arrive; this takes a bf16 output
+// (the output slab then fits the third stage buffer) with 16-byte stores
+// (16 per wave, which the first waits of the next tile let pass).
+template <typename Out, bool kVec, int WNB, typename TileOf>
+__device__ __forceinline__ void gemm_tiles(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
+                                           const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k,
+                                           float ka, float kb, Out* __restrict__ out, uint8_t* lds, TileOf tile_of) {
   constexpr int kTileW = 128 * WNB;  // columns of the tile
+  constexpr int kOut = static_cast<int>(sizeof(Out));
+  constexpr int kPer = 16 / kOut;              // outputs per 16-byte chunk
+  constexpr int kLanesPerRow = 32 * WNB / kPer;
+  constexpr int kPitch = 32 * WNB * kOut + 16;  // slab row pitch in bytes
+  // Memory operations a wave issues after the next tile's first two stages,
+  // when those go first: the load of the next tile's scales into LDS and the
+  // epilogue's 16-byte stores.
+  constexpr int kAfterStages = 1 + 4 * (32 * kLanesPerRow / 64);
+  constexpr bool kOverlap = kVec && kOut == 2 && WNB == 2;
+  static_assert(!kOverlap || 8 * 32 * kPitch <= kStage, "bf16 slabs fit the third stage buffer");
+  static_assert(8 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   auto stage_mem = [&](auto bi) -> uint8_t* { return lds + decltype(bi)::value * kStage; };
+  // Clip scales of a tile: [0, 256) rows, [256, 512) columns, two buffers
+  // (tile r uses buffer r % 2, so that the next tile's can land while this
+  // tile's epilogue reads its own).
+  auto scales_mem = [&](int r) -> float* { return reinterpret_cast<float*>(lds + 3 * kStage) + (r & 1) * 512; };
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int cb0 = col0 >> 5;  // first B block of the tile
-
+  // The lane's addresses are derived from `lane` afresh in each phase of a
+  // tile (main loop, epilogue): `renew` hides its value from the compiler,
+  // so that it does not compute one phase's addresses ahead and keep them in
+  // registers through the other.
+  int lane = tid & 63;
+  auto renew = [&]() { asm volatile("" : "+v"(lane)); };
   const int chunks = k >> 7;
+  const int stages = chunks;
   const uint32_t rb_bytes = static_cast<uint32_t>(chunks) * kBlock;  // one 32-row block, all of k
   const int rb_a = (m + 31) >> 5, rb_b = (n + 31) >> 5;
-  const i32x4 ra = raw_rsrc(a + static_cast<size_t>(tm) * 8 * rb_bytes, min(rb_a - tm * 8, 8) * rb_bytes);
-  // (a half tile can lie wholly past n: then its windows are empty and every
-  // load reads zeros)
-  const int b_blocks = __builtin_amdgcn_readfirstlane(max(min(rb_b - cb0, 4 * WNB), 0));
-  const i32x4 rb = raw_rsrc(b + static_cast<size_t>(cb0) * rb_bytes, b_blocks * rb_bytes);
 
-  // Stage st into LDS: A's 8 blocks are 24 KB = 24 wave instructions, wave w
-  // issuing t = w + 8 u, u < 3.  B's 4 WNB blocks are 12 WNB instructions:
-  // for a full tile spread the same way; for a half tile (12) wave w issues
-  // t = (w + 8 u) % 12, u < 2, so waves 4..7 repeat four of them (the same
-  // bytes to the same place) and every wave issues the same number of loads.
+  struct Tile {
+    int tm, col0;
+    i32x4 ra, rb;
+  };
+  auto make_tile = [&](int tm, int col0) -> Tile {
+    Tile t;
+    t.tm = tm;
+    t.col0 = col0;
+    t.ra = raw_rsrc(a + static_cast<size_t>(tm) * 8 * rb_bytes, min(rb_a - tm * 8, 8) * rb_bytes);
+    // (a half tile can lie wholly past n: then its windows are empty and every
+    // load reads zeros)
+    const int cb0 = col0 >> 5;
+    const int b_blocks = __builtin_amdgcn_readfirstlane(max(min(rb_b - cb0, 4 * WNB), 0));
+    t.rb = raw_rsrc(b + static_cast<size_t>(cb0) * rb_bytes, b_blocks * rb_bytes);
+    return t;
+  };
+  // The tile's row and column clip scales into scales_mem(r): wave w < 4
+  // loads rows 64 w .. 64 w + 63, wave 4 + c columns 64 c .. 64 c + 63, one
+  // load into LDS each (entries past m or n read zero).
+  auto fetch_scales = [&](const Tile& t, int r) {
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(scales_mem(r))) + 256 * wave;
+    if (wave < 4) {
+      const int first = t.tm * kTileM + 64 * wave;
+      const int count = __builtin_amdgcn_readfirstlane(max(min(m - first, 64), 0));
+      dma4(base, lane * 4, raw_rsrc(sa + first, count * 4));
+    } else {
+      const int first = t.col0 + 64 * (wave - 4);
+      const int count = __builtin_amdgcn_readfirstlane(max(min(n - first, 64), 0));
+      dma4(base, lane * 4, raw_rsrc(sb + first, count * 4));
+    }
+  };
+
+  // Stage st of tile t into LDS: A's 8 blocks are 24 KB = 24 wave
+  // instructions, wave w issuing t = w + 8 u, u < 3.  B's 4 WNB blocks are
+  // 12 WNB instructions: for a full tile spread the same way; for a half tile
+  // (12) wave w issues t = (w + 8 u) % 12, u < 2, so waves 4..7 repeat four of
+  // them (the same bytes to the same place) and every wave issues the same
+  // number of loads.
   constexpr int kLoads = WNB == 2 ? 6 : 5;  // loads one wave issues per stage
-  auto fetch = [&](int st, auto bi) {
+  auto fetch = [&](const Tile& tl, int st, auto bi) {
     const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage_mem(bi)));
-    const i32x4 qa = ra, qb = rb;
+    const i32x4 qa = tl.ra, qb = tl.rb;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int t = wave + 8 * u, blk = t / 3, part = t % 3;
@@ -144,8 +212,6 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, const f
       }
     }
   };
-  // Wait until at most one stage's loads of this wave are in flight.
-  auto wait_one_stage = [&]() { wait_vmcnt<kLoads>(); };
 
   // Fragment (block rbk, k-half ks) of operand op: this lane's 24 bytes.
   auto frag = [&](auto bi, int op, int rbk, int ks) -> v8i {
@@ -155,146 +221,164 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, const f
                static_cast<int>(x1[1]), static_cast<int>(x2[0]), static_cast<int>(x2[1]), 0, 0};
   };
 
-  // acc[j][i]: 32 x 32 tile of the product B A^T for B block j and A block i,
-  // so lane l holds output row 32 i + l % 32 and four consecutive columns per
-  // register quad.
-  v16f acc[WNB][4];
-#pragma unroll
-  for (int j = 0; j < WNB; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = v16f{};
+  int tm0, col00;
+  if (!tile_of(0, tm0, col00)) return;
+  Tile cur = make_tile(tm0, col00);
+  fetch_scales(cur, 0);
+  fetch(cur, 0, I0{});
+  fetch(cur, stages > 1 ? 1 : 0, I1{});
+  bool stores_pending = false;  // the previous tile's output stores follow this tile's first two stages
 
-  // This tile's row (threads 0..255) and column (256..511) clip scales,
-  // loaded now so that the epilogue does not wait for them.
-  const bool row_side = tid < kTileM;
-  float my_scale;
-  {
-    const auto rsa = make_rsrc(sa + static_cast<size_t>(tm) * kTileM, min(m - tm * kTileM, kTileM) * 4);
-    const auto rsb = make_rsrc(sb + col0, max(min(n - col0, kTileW), 0) * 4);
-    my_scale = __builtin_bit_cast(float, row_side ? __builtin_amdgcn_raw_buffer_load_b32(rsa, tid * 4, 0, 0)
-                                                  : __builtin_amdgcn_raw_buffer_load_b32(rsb, (tid - kTileM) * 4, 0, 0));
-  }
-
-  const int stages = chunks;
-  fetch(0, I0{});
-  fetch(stages > 1 ? 1 : 0, I1{});
-  wait_one_stage();  // stage 0 has landed (stage 1 may be in flight)
-  __syncthreads();
-  v8i f0a[4], f0b[WNB], f1a[4], f1b[WNB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
-#pragma unroll
-  for (int j = 0; j < WNB; ++j) f0b[j] = frag(I0{}, 1, wn * WNB + j, 0);
-  // One stage: bi holds stage s, bn stage s + 1, b2 receives stage s + 2.
-  // b2 last held stage s - 1, whose reads every wave finished before the
-  // previous barrier.
-  auto step = [&](int s, auto bi, auto bn, auto b2) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f1a[i] = frag(bi, 0, wm * 4 + i, 1);
-#pragma unroll
-    for (int j = 0; j < WNB; ++j) f1b[j] = frag(bi, 1, wn * WNB + j, 1);
+  for (int r = 0;; ++r) {
+    // acc[j][i]: 32 x 32 tile of the product B A^T for B block j and A block
+    // i, so lane l holds output row 32 i + l % 32 and four consecutive
+    // columns per register quad.
+    v16f acc[WNB][4];
 #pragma unroll
     for (int j = 0; j < WNB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0b[j], f0a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
-    fetch(s + 2 < stages ? s + 2 : stages - 1, b2);
-    wait_one_stage();                   // stage s + 1 has landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // and this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f0a[i] = frag(bn, 0, wm * 4 + i, 0);
-#pragma unroll
-    for (int j = 0; j < WNB; ++j) f0b[j] = frag(bn, 1, wn * WNB + j, 0);
-#pragma unroll
-    for (int j = 0; j < WNB; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1b[j], f1a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
-  };
-  int s = 0;
-  for (; s + 3 <= stages; s += 3) {
-    step(s, I0{}, I1{}, I2{});
-    step(s + 1, I1{}, I2{}, I0{});
-    step(s + 2, I2{}, I0{}, I1{});
-  }
-  if (s < stages) step(s++, I0{}, I1{}, I2{});
-  if (s < stages) step(s++, I1{}, I2{}, I0{});
-  wait_vmcnt<0>();  // no load into LDS in flight before it is reused
-  __syncthreads();
+      for (int i = 0; i < 4; ++i) acc[j][i] = v16f{};
 
-  // Epilogue.  Row and column factors Delta = s * 2 / (L - 1) go to LDS.
-  float* fac = reinterpret_cast<float*>(lds);  // [0, 256): rows, [256, 512): columns
-  if (tid < kTileM + kTileW) fac[tid] = my_scale * (row_side ? ka : kb);
-  __syncthreads();
-  // Each wave stages a 32 x 32 WNB slab of its part in its own LDS region and
-  // writes it as whole row segments.
-  constexpr int kOut = static_cast<int>(sizeof(Out));
-  constexpr int kPitch = 32 * WNB * kOut + 16;  // slab row pitch in bytes
-  constexpr int kPer = 16 / kOut;              // outputs per 16-byte chunk
-  constexpr int kLanesPerRow = 32 * WNB / kPer;
-  static_assert(8 * 32 * kPitch <= 2 * kStage, "slabs fit in the second and third stage buffers");
-  uint8_t* slab = lds + kStage + wave * 32 * kPitch;  // the factors stay in the first
-  const int rows_left = m - tm * kTileM;
-  const auto rout = make_rsrc(out + static_cast<size_t>(tm) * kTileM * n,
-                              static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
-  const int r32 = lane & 31, h = lane >> 5;
-  // column factors of the lane's columns: 32 j + 8 q + 4 h + (0..3) of the wave's 32 WNB
-  float4 fbs[WNB][4];
+    renew();
+    // Stage 0 has landed (stage 1 and the previous tile's stores may be in flight).
+    if (kOverlap && stores_pending)
+      wait_vmcnt<kLoads + kAfterStages>();
+    else
+      wait_vmcnt<kLoads>();
+    lds_barrier();
+    v8i f0a[4], f0b[WNB], f1a[4], f1b[WNB];
 #pragma unroll
-  for (int j = 0; j < WNB; ++j)
+    for (int i = 0; i < 4; ++i) f0a[i] = frag(I0{}, 0, wm * 4 + i, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      fbs[j][q] = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 32 * WNB + 32 * j + 8 * q + 4 * h]);
+    for (int j = 0; j < WNB; ++j) f0b[j] = frag(I0{}, 1, wn * WNB + j, 0);
+    // One stage: bi holds stage s, bn stage s + 1, b2 receives stage s + 2.
+    // b2 last held stage s - 1, whose reads every wave finished before the
+    // previous barrier.  Stages past the last are fetched again (the last
+    // one), so that every stage's wait counts the same loads.
+    auto step = [&](int s, auto bi, auto bn, auto b2) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float fa = fac[wm * 128 + 32 * i + r32];
+      for (int i = 0; i < 4; ++i) f1a[i] = frag(bi, 0, wm * 4 + i, 1);
 #pragma unroll
-    for (int j = 0; j < WNB; ++j)
+      for (int j = 0; j < WNB; ++j) f1b[j] = frag(bi, 1, wn * WNB + j, 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 32 WNB
-        const float4 fb = fbs[j][q];
-        const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
-        const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
-        uint8_t* d = slab + r32 * kPitch + cl * kOut;
-        if constexpr (kOut == 4) {
-          *reinterpret_cast<u32x4*>(d) =
-              u32x4{__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
-        } else {
-          *reinterpret_cast<u32x2*>(d) =
-              u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        }
-      }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int j = 0; j < WNB; ++j)
 #pragma unroll
-    for (int t = 0; t < 32 * kLanesPerRow / 64; ++t) {
-      const int sr = t * (64 / kLanesPerRow) + lane / kLanesPerRow, sc = (lane % kLanesPerRow) * kPer;
-      const int row = wm * 128 + 32 * i + sr;  // within the tile
-      const int col = col0 + wn * 32 * WNB + sc;
-      const uint8_t* src = slab + sr * kPitch + sc * kOut;
-      if constexpr (kVec) {
-        // n is a multiple of kPer: a chunk is wholly inside or wholly past the row
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        const int off = col < n ? (row * n + col) * kOut : kNowhereOff;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
-      } else {
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0b[j], f0a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
+      fetch(cur, s + 2 < stages ? s + 2 : stages - 1, b2);
+      // stage s + 1 has landed (on the first stage the previous tile's
+      // scale load and stores, issued before this stage's loads, may still
+      // be in flight)
+      if (kOverlap && stores_pending && s == 0)
+        wait_vmcnt<kLoads + kAfterStages>();
+      else
+        wait_vmcnt<kLoads>();
+      lds_barrier();  // and every wave's LDS reads of stage s are done
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int off = col + e < n ? (row * n + col + e) * kOut : kNowhereOff;
+      for (int i = 0; i < 4; ++i) f0a[i] = frag(bn, 0, wm * 4 + i, 0);
+#pragma unroll
+      for (int j = 0; j < WNB; ++j) f0b[j] = frag(bn, 1, wn * WNB + j, 0);
+#pragma unroll
+      for (int j = 0; j < WNB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1b[j], f1a[i], acc[j][i], 2, 2, 0, 127, 0, 127);
+    };
+    int s = 0;
+    for (; s + 3 <= stages; s += 3) {
+      step(s, I0{}, I1{}, I2{});
+      step(s + 1, I1{}, I2{}, I0{});
+      step(s + 2, I2{}, I0{}, I1{});
+    }
+    if (s < stages) step(s++, I0{}, I1{}, I2{});
+    if (s < stages) step(s++, I1{}, I2{}, I0{});
+    wait_vmcnt<0>();  // no load into LDS in flight before it is reused
+    lds_barrier();
+
+    renew();
+    // The next tile: its first two stages go out before this tile's stores
+    // (only with kOverlap; otherwise after them), its scale once this
+    // tile's has been used.
+    int tm_n = 0, col0_n = 0;
+    const bool has_next = tile_of(r + 1, tm_n, col0_n);
+    const Tile next = has_next ? make_tile(tm_n, col0_n) : cur;
+    if (kOverlap && has_next) {
+      fetch(next, 0, I0{});
+      fetch(next, stages > 1 ? 1 : 0, I1{});
+    }
+
+    // Epilogue.  The row and column factors are Delta = s * 2 / (L - 1).
+    if (kOverlap && has_next) fetch_scales(next, r + 1);
+    const float* fac = scales_mem(r);
+    // Each wave stages a 32 x 32 WNB slab of its part in its own LDS region
+    // (the third stage buffer when the next tile's stages fill the first two)
+    // and writes it as whole row segments.
+    uint8_t* slab = lds + (kOverlap ? 2 : 1) * kStage + wave * 32 * kPitch;
+    const int rows_left = m - cur.tm * kTileM;
+    const auto rout = make_rsrc(out + static_cast<size_t>(cur.tm) * kTileM * n,
+                                static_cast<uint32_t>(min(rows_left, kTileM)) * static_cast<uint32_t>(n) * kOut);
+    const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float fa = fac[wm * 128 + 32 * i + r32] * ka;
+#pragma unroll
+      for (int j = 0; j < WNB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cl = 32 * j + 8 * q + 4 * h;  // column within the wave's 32 WNB
+          // column factors of the lane's columns cl .. cl + 3
+          const float4 sbv = *reinterpret_cast<const float4*>(&fac[kTileM + wn * 32 * WNB + cl]);
+          const float4 fb = make_float4(sbv.x * kb, sbv.y * kb, sbv.z * kb, sbv.w * kb);
+          const float y0 = acc[j][i][4 * q + 0] * (fa * fb.x), y1 = acc[j][i][4 * q + 1] * (fa * fb.y);
+          const float y2 = acc[j][i][4 * q + 2] * (fa * fb.z), y3 = acc[j][i][4 * q + 3] * (fa * fb.w);
+          uint8_t* d = slab + r32 * kPitch + cl * kOut;
           if constexpr (kOut == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src + 4 * e), rout, off, 0, 0);
+            *reinterpret_cast<u32x4*>(d) =
+                u32x4{__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
           } else {
-            __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const uint16_t*>(src + 2 * e), rout, off, 0, 0);
+            *reinterpret_cast<u32x2*>(d) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+          }
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 32 * kLanesPerRow / 64; ++t) {
+        const int sr = t * (64 / kLanesPerRow) + lane / kLanesPerRow, sc = (lane % kLanesPerRow) * kPer;
+        const int row = wm * 128 + 32 * i + sr;  // within the tile
+        const int col = cur.col0 + wn * 32 * WNB + sc;
+        const uint8_t* src = slab + sr * kPitch + sc * kOut;
+        if constexpr (kVec) {
+          // n is a multiple of kPer: a chunk is wholly inside or wholly past the row
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+          const int off = col < n ? (row * n + col) * kOut : kNowhereOff;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const int off = col + e < n ? (row * n + col + e) * kOut : kNowhereOff;
+            if constexpr (kOut == 4) {
+              __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src + 4 * e), rout, off, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const uint16_t*>(src + 2 * e), rout, off, 0, 0);
+            }
           }
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (!has_next) return;
+    if (!kOverlap) {
+      // every wave's slab reads are done before the next stages land there
+      lds_barrier();
+      fetch_scales(next, r + 1);
+      fetch(next, 0, I0{});
+      fetch(next, stages > 1 ? 1 : 0, I1{});
+    }
+    cur = next;
+    stores_pending = kOverlap;
   }
 }
 
@@ -307,31 +391,55 @@ __device__ __forceinline__ void tile_at(int pid, int tiles_m, int tiles_n, int& 
   tn = (pid % group) / gm;
 }
 
-// Full tiles (WNB = 2): workgroup w computes tile w of the first
-// `tile_count` tiles, after the XCD remap below.  Half tiles (WNB = 1):
-// workgroup w computes half w % 2 of tile first_tile + w / 2, for the tiles
-// of a last round that would hold at most half the compute units.
-template <typename Out, bool kVec, int WNB>
+// Full tiles (WNB = 2), tiles 0 .. tile_count - 1 of the tile order above.
+// Workgroups are dealt to the 8 XCDs round-robin; each XCD takes a
+// contiguous range of tiles, so that the tiles sharing operand blocks share
+// an L2.  Without kWalk every workgroup computes one tile (the last
+// tile_count % 8 keep their own index); with it the grid is a multiple of 8
+// workgroups that each walk their XCD's range, gridDim.x / 8 tiles per XCD
+// at a time.  Half tiles (WNB = 1): workgroup w computes half w % 2 of
+// tile first_tile + w / 2, for the tiles of a last round that would hold at
+// most half the compute units.
+template <typename Out, bool kVec, int WNB, bool kWalk = false>
 __global__ void __launch_bounds__(512, 1)
     quest_gemm_e2m3_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa, int m,
                            const uint8_t* __restrict__ b, const float* __restrict__ sb, int n, int k, float ka,
                            float kb, Out* __restrict__ out, int tile_count, int first_tile) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kStage + 2 * 2 * kTileM * 4];
   const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
-  int tm, tn;
   if constexpr (WNB == 2) {
-    // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
-    // contiguous range of tiles, so that the tiles sharing operand blocks
-    // share an L2.
-    int pid = blockIdx.x;
-    const int full = tile_count & ~7;
-    if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
-    tile_at(pid, tiles_m, tiles_n, tm, tn);
-    gemm_tile<Out, kVec, 2>(a, sa, m, b, sb, n, k, ka, kb, out, tm, tn * kTileN, lds);
+    const int bid = blockIdx.x;
+    if constexpr (!kWalk) {
+      gemm_tiles<Out, kVec, 2>(a, sa, m, b, sb, n, k, ka, kb, out, lds, [&](int r, int& tm, int& col0) {
+        if (r > 0) return false;
+        int pid = bid, tn;
+        const int full = tile_count & ~7;
+        if (pid < full) pid = (pid & 7) * (full >> 3) + (pid >> 3);
+        tile_at(pid, tiles_m, tiles_n, tm, tn);
+        col0 = tn * kTileN;
+        return true;
+      });
+    } else {
+      const int per_xcd = tile_count >> 3, per_round = static_cast<int>(gridDim.x) >> 3;
+      const int xcd = bid & 7, slot = bid >> 3;
+      gemm_tiles<Out, kVec, 2>(a, sa, m, b, sb, n, k, ka, kb, out, lds, [&](int r, int& tm, int& col0) {
+        const int q = r * per_round + slot;
+        if (q >= per_xcd) return false;
+        int tn;
+        tile_at(xcd * per_xcd + q, tiles_m, tiles_n, tm, tn);
+        col0 = tn * kTileN;
+        return true;
+      });
+    }
   } else {
     const int h = blockIdx.x;
-    tile_at(first_tile + (h >> 1), tiles_m, tiles_n, tm, tn);
-    gemm_tile<Out, kVec, 1>(a, sa, m, b, sb, n, k, ka, kb, out, tm, tn * kTileN + (h & 1) * (kTileN / 2), lds);
+    gemm_tiles<Out, kVec, 1>(a, sa, m, b, sb, n, k, ka, kb, out, lds, [&](int r, int& tm, int& col0) {
+      if (r > 0) return false;
+      int tn;
+      tile_at(first_tile + (h >> 1), tiles_m, tiles_n, tm, tn);
+      col0 = tn * kTileN + (h & 1) * (kTileN / 2);
+      return true;
+    });
   }
 }
 
@@ -357,9 +465,25 @@ hipError_t launch(const GemmLaunch& g) {
   const int cus = device_cus();
   const int last = tiles % cus;
   const int full_tiles = tiles > cus && last > 0 && 2 * last <= cus ? tiles - last : tiles;
-  hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec, 2>), dim3(full_tiles), dim3(512), 0,
-                     static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
-                     static_cast<Out*>(g.out), full_tiles, 0);
+  // Several tiles per workgroup (the next tile's first stages requested
+  // before the last one's stores) for a bf16 output of whole 16-byte chunks
+  // and at least three stages, when the full tiles are more than one round
+  // and split evenly over the XCDs.
+  const bool walk = sizeof(Out) == 2 && kVec && g.k >= 3 * 128 && full_tiles > cus && full_tiles % 8 == 0 &&
+                    cus % 8 == 0;
+  bool launched = false;
+  if constexpr (sizeof(Out) == 2 && kVec) {
+    if (walk) {
+      hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec, 2, true>), dim3(cus), dim3(512), 0,
+                         static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
+                         static_cast<Out*>(g.out), full_tiles, 0);
+      launched = true;
+    }
+  }
+  if (!launched)
+    hipLaunchKernelGGL((quest_gemm_e2m3_kernel<Out, kVec, 2>), dim3(full_tiles), dim3(512), 0,
+                       static_cast<hipStream_t>(g.stream), g.a, g.sa, g.m, g.b, g.sb, g.n, g.k, g.ka, g.kb,
+                       static_cast<Out*>(g.out), full_tiles, 0);
   if (full_tiles < tiles) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

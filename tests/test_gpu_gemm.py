@@ -300,6 +300,38 @@ def test_block_products_full_size_sampled(dev, name, act, wt):
 
 
 # ---------------------------------------------------------------------------
+# Products of more full tiles than compute units, whose workgroups each walk
+# several tiles (bf16 output): ragged m and n, a short last round split into
+# half tiles, sampled outputs against the oracle and a guard band around the
+# output.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k", [(10000, 3000, 1024), (16484, 2048, 2048), (16384, 5632, 384)])
+def test_product_tile_walk_sampled(dev, m, n, k):
+    log(f"tile-walk product {m}x{k} by {n}x{k}")
+    x = make_tensor(TensorSpec("w.x", m, k, "bf16", "student_t", 4, 9300 + m, outlier_cols=k // 100,
+                               outlier_scale=20.0), dev)
+    w = make_tensor(TensorSpec("w.w", n, k, "bf16", "normal", 0.02, 9400 + n), dev)
+    _, sx, _, ox = qa.quantize_fwd_op(x, 128, 4)
+    _, sw, _, ow = qa.quantize_fwd_op(w, 128, 4)
+    guard = 4096
+    buf = torch.full((m * n + 2 * guard,), -7.0, dtype=torch.bfloat16, device=dev)
+    y = buf[guard:guard + m * n].view(m, n)
+    qa.gemm(ox, sx, m, 4, ow, sw, n, 4, k, out=y)
+    torch.cuda.synchronize()
+    assert bool((buf[:guard] == -7.0).all()) and bool((buf[guard + m * n:] == -7.0).all())
+    ri = sample(m, 24, 9500 + m)
+    rj = sample(n, 24, 9600 + n)
+    xs = to_float64(x.index_select(0, torch.as_tensor(ri, device=dev)))
+    ws = to_float64(w.index_select(0, torch.as_tensor(rj, device=dev)))
+    f = qo.qat_linear_fwd(xs, ws, 128, 4, 4)
+    skip = band_rows(f["fx"], 4)[:, None] | band_rows(f["fw"], 4)[None, :]
+    got = y.index_select(0, torch.as_tensor(ri, device=dev)).index_select(1, torch.as_tensor(rj, device=dev))
+    ratio = check_product(got, f["y"], 4e-3 + 1e-5, skip, abs_sum=np.abs(f["qx"]) @ np.abs(f["qw"]).T, k=k)
+    assert not bool(torch.isnan(y).any())
+    log(f"tile walk ok: {len(ri)}x{len(rj)} sampled outputs, max rel {ratio:.3g}")
+
+
+# ---------------------------------------------------------------------------
 # Stored codes to the operand (quest_codes_to_operand): the same bytes as the
 # operand quest_quantize_fwd_op writes with those codes on every row of the
 # tensor (the padding rows of the last 32-row block are left alone by the
