@@ -425,41 +425,49 @@ def qat_linear_step(torch, dev, reps):
     operands rebuilt from their codes, the two BF16 gradient products and two
     trust-masked backwards) against torch's BF16 linear, each as
     `reps` back-to-back forward + backward passes (torch.autograd.grad, so no
-    gradient accumulation) between events on the launch stream.
+    gradient accumulation) between events on the launch stream, over rotating
+    copies of the inputs.
     """
     from quantization_aware_amd.linear import quest_linear
     from quest_inputs import LAYER_ACT_2048, TensorSpec, layer_products, make_tensor
 
     wt = [w for name, _, w in layer_products() if name == "q"][0]
-    x = make_tensor(LAYER_ACT_2048, dev).requires_grad_(True)
-    w = make_tensor(wt, dev).requires_grad_(True)
-    dy = make_tensor(TensorSpec("bench.qat.dy", x.shape[0], w.shape[0], "bf16", "normal", 1e-3, 9900), dev)
+    x0 = make_tensor(LAYER_ACT_2048, dev)
+    w0 = make_tensor(wt, dev)
+    dy0 = make_tensor(TensorSpec("bench.qat.dy", x0.shape[0], w0.shape[0], "bf16", "normal", 1e-3, 9900), dev)
+    # Copies of x, w and dy (136 MiB a set) rotate, so that more than 512 MiB is
+    # touched between two uses of one set and no step finds its inputs in the
+    # 256 MB last-level cache.
+    sets = 4
+    xs = [x0.clone().requires_grad_(True) for _ in range(sets)]
+    ws = [w0.clone().requires_grad_(True) for _ in range(sets)]
+    dys = [dy0.clone() for _ in range(sets)]
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
+        for i in range(3):
+            fn(i % sets)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(reps):
-            fn()
+        for i in range(reps):
+            fn(i % sets)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    def quest():
-        y = quest_linear(x, w, block=BLOCK, bits_x=4, bits_w=4, compute_dtype=torch.bfloat16)
-        torch.autograd.grad(y, (x, w), dy)
+    def quest(i):
+        y = quest_linear(xs[i], ws[i], block=BLOCK, bits_x=4, bits_w=4, compute_dtype=torch.bfloat16)
+        torch.autograd.grad(y, (xs[i], ws[i]), dys[i])
 
-    def bf16():
-        y = torch.nn.functional.linear(x, w)
-        torch.autograd.grad(y, (x, w), dy)
+    def bf16(i):
+        y = torch.nn.functional.linear(xs[i], ws[i])
+        torch.autograd.grad(y, (xs[i], ws[i]), dys[i])
 
     t_q, t_b = timed(quest), timed(bf16)
-    return {"layer": "q projection", "tokens": x.shape[0], "in_features": x.shape[1], "out_features": w.shape[0],
+    return {"layer": "q projection", "tokens": x0.shape[0], "in_features": x0.shape[1], "out_features": w0.shape[0],
             "bits": 4, "block": BLOCK, "compute_dtype": "bf16", "quest_step_us": 1000 * t_q,
-            "bf16_step_us": 1000 * t_b, "quest_over_bf16": t_q / t_b,
+            "bf16_step_us": 1000 * t_b, "quest_over_bf16": t_q / t_b, "input_sets": sets,
             "note": "training step of the QuEST layer (quantisers, FP6 forward product, BF16 gradient products, "
                     "trust backwards) vs a plain BF16 linear layer"}
 
