@@ -130,8 +130,9 @@ __device__ __forceinline__ void wave_load_runs(const void* base, int64_t first_p
 }
 
 // Store the 64 runs of a wave (lane l holds the 4U dwords of run
-// first_piece / U + l); pieces at or past total_pieces are dropped.
-template <int U>
+// first_piece / U + l); pieces at or past total_pieces are dropped.  P is
+// the stores' cache policy.
+template <int U, int P = kNonTemporal>
 __device__ __forceinline__ void wave_store_runs(void* base, int64_t first_piece, int64_t total_pieces, int lane,
                                                 u32x4* stage, const uint32_t (&in)[4 * U]) {
   __builtin_amdgcn_wave_barrier();
@@ -151,7 +152,7 @@ __device__ __forceinline__ void wave_store_runs(void* base, int64_t first_piece,
     const int q = 64 * k + lane;
     const int rr = q / U, c = q % U;
     const u32x4 t = stage[64 * c + (rr ^ stage_xor<U>(c))];
-    __builtin_amdgcn_raw_buffer_store_b128(t, r, q * 16, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, q * 16, 0, P);
   }
 }
 

@@ -1068,7 +1068,11 @@ __global__ void __launch_bounds__(256)
   }
   uint32_t raw[4 * U];
   narrow_run(v, raw);
-  wave_store_runs<U>(out, run0 * U, total_runs * U, lane, stage_all[wave], raw);
+  // Default cache policy: a rebuilt operand is read by the product that
+  // follows (the QAT layer's gradient products), which then finds it in the
+  // last-level cache (a training step of the layer 12 us faster than with
+  // non-temporal stores).
+  wave_store_runs<U, 0>(out, run0 * U, total_runs * U, lane, stage_all[wave], raw);
 }
 
 // ----------------------------------------------------------------------------
