@@ -98,25 +98,25 @@ class QuestLinearFunction(torch.autograd.Function):
         if ctx.fp6:
             cx, sx, cw, sw, mask_x, mask_w = ctx.saved_tensors
             n, m, k, bits_x, bits_w, compute_dtype = ctx.dims
-            # Q(x) for the weight gradient and Q(w) for the input gradient are
-            # rebuilt from the codes, each just before its product (the weight
-            # gradient first: the activation-sized Q(x) is freed before Q(w)
-            # is built, and each product reads an operand just written).
-            rebuild_x = lambda: dequantize(cx, sx, n, k, bits_x, out_dtype=compute_dtype)
-            rebuild_w = lambda: dequantize(cw, sw, m, k, bits_w, out_dtype=compute_dtype)
+            # Q(x) for the weight gradient and Q(w) for the input gradient,
+            # rebuilt from the codes (both first: the rebuilds keep the GPU
+            # busy while the host sets up the products)
+            qx = dequantize(cx, sx, n, k, bits_x, out_dtype=compute_dtype) if ctx.needs_input_grad[1] else None
+            qw = dequantize(cw, sw, m, k, bits_w, out_dtype=compute_dtype) if ctx.needs_input_grad[0] else None
         else:
             qx, qw, mask_x, mask_w = ctx.saved_tensors
             compute_dtype = qx.dtype
-            rebuild_x, rebuild_w = lambda: qx, lambda: qw
         dy = dy.to(compute_dtype).contiguous()
         dx = dw = None
+        # The weight gradient first: its product reads Q(x) just after the
+        # rebuild wrote it, while it is still in the last-level cache.
         if ctx.needs_input_grad[1]:
             # gradient reaching Q(w), Hadamard domain (a 2-D product with a
             # transposed left operand, as torch's own linear backward computes it)
-            g = torch.mm(dy.t(), rebuild_x())
+            g = torch.mm(dy.t(), qx)
             dw = trust_bwd(g, mask_w, ctx.block, out=g).to(ctx.w_dtype)
         if ctx.needs_input_grad[0]:
-            g = torch.mm(dy, rebuild_w())  # gradient reaching Q(x), Hadamard domain
+            g = torch.mm(dy, qw)  # gradient reaching Q(x), Hadamard domain
             dx = trust_bwd(g, mask_x, ctx.block, out=g).to(ctx.x_dtype)
         return dx, dw, None, None, None, None, None, None, None
 
