@@ -265,8 +265,8 @@ def config_runs(lib, qa, torch, dev, reps, names):
         rec = {"workload": wl.description,
                "grouped": entry(timed(grouped, n), alg, elements),
                "all_seven": entry(timed(all_seven, n), alg, elements),
-               "note": "grouped: one quest_quantize_fwd_group call (q, k, v, o, gate, up share one launch; down, "
-                       "5632 columns, its own); all_seven: seven quest_quantize_fwd calls",
+               "note": "grouped: one quest_quantize_fwd_group call (one launch: the tiles of q, k, v, o, gate, up, "
+                       "then down's rows); all_seven: seven quest_quantize_fwd calls",
                "buffer_sets": n, "per_tensor_us": {}}
         for j, spec in enumerate(wl.fwd):
             rec["per_tensor_us"][spec.name.split(".")[1]] = round(timed(lambda i: calls[i][j](), n), 3)

@@ -124,9 +124,11 @@ quest_status quest_quantize_fwd(const void* x, quest_dtype x_dtype, int64_t rows
  * (same block, bit width and input dtype), bit for bit.  A quantisation-aware
  * training step quantises every weight of a model (pith.science review of
  * QuEST, "What carries the argument": the quantiser is applied to weights and
- * activations in every forward pass); the library launches the bf16 tensors
- * whose rows have 512, 1024 or 2048 entries (b <= 4) together, one launch
- * per width for up to eight tensors, and the others one by one.
+ * activations in every forward pass); with b <= 4 the library launches the
+ * bf16 tensors whose rows have 512, 1024 or 2048 entries together (one
+ * launch per width for up to eight tensors) and adds those whose rows have
+ * 2560 to 8192 entries (a multiple of 512; up to four per launch) to the
+ * first of these launches, and launches the others one by one.
  *
  *   tensors  host array of `count` descriptors, read during the call only;
  *            each names x, rows, cols, codes, scale and mask as the

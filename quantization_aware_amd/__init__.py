@@ -244,8 +244,8 @@ def quantize_fwd_group(xs, block: int, b: int, stream=None):
     """quantize_fwd of several 2-D tensors of one dtype and device in one call (quest_quantize_fwd_group).
 
     Returns a list of (codes, scale, mask), one per tensor, equal to what
-    quantize_fwd returns for each.  Tensors of 512, 1024 or 2048 bf16 columns
-    (b <= 4) share launches.
+    quantize_fwd returns for each.  bf16 tensors (b <= 4) of 512, 1024 or 2048
+    columns, and of 2560 to 8192 columns (a multiple of 512), share launches.
     """
     lib = load_library()
     xs = list(xs)

@@ -264,15 +264,20 @@ quest_status quest_quantize_fwd_group(const quest_fwd_tensor* tensors, int count
   std::call_once(g_env_once, read_env);
   const int lb = log2_block(block);
   const double alpha = quest_fit_alpha(b);
-  // bf16 rows of 512, 1024 or 2048 entries (b <= 4) go in grouped launches,
-  // one per width; everything else as quest_quantize_fwd.
-  std::vector<quest::FwdGroupItem> group[3];
+  // bf16 tensors with b <= 4 go in grouped launches: rows of 512, 1024 or
+  // 2048 entries one launch per width, rows of 2560 to 8192 entries (a
+  // multiple of 512) with the first of them (or on their own); everything
+  // else as quest_quantize_fwd.
+  std::vector<quest::FwdGroupItem> group[3], wide;
+  const bool grouped = x_dtype == QUEST_BF16 && b <= 4 && g_allow_mfma;
   for (int i = 0; i < count; ++i) {
     const quest_fwd_tensor& t = tensors[i];
     if (t.rows == 0) continue;
-    const int w = t.cols == 512 ? 0 : t.cols == 1024 ? 1 : t.cols == 2048 ? 2 : -1;
-    if (x_dtype == QUEST_BF16 && b <= 4 && g_allow_mfma && w >= 0) {
-      group[w].push_back({t.x, t.rows, t.codes, t.scale, t.mask});
+    const quest::FwdGroupItem item = {t.x, t.rows, t.cols, t.codes, t.scale, t.mask};
+    if (grouped && quest::fwd_group_tile_cols(t.cols)) {
+      group[t.cols == 512 ? 0 : t.cols == 1024 ? 1 : 2].push_back(item);
+    } else if (grouped && quest::fwd_group_wide_cols(t.cols)) {
+      wide.push_back(item);
     } else {
       const quest_status st = quantize_fwd_common(t.x, x_dtype, t.rows, t.cols, block, b, 1.0, t.codes, true, t.scale,
                                                   t.mask, true, nullptr, QUEST_BF16, false, nullptr, stream);
@@ -281,7 +286,14 @@ quest_status quest_quantize_fwd_group(const quest_fwd_tensor* tensors, int count
   }
   for (int w = 0; w < 3; ++w) {
     if (group[w].empty()) continue;
-    const hipError_t e = quest::launch_fwd_group(group[w].data(), static_cast<int>(group[w].size()), 512 << w, lb, b,
+    const hipError_t e = quest::launch_fwd_group(group[w].data(), static_cast<int>(group[w].size()), 512 << w,
+                                                 wide.data(), static_cast<int>(wide.size()), lb, b, alpha,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return QUEST_EHIP;
+    wide.clear();
+  }
+  if (!wide.empty()) {
+    const hipError_t e = quest::launch_fwd_group(nullptr, 0, 2048, wide.data(), static_cast<int>(wide.size()), lb, b,
                                                  alpha, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return QUEST_EHIP;
   }

@@ -1,5 +1,5 @@
 // Forward quantisation with no dequantised output, for bf16 and fp32 inputs,
-// and the grouped forward of several bf16 tensors of one width.
+// and the grouped forward of several bf16 tensors.
 #include "quest_kernels.h"
 
 namespace quest {
@@ -23,10 +23,11 @@ hipError_t group_bits(const FwdGroup& g, int64_t cols, int bits, double alpha, h
 
 }  // namespace
 
-hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, int log_block, int bits, double alpha,
-                            hipStream_t stream) {
+hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, const FwdGroupItem* wide,
+                            int wide_count, int log_block, int bits, double alpha, hipStream_t stream) {
   const int64_t runs_per_row = cols / RUN;
-  for (int first = 0; first < count; first += kFwdGroupMax) {
+  int first = 0, wfirst = 0;
+  while (first < count || wfirst < wide_count) {
     FwdGroup g = {};
     g.count = count - first < kFwdGroupMax ? count - first : kFwdGroupMax;
     int64_t tiles = 0;
@@ -41,6 +42,22 @@ hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, 
       tiles += (g.total_runs[i] + 63) / 64;
     }
     g.first_tile[g.count] = tiles;
+    g.wide_count = wide_count - wfirst < kFwdGroupWideMax ? wide_count - wfirst : kFwdGroupWideMax;
+    int64_t wrows = 0;
+    for (int i = 0; i < g.wide_count; ++i) {
+      const FwdGroupItem& it = wide[wfirst + i];
+      g.wide_first_row[i] = wrows;
+      g.wide_runs[i] = static_cast<int>(it.cols / RUN);
+      g.wide_inv_cols[i] = static_cast<float>(1.0 / double(it.cols));
+      g.wide_x[i] = static_cast<const uint16_t*>(it.x);
+      g.wide_codes[i] = it.codes;
+      g.wide_scale[i] = it.scale;
+      g.wide_mask[i] = reinterpret_cast<uint32_t*>(it.mask);
+      wrows += it.rows;
+    }
+    g.wide_first_row[g.wide_count] = wrows;
+    first += g.count;
+    wfirst += g.wide_count;
     hipError_t e;
     switch (log_block) {
       case 6: e = group_bits<6>(g, cols, bits, alpha, stream); break;

@@ -716,50 +716,36 @@ __global__ void __launch_bounds__(256)
                                                  opstage);
 }
 
-// Several tensors of one width in one launch (quest_quantize_fwd_group):
-// each tensor's tiles follow the previous tensor's, and a wave finds its
-// tensor by comparing its tile with the running tile counts (a scan over
-// compile-time indices, so the table stays in scalar registers).  Per
-// tensor the work is quest_fwd_mfma_kernel's; a workgroup may span two
-// tensors (no barrier in this path).
+// Several tensors in one launch (quest_quantize_fwd_group): tensors of one
+// width of at most 2048 columns, each tensor's tiles following the previous
+// tensor's (a wave finds its tensor by comparing its tile with the running
+// tile counts: a scan over compile-time indices, so the table stays in
+// scalar registers; per tensor the work is quest_fwd_mfma_kernel's, and a
+// workgroup may span two tensors, with no barrier in this path), then the
+// rows of wider tensors (2560 to 8192 columns), one row per workgroup as in
+// the matrix-core row kernel.
 constexpr int kFwdGroupMax = 8;
+constexpr int kFwdGroupWideMax = 4;
 
 struct FwdGroup {
-  int count;                               // tensors in this launch, 1 .. kFwdGroupMax
+  int count;                               // tensors in this launch, 0 .. kFwdGroupMax
   int64_t first_tile[kFwdGroupMax + 1];    // running tile counts; first_tile[count] = all tiles
   int64_t total_runs[kFwdGroupMax];
   const uint16_t* x[kFwdGroupMax];
   uint8_t* codes[kFwdGroupMax];
   float* scale[kFwdGroupMax];
   uint32_t* mask[kFwdGroupMax];
+  // Wide tensors (rows of 16 m runs, 4 < m <= 16): one row per workgroup,
+  // after the tile workgroups.
+  int wide_count;                               // 0 .. kFwdGroupWideMax
+  int64_t wide_first_row[kFwdGroupWideMax + 1];  // running row counts
+  int wide_runs[kFwdGroupWideMax];               // runs per row
+  float wide_inv_cols[kFwdGroupWideMax];
+  const uint16_t* wide_x[kFwdGroupWideMax];
+  uint8_t* wide_codes[kFwdGroupWideMax];
+  float* wide_scale[kFwdGroupWideMax];
+  uint32_t* wide_mask[kFwdGroupWideMax];
 };
-
-template <int LOGN, int B, int LOGR>
-__global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, FwdConsts k) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
-  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const uint16_t* x = g.x[0];
-  uint8_t* codes = g.codes[0];
-  float* scale = g.scale[0];
-  uint32_t* mask = g.mask[0];
-  int64_t runs = g.total_runs[0], first = 0, end = g.first_tile[1];
-#pragma unroll
-  for (int i = 1; i < kFwdGroupMax; ++i) {
-    if (i < g.count && tile >= g.first_tile[i]) {
-      x = g.x[i];
-      codes = g.codes[i];
-      scale = g.scale[i];
-      mask = g.mask[i];
-      runs = g.total_runs[i];
-      first = g.first_tile[i];
-      end = g.first_tile[i + 1];
-    }
-  }
-  if (tile >= end) return;
-  fwd_mfma_tile<LOGN, B, LOGR, void, true>(x, runs, k, codes, scale, mask, nullptr, tile - first, lane, wave,
-                                           nullptr);
-}
 
 // Dynamic LDS of the row-per-workgroup kernels (sized at launch).
 extern __shared__ u32x4 rows_lds[];
@@ -775,13 +761,11 @@ extern __shared__ u32x4 rows_lds[];
 // block of rows (no grid-stride loop): with a barrier per block, letting the
 // hardware refill compute units as workgroups finish hides latency better
 // than a resident loop.
-template <int LOGN, int B, typename Dq, bool kQuant = true>
-__global__ void __launch_bounds__(1024)
-    quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
-                               FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
-                               uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
-  __shared__ float group_ss[64];
-  const int64_t wg = fwd_wg_index<Dq>();
+template <int LOGN, int B, typename Dq, bool kQuant>
+__device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row,
+                                              int rows_per_wg, const FwdConsts& k, uint8_t* __restrict__ codes,
+                                              float* __restrict__ scale, uint32_t* __restrict__ mask,
+                                              Dq* __restrict__ dq, int64_t wg, float* group_ss) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t total_runs = rows * runs_per_row;
@@ -872,6 +856,61 @@ __global__ void __launch_bounds__(1024)
       window_at(scale, wg * rows_per_wg * 4, rows * 4, rows_per_wg * 4);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), scale_r, first ? my_row * 4 : kNowhere, 0, 0);
 }
+
+template <int LOGN, int B, typename Dq, bool kQuant = true>
+__global__ void __launch_bounds__(1024)
+    quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
+                               FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
+                               uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
+  __shared__ float group_ss[64];
+  fwd_mfma_rows<LOGN, B, Dq, kQuant>(x, rows, runs_per_row, rows_per_wg, k, codes, scale, mask, dq,
+                                     fwd_wg_index<Dq>(), group_ss);
+}
+
+template <int LOGN, int B, int LOGR>
+__global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, FwdConsts k) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t tile_wgs = (g.first_tile[g.count] + 3) / 4;
+  if (static_cast<int64_t>(blockIdx.x) >= tile_wgs) {
+    // A row of a wide tensor: the row kernel's work with one row per
+    // workgroup of four waves (runs past the row read zeros, store nothing).
+    __shared__ float group_ss[64];
+    const int64_t row = static_cast<int64_t>(blockIdx.x) - tile_wgs;
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kFwdGroupWideMax; ++j)
+      if (j < g.wide_count && row >= g.wide_first_row[j]) i = j;
+    FwdConsts kw = k;
+    kw.inv_cols = g.wide_inv_cols[i];
+    fwd_mfma_rows<LOGN, B, void, true>(g.wide_x[i], g.wide_first_row[i + 1] - g.wide_first_row[i], g.wide_runs[i], 1,
+                                       kw, g.wide_codes[i], g.wide_scale[i], g.wide_mask[i], nullptr,
+                                       row - g.wide_first_row[i], group_ss);
+    return;
+  }
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const uint16_t* x = g.x[0];
+  uint8_t* codes = g.codes[0];
+  float* scale = g.scale[0];
+  uint32_t* mask = g.mask[0];
+  int64_t runs = g.total_runs[0], first = 0, end = g.first_tile[1];
+#pragma unroll
+  for (int i = 1; i < kFwdGroupMax; ++i) {
+    if (i < g.count && tile >= g.first_tile[i]) {
+      x = g.x[i];
+      codes = g.codes[i];
+      scale = g.scale[i];
+      mask = g.mask[i];
+      runs = g.total_runs[i];
+      first = g.first_tile[i];
+      end = g.first_tile[i + 1];
+    }
+  }
+  if (tile >= end) return;
+  fwd_mfma_tile<LOGN, B, LOGR, void, true>(x, runs, k, codes, scale, mask, nullptr, tile - first, lane, wave,
+                                           nullptr);
+}
+
 
 // LDS of the row-per-workgroup kernels, sized at launch by their wave count:
 // per wave a staging area of 64 * US 16-byte slots, then one float per lane
@@ -1150,12 +1189,13 @@ FwdConsts fwd_consts(double alpha, double trust, int64_t cols) {
   return k;
 }
 
-// One grouped launch: every tensor of `g` has rows of `cols` entries, cols
-// 512, 1024 or 2048 (16, 32 or 64 runs), bf16, b <= 4.
+// One grouped launch: every tile tensor of `g` has rows of `cols` entries,
+// cols 512, 1024 or 2048 (16, 32 or 64 runs; any of them when g has no tile
+// tensor), and its wide tensors rows of 2560 to 8192 entries; bf16, b <= 4.
 template <int LOGN, int B>
 hipError_t fwd_group_dispatch(const FwdGroup& g, int64_t cols, double alpha, hipStream_t stream) {
   const FwdConsts k = fwd_consts<LOGN, B>(alpha, 1.0, cols);
-  const dim3 grid(static_cast<uint32_t>((g.first_tile[g.count] + 3) / 4));
+  const dim3 grid(static_cast<uint32_t>((g.first_tile[g.count] + 3) / 4 + g.wide_first_row[g.wide_count]));
   switch (cols / RUN) {
     case 16:
       hipLaunchKernelGGL((quest_fwd_mfma_group_kernel<LOGN, B, 4>), grid, dim3(256), 0, stream, g, k);

@@ -35,16 +35,24 @@ hipError_t launch_fwd_op(const void* x, int x_is_bf16, int log_block, int bits, 
 struct FwdGroupItem {
   const void* x;  // bf16
   int64_t rows;
+  int64_t cols;
   uint8_t* codes;
   float* scale;
   uint8_t* mask;
 };
 
-// The forward (trust 1) of `count` bf16 tensors whose rows all have `cols`
-// entries, cols 512, 1024 or 2048, bits <= 4, in launches of at most eight
-// tensors; rows >= 1 for every item.  All arguments already validated.
-hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, int log_block, int bits, double alpha,
-                            hipStream_t stream);
+// Whether a bf16 tensor of `cols` entries per row (bits <= 4) takes the
+// grouped launch: as a tile tensor (512, 1024, 2048) or as a wide one (a
+// multiple of 512 from 2560 to 8192).
+inline bool fwd_group_tile_cols(int64_t cols) { return cols == 512 || cols == 1024 || cols == 2048; }
+inline bool fwd_group_wide_cols(int64_t cols) { return cols > 2048 && cols <= 8192 && cols % 512 == 0; }
+
+// The forward (trust 1) of bf16 tensors, bits <= 4: `count` tile tensors
+// whose rows all have `cols` entries (512, 1024 or 2048) and `wide_count`
+// wide tensors, in launches of at most eight tile and four wide tensors;
+// rows >= 1 for every item.  All arguments already validated.
+hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, const FwdGroupItem* wide,
+                            int wide_count, int log_block, int bits, double alpha, hipStream_t stream);
 
 // Packed codes (bits <= 4, cols a multiple of 128) to the tiled FP6 operand.
 hipError_t launch_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint8_t* operand,

@@ -496,10 +496,12 @@ def test_valu_bwd_switch_matches_oracle_and_mfma(dev, tmp_path, rows, cols, bloc
 # ---------------------------------------------------------------------------
 # Grouped forward (quest_quantize_fwd_group): every tensor's codes, scale and
 # mask equal quest_quantize_fwd's bit for bit, whether it shares a launch
-# (bf16, 512 / 1024 / 2048 columns, b <= 4) or takes its own.
+# (bf16, b <= 4: 512 / 1024 / 2048 columns by tiles, 2560 to 8192 columns a
+# row per workgroup) or takes its own.
 # ---------------------------------------------------------------------------
 GROUP_SHAPES = [(2048, 2048), (77, 2048), (1, 2048), (300, 512), (5, 512), (129, 1024), (96, 5632), (33, 256),
-                (2048, 1024), (3, 2048), (64, 2048), (1000, 512), (0, 2048), (17, 640)]
+                (2048, 1024), (3, 2048), (64, 2048), (1000, 512), (0, 2048), (17, 640), (33, 2560), (5, 8192),
+                (20, 3072)]
 
 
 @pytest.mark.parametrize("dt,b,block", [("bf16", 4, 128), ("bf16", 1, 64), ("bf16", 3, 256), ("f32", 4, 128),
@@ -523,6 +525,22 @@ def test_group_equals_single_calls(dev, dt, b, block):
         x64 = to_float64(xs[i]) if dt == "bf16" else xs[i].cpu().numpy().astype(np.float64)
         c, sc, m = (t.cpu().numpy() for t in got[i])
         check_fwd(x64, block, b, c, sc, m)
+
+
+def test_group_wide_only_and_many_wide(dev):
+    """Wide tensors alone (no tile tensor in the call) and more of them than one launch takes (six wide
+    tensors: a launch of four, then one of two), with a tile tensor in the second call."""
+    shapes = [(40, 5632), (3, 2560), (65, 4096), (1, 8192), (9, 3584), (17, 5632)]
+    xs = [make_tensor(TensorSpec(f"gw{i}", r, c, "bf16", "student_t", 4, 8600 + i, outlier_cols=4,
+                                 outlier_scale=20.0), dev) for i, (r, c) in enumerate(shapes)]
+    for extra in ([], [make_tensor(TensorSpec("gw.t", 70, 2048, "bf16", "normal", 1.0, 8690), dev)]):
+        got = qa.quantize_fwd_group(xs + extra, 128, 4)
+        for i, x in enumerate(xs + extra):
+            ref = qa.quantize_fwd(x, 128, 4)
+            torch.cuda.synchronize()
+            for name, g_, r_ in zip(("codes", "scale", "mask"), got[i], ref):
+                assert torch.equal(g_, r_), f"tensor {i} {tuple(x.shape)}: {name} differs from quest_quantize_fwd"
+    check_fwd(to_float64(xs[0]), 128, 4, *(t.cpu().numpy() for t in got[0]))
 
 
 def test_group_c3_weights_equal_single_calls(dev):

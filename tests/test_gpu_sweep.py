@@ -157,7 +157,7 @@ def test_sweep_group(dev, case):
     block = int(rng.choice([64, 128, 256]))
     b = int(rng.integers(1, 9))
     dt = "bf16" if rng.random() < 0.8 else "f32"
-    widths = [c for c in (512, 1024, 2048, 256, 640, 5632, 1536) if c % block == 0]
+    widths = [c for c in (512, 1024, 2048, 256, 640, 5632, 1536, 2560, 8192) if c % block == 0]
     count = int(rng.integers(1, 13))
     shapes = [(int(rng.integers(0, 300)) if rng.random() < 0.9 else 0, int(rng.choice(widths))) for _ in range(count)]
     log(f"group case {case}: {count} {dt} tensors, block {block}, b={b}: {shapes}")
