@@ -765,7 +765,8 @@ template <int LOGN, int B, typename Dq, bool kQuant>
 __device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row,
                                               int rows_per_wg, const FwdConsts& k, uint8_t* __restrict__ codes,
                                               float* __restrict__ scale, uint32_t* __restrict__ mask,
-                                              Dq* __restrict__ dq, int64_t wg, float* group_ss) {
+                                              Dq* __restrict__ dq, int64_t wg) {
+  __shared__ float group_ss[64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t total_runs = rows * runs_per_row;
@@ -862,9 +863,8 @@ __global__ void __launch_bounds__(1024)
     quest_fwd_mfma_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, int rows_per_wg,
                                FwdConsts k, uint8_t* __restrict__ codes, float* __restrict__ scale,
                                uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
-  __shared__ float group_ss[64];
   fwd_mfma_rows<LOGN, B, Dq, kQuant>(x, rows, runs_per_row, rows_per_wg, k, codes, scale, mask, dq,
-                                     fwd_wg_index<Dq>(), group_ss);
+                                     fwd_wg_index<Dq>());
 }
 
 template <int LOGN, int B, int LOGR>
@@ -875,7 +875,6 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
   if (static_cast<int64_t>(blockIdx.x) >= tile_wgs) {
     // A row of a wide tensor: the row kernel's work with one row per
     // workgroup of four waves (runs past the row read zeros, store nothing).
-    __shared__ float group_ss[64];
     const int64_t row = static_cast<int64_t>(blockIdx.x) - tile_wgs;
     int i = 0;
 #pragma unroll
@@ -885,7 +884,7 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
     kw.inv_cols = g.wide_inv_cols[i];
     fwd_mfma_rows<LOGN, B, void, true>(g.wide_x[i], g.wide_first_row[i + 1] - g.wide_first_row[i], g.wide_runs[i], 1,
                                        kw, g.wide_codes[i], g.wide_scale[i], g.wide_mask[i], nullptr,
-                                       row - g.wide_first_row[i], group_ss);
+                                       row - g.wide_first_row[i]);
     return;
   }
   const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
