@@ -29,8 +29,11 @@
 // stage (k = 128) a wave runs 16 MFMAs in two halves, reading the next half's
 // fragments from LDS meanwhile; one barrier per stage publishes the next
 // stage.  With two waves per SIMD one wave's fragment reads and waits overlap
-// the other's MFMAs.  The epilogue scales by Delta_a Delta_b and writes whole
-// row segments through LDS.
+// the other's MFMAs.  The clip scales reach LDS the same way.  The epilogue
+// scales by Delta_a Delta_b and writes whole row segments through LDS.  When
+// the tiles are more than one round, one workgroup per compute unit walks
+// several tiles, requesting the next tile's first stages before it stores the
+// finished one.
 #include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
