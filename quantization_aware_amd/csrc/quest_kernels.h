@@ -118,12 +118,13 @@ __device__ __forceinline__ uint32_t quantise8(const float* v, float kk) {
   static_assert(B >= 1 && B <= 4, "8 codes of at most 4 bits fit one dword");
   constexpr float L = static_cast<float>(1 << B);
   if constexpr (B == 1) {
-    float p[8];
+    // Code 1 where v kk >= 0: v kk + 0 is +0 for a zero product of either
+    // sign, so the code is the complement of the sign bit, pushed in with one
+    // funnel shift per entry (entry j ends in bit j).
+    uint32_t s = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = v[j] * kk;
-    uint32_t w = 0u;
-    push8_nonneg(w, p);
-    return w;
+    for (int j = 7; j >= 0; --j) s = __builtin_amdgcn_alignbit(s, __float_as_uint(__builtin_fmaf(v[j], kk, 0.f)), 31);
+    return ~s & 0xFFu;
   } else if constexpr (B == 2 || B == 4) {
     constexpr int PER_BYTE = 8 / B;
     const float off = 0.5f * (L - 1.f);
