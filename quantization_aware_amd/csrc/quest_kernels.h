@@ -762,7 +762,7 @@ extern __shared__ u32x4 rows_lds[];
 // block of rows (no grid-stride loop): with a barrier per block, letting the
 // hardware refill compute units as workgroups finish hides latency better
 // than a resident loop.
-template <int LOGN, int B, typename Dq, bool kQuant>
+template <int LOGN, int B, typename Dq, bool kQuant, bool kMayIdle = false>
 __device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row,
                                               int rows_per_wg, const FwdConsts& k, uint8_t* __restrict__ codes,
                                               float* __restrict__ scale, uint32_t* __restrict__ mask,
@@ -777,22 +777,32 @@ __device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, in
   const bf16x8_t h0 = hadamard_fragment(lane, 0);
   const bf16x8_t h1 = hadamard_fragment(lane, 1);
 
-  const rsrc_t in_r = window_at(x, wg_first_run * 64, total_runs * 64, wg_runs * 64);
-  const int in_off = wave * 4096 + 64 * (lane & 15) + 16 * (lane >> 4);
-  u32x4 f[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(in_r, in_off + 1024 * j, 0, kNonTemporal);
-
+  // kMayIdle: the grouped launch, whose 256-lane workgroups each take one
+  // row of at most 256 runs.  A wave holding no run of that row skips the
+  // loads and the transform and leaves after the barrier (the other launches
+  // start only the waves their rows need).
+  const bool idle = kMayIdle && 64 * wave >= static_cast<int>(wg_runs);
   float v[RUN];
-  float part[4];
+  float tau = 1.f;
+  if (!idle) {
+    const rsrc_t in_r = window_at(x, wg_first_run * 64, total_runs * 64, wg_runs * 64);
+    const int in_off = wave * 4096 + 64 * (lane & 15) + 16 * (lane >> 4);
+    u32x4 f[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    mfma_run_outputs(h0, h1, f[j], v + 8 * j);
-    part[j] = group_sum(sum_squares_fragment(f[j]), 6);
+    for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(in_r, in_off + 1024 * j, 0, kNonTemporal);
+    float part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mfma_run_outputs(h0, h1, f[j], v + 8 * j);
+      part[j] = group_sum(sum_squares_fragment(f[j]), 6);
+    }
+    if (lane < 4) group_ss[4 * wave + lane] = lane == 0 ? part[0] : lane == 1 ? part[1] : lane == 2 ? part[2] : part[3];
+    tau = fwht_cross_lanes<LOGN, true>(v, lane);
   }
-  if (lane < 4) group_ss[4 * wave + lane] = lane == 0 ? part[0] : lane == 1 ? part[1] : lane == 2 ? part[2] : part[3];
-  const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
   __syncthreads();
+  if constexpr (kMayIdle && !kIsOperand<Dq>) {
+    if (idle) return;
+  }
 
   // Row of each slot (wave-uniform); a wave's 64 runs touch at most two rows.
   const int row_a = (4 * wave) / groups_per_row;
@@ -875,7 +885,8 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
   const int64_t tile_wgs = (g.first_tile[g.count] + 3) / 4;
   if (static_cast<int64_t>(blockIdx.x) >= tile_wgs) {
     // A row of a wide tensor: the row kernel's work with one row per
-    // workgroup of four waves (runs past the row read zeros, store nothing).
+    // workgroup of four waves (runs past the row read zeros and store
+    // nothing; a wave wholly past it only joins the barrier).
     const int64_t row = static_cast<int64_t>(blockIdx.x) - tile_wgs;
     int i = 0;
 #pragma unroll
@@ -883,9 +894,9 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
       if (j < g.wide_count && row >= g.wide_first_row[j]) i = j;
     FwdConsts kw = k;
     kw.inv_cols = g.wide_inv_cols[i];
-    fwd_mfma_rows<LOGN, B, void, true>(g.wide_x[i], g.wide_first_row[i + 1] - g.wide_first_row[i], g.wide_runs[i], 1,
-                                       kw, g.wide_codes[i], g.wide_scale[i], g.wide_mask[i], nullptr,
-                                       row - g.wide_first_row[i]);
+    fwd_mfma_rows<LOGN, B, void, true, true>(g.wide_x[i], g.wide_first_row[i + 1] - g.wide_first_row[i],
+                                             g.wide_runs[i], 1, kw, g.wide_codes[i], g.wide_scale[i], g.wide_mask[i],
+                                             nullptr, row - g.wide_first_row[i]);
     return;
   }
   const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
