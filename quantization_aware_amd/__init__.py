@@ -347,25 +347,35 @@ def operand_bytes(rows: int, cols: int) -> int:
 
 
 def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, with_codes: bool = False,
-                    with_mask: bool = False, operand=None, scale=None, stream=None):
+                    with_mask: bool = False, operand=None, scale=None, stream=None, codes=None, mask=None):
     """Forward writing the matrix-core operand (quest_quantize_fwd_op).
 
     Returns (codes or None, scale, mask or None, operand); the operand is a
-    flat uint8 tensor of operand_bytes(rows, cols) bytes.
+    flat uint8 tensor of operand_bytes(rows, cols) bytes.  codes / mask, when
+    given, are caller buffers for those outputs (uint8, contiguous, at least
+    codes_bytes / mask_bytes long) and imply with_codes / with_mask.
     """
     lib = load_library()
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor (rows x cols)")
     rows, cols = x.shape
     dev = x.device
-    codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev) if with_codes else None
+    if codes is None and with_codes:
+        codes = torch.empty((rows, cols * b // 8), dtype=torch.uint8, device=dev)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=dev)
-    mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev) if with_mask else None
+    if mask is None and with_mask:
+        mask = torch.empty((rows, cols // 8), dtype=torch.uint8, device=dev)
     if operand is None:
         operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=dev)
     _buffer("scale", scale, torch.float32, rows)
     _buffer("operand", operand, torch.uint8, operand_bytes(rows, cols))
+    if codes is not None:
+        _buffer("codes", codes, torch.uint8, codes_bytes(rows, cols, b))
+        _on_device(dev, codes=codes)
+    if mask is not None:
+        _buffer("mask", mask, torch.uint8, mask_bytes(rows, cols))
+        _on_device(dev, mask=mask)
     _on_device(dev, x=x, scale=scale, operand=operand)
     st = lib.quest_quantize_fwd_op(
         x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),

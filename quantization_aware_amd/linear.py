@@ -79,13 +79,36 @@ class QuestLinearFunction(torch.autograd.Function):
         ctx.fp6 = (grid == "int" and max(bits_x, bits_w) <= 4 and x.shape[1] % 128 == 0 and x.shape[1] <= 65536
                    and 0 < w.shape[0] <= 2 ** 20 and 0 < x.shape[0] <= 2 ** 30)
         if ctx.fp6:
-            cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, with_codes=True, with_mask=True)
-            cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, with_codes=True, with_mask=True)
+            n, k = x.shape
+            m = w.shape[0]
+            # With one bit width and n a multiple of 4 (every buffer 16-byte
+            # aligned), the codes, scales and masks of x and w are the rows of
+            # one (n + m)-row tensor each, so that the backward rebuilds both
+            # operands in one quest_dequantize launch and masks both gradients
+            # in one quest_trust_bwd launch.
+            ctx.joint = bits_x == bits_w and n % 4 == 0
+            if ctx.joint:
+                dev = x.device
+                codes = torch.empty((n + m, k * bits_x // 8), dtype=torch.uint8, device=dev)
+                scale = torch.empty((n + m,), dtype=torch.float32, device=dev)
+                mask = torch.empty((n + m, k // 8), dtype=torch.uint8, device=dev)
+                cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, codes=codes[:n],
+                                                     scale=scale[:n], mask=mask[:n])
+                cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, codes=codes[n:],
+                                                     scale=scale[n:], mask=mask[n:])
+            else:
+                cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, with_codes=True,
+                                                     with_mask=True)
+                cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, with_codes=True,
+                                                     with_mask=True)
             out_dtype = torch.float32 if compute_dtype == torch.float32 else torch.bfloat16
-            y = gemm(ox, sx, x.shape[0], bits_x, ow, sw, w.shape[0], bits_w, x.shape[1], out_dtype=out_dtype)
+            y = gemm(ox, sx, n, bits_x, ow, sw, m, bits_w, k, out_dtype=out_dtype)
             y = y.to(compute_dtype)
-            ctx.save_for_backward(cx, sx, cw, sw, mask_x, mask_w)
-            ctx.dims = (x.shape[0], w.shape[0], x.shape[1], bits_x, bits_w, compute_dtype)
+            if ctx.joint:
+                ctx.save_for_backward(codes, scale, mask)
+            else:
+                ctx.save_for_backward(cx, sx, cw, sw, mask_x, mask_w)
+            ctx.dims = (n, m, k, bits_x, bits_w, compute_dtype)
             return y
         mask_x, qx = _quantise(x, block, bits_x, trust_x, grid, compute_dtype)
         mask_w, qw = _quantise(w, block, bits_w, trust_w, grid, compute_dtype)
@@ -95,8 +118,15 @@ class QuestLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy):
+        if ctx.fp6 and ctx.joint and ctx.needs_input_grad[0] and ctx.needs_input_grad[1]:
+            return QuestLinearFunction._backward_joint(ctx, dy)
         if ctx.fp6:
-            cx, sx, cw, sw, mask_x, mask_w = ctx.saved_tensors
+            if ctx.joint:
+                codes, scale, mask = ctx.saved_tensors
+                n = ctx.dims[0]
+                cx, sx, mask_x, cw, sw, mask_w = codes[:n], scale[:n], mask[:n], codes[n:], scale[n:], mask[n:]
+            else:
+                cx, sx, cw, sw, mask_x, mask_w = ctx.saved_tensors
             n, m, k, bits_x, bits_w, compute_dtype = ctx.dims
             # Q(x) for the weight gradient and Q(w) for the input gradient,
             # rebuilt from the codes (both first: the rebuilds keep the GPU
@@ -119,6 +149,29 @@ class QuestLinearFunction(torch.autograd.Function):
             g = torch.mm(dy, qw)  # gradient reaching Q(x), Hadamard domain
             dx = trust_bwd(g, mask_x, ctx.block, out=g).to(ctx.x_dtype)
         return dx, dw, None, None, None, None, None, None, None
+
+    @staticmethod
+    def _backward_joint(ctx, dy):
+        """Both gradients of the FP6 path, x's and w's state held as the rows of one tensor each.
+
+        One rebuild launch gives [Q(x); Q(w)], the two products write
+        [dy Q(w); dy^T Q(x)] (the weight gradient first, while Q(x) is still in
+        the last-level cache), and one trust backward masks and transforms
+        both back in place.
+        """
+        codes, scale, mask = ctx.saved_tensors
+        n, m, k, bits, _, compute_dtype = ctx.dims
+        q = dequantize(codes, scale, n + m, k, bits, out_dtype=compute_dtype)
+        qx, qw = q[:n], q[n:]
+        dy = dy.to(compute_dtype).contiguous()
+        g = torch.empty((n + m, k), dtype=compute_dtype, device=dy.device)
+        # gradients reaching Q(w) and Q(x), Hadamard domain (the weight's as a
+        # 2-D product with a transposed left operand, as torch's own linear
+        # backward computes it)
+        torch.mm(dy.t(), qx, out=g[n:])
+        torch.mm(dy, qw, out=g[:n])
+        trust_bwd(g, mask, ctx.block, out=g)
+        return g[:n].to(ctx.x_dtype), g[n:].to(ctx.w_dtype), None, None, None, None, None, None, None
 
 
 def quest_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None, block: int = 128,

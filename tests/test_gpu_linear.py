@@ -161,6 +161,7 @@ def reach_of(bx_: np.ndarray, bw_: np.ndarray, block: int):
 @pytest.mark.parametrize("n,k,m,block,bx,bw,fp6", [
     # the FP6 forward product (int grid, b <= 4, K a multiple of 128)
     (256, 1024, 384, 128, 4, 4, True), (96, 2048, 160, 64, 2, 3, True), (130, 512, 64, 256, 4, 1, True),
+    (132, 1024, 96, 64, 3, 3, True), (130, 1024, 96, 128, 3, 3, True),
     # the dequantised operands and a library product: K not a multiple of 128, or b > 4
     (96, 192, 160, 64, 2, 3, False), (128, 1024, 96, 128, 5, 4, False), (64, 640, 72, 128, 8, 6, False)])
 def test_linear_matches_oracle(dev, n, k, m, block, bx, bw, fp6, compute_dtype):
@@ -231,7 +232,9 @@ def test_linear_training_forward_path(dev, bits, k, fp6):
     y = QuestLinearFunction.apply(x, w, block, bits, bits, torch.bfloat16, 1.0, 1.0, "int")
     saved = y.grad_fn.saved_tensors
     if fp6:
-        assert len(saved) == 6 and saved[0].dtype == torch.uint8 and saved[0].shape == (64, k * bits // 8)
+        # one bit width and 64 rows: x's and w's codes, scales and masks as the rows of one tensor each
+        assert len(saved) == 3 and saved[0].dtype == torch.uint8 and saved[0].shape == (64 + 32, k * bits // 8)
+        assert saved[1].shape == (64 + 32,) and saved[2].shape == (64 + 32, k // 8)
     else:
         assert len(saved) == 4 and saved[0].dtype == torch.bfloat16 and saved[0].shape == (64, k)
     y.float().sum().backward()
@@ -308,3 +311,28 @@ def test_linear_module_frozen_fp6_product(dev, compute_dtype):
         close_product_plus_bias(y.reshape(120, 384), f, bias64, "frozen y", skip_y)
     layer.train()
     assert layer._w_operand is None
+
+
+@pytest.mark.parametrize("n", [128, 130])
+def test_linear_one_gradient_matches_both(dev, n):
+    """The FP6 layer's backward for one gradient (x's or w's alone) against both at once: with one bit
+    width and n a multiple of 4 the two operands' state shares one tensor per output and both gradients
+    come from one rebuild and one trust backward (n = 128); otherwise (n = 130) each has its own."""
+    k, m = 1024, 192
+    x = make_tensor(TensorSpec("one.x", n, k, "bf16", "student_t", 4, 9990), dev)
+    w = make_tensor(TensorSpec("one.w", m, k, "bf16", "normal", 0.02, 9991), dev)
+    dy = make_tensor(TensorSpec("one.dy", n, m, "bf16", "normal", 1e-3, 9992), dev)
+    log(f"one gradient against both, {n}x{k} by {m}x{k}")
+    xg, wg = x.clone().requires_grad_(True), w.clone().requires_grad_(True)
+    dx, dw = torch.autograd.grad(quest_linear(xg, wg, block=128), (xg, wg), dy)
+    xg1 = x.clone().requires_grad_(True)
+    (dx1,) = torch.autograd.grad(quest_linear(xg1, w, block=128), (xg1,), dy)
+    wg1 = w.clone().requires_grad_(True)
+    (dw1,) = torch.autograd.grad(quest_linear(x, wg1, block=128), (wg1,), dy)
+    torch.cuda.synchronize()
+    assert dx.shape == (n, k) and dw.shape == (m, k)
+    # the gradient products are library GEMMs: allow their own summation order
+    for got, ref, what in ((dx, dx1, "dx"), (dw, dw1, "dw")):
+        err = (got.float() - ref.float()).abs().max().item()
+        scale = ref.float().abs().max().item()
+        assert err <= 1e-3 * scale, f"{what} off by {err} (largest entry {scale})"
