@@ -72,6 +72,18 @@ def test_fwd_op_rejects_small_operand_and_scale():
         qa.quantize_fwd_op(x, 128, 4)
 
 
+def test_fwd_op_rejects_small_or_mistyped_codes_and_mask():
+    x = torch.zeros((33, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="codes too small"):
+        qa.quantize_fwd_op(x, 128, 4, codes=u8(33 * 128 - 1))
+    with pytest.raises(ValueError, match="mask too small"):
+        qa.quantize_fwd_op(x, 128, 4, mask=u8(33 * 32 - 1))
+    with pytest.raises(TypeError, match="codes must be"):
+        qa.quantize_fwd_op(x, 128, 3, codes=torch.zeros(33 * 96, dtype=torch.int8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qa.quantize_fwd_op(x, 128, 4, codes=u8(33 * 128), mask=u8(33 * 32))
+
+
 def test_grid_dequantisers_reject_small_inputs():
     with pytest.raises(ValueError, match="codes too small"):
         qa.dequantize_fp4(u8(16 * 256 // 2 - 1), f32(16), 16, 256)
