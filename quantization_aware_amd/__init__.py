@@ -370,13 +370,14 @@ def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
         operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=dev)
     _buffer("scale", scale, torch.float32, rows)
     _buffer("operand", operand, torch.uint8, operand_bytes(rows, cols))
+    outs = {}
     if codes is not None:
         _buffer("codes", codes, torch.uint8, codes_bytes(rows, cols, b))
-        _on_device(dev, codes=codes)
+        outs["codes"] = codes
     if mask is not None:
         _buffer("mask", mask, torch.uint8, mask_bytes(rows, cols))
-        _on_device(dev, mask=mask)
-    _on_device(dev, x=x, scale=scale, operand=operand)
+        outs["mask"] = mask
+    _on_device(dev, x=x, scale=scale, operand=operand, **outs)
     st = lib.quest_quantize_fwd_op(
         x.data_ptr(), _dtype_code(x), rows, cols, int(block), int(b), float(trust),
         codes.data_ptr() if codes is not None else None, scale.data_ptr(),
