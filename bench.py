@@ -421,9 +421,10 @@ def qat_linear_step(torch, dev, reps):
 
     The q projection of the block (16384 tokens x 2048 by 2048 x 2048), b = 4
     for both operands, block 128, bf16 compute: quest_linear (two operand
-    forwards with codes and mask, the FP6 product; in the backward the two
-    operands rebuilt from their codes, the two BF16 gradient products and two
-    trust-masked backwards) against torch's BF16 linear, each as
+    forwards with codes and mask, the FP6 product; in the backward both
+    operands rebuilt from their codes in one launch, the two BF16 gradient
+    products, and both gradients masked and transformed back in one launch)
+    against torch's BF16 linear, each as
     `reps` back-to-back forward + backward passes (torch.autograd.grad, so no
     gradient accumulation) between events on the launch stream, over rotating
     copies of the inputs.
