@@ -23,7 +23,9 @@
  *     allocates, frees or synchronises.
  *   - Device calls enqueue their kernels on `stream` (a hipStream_t; NULL is
  *     the null stream) and return without waiting.  A status other than
- *     QUEST_EHIP means nothing was enqueued.
+ *     QUEST_EHIP means nothing was enqueued.  They enqueue nothing but
+ *     kernels (no copy, fill or wait), so a sequence of calls on a stream
+ *     under HIP graph capture records into the graph and replays as called.
  *   - Arguments are checked before anything is launched.  On any error the
  *     call writes nothing and returns a status code; no C++ exception crosses
  *     this interface.
