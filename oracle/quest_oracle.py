@@ -123,7 +123,12 @@ def blockwise_hadamard(x: np.ndarray, n: int) -> np.ndarray:
     """Apply the orthonormal Hadamard matrix to every length-n block of every row.
 
     y[r, k*n:(k+1)*n] = (H_n / sqrt(n)) @ x[r, k*n:(k+1)*n], computed as a
-    dense matrix product against the explicit n x n matrix.
+    dense matrix product against the explicit +-1 matrix H_n, divided by
+    sqrt(n) afterwards.  The +-1 sums of bf16 inputs (and of fp32 inputs of
+    moderate dynamic range) are exact in float64, and one division per entry
+    maps equal sums to equal outputs, so entries that are equal in magnitude
+    by the definition stay equal: the 2:4 rule breaks such ties by index, not
+    by rounding noise of the product.
     """
     x = np.asarray(x, dtype=np.float64)
     if x.ndim != 2:
@@ -131,10 +136,10 @@ def blockwise_hadamard(x: np.ndarray, n: int) -> np.ndarray:
     rows, cols = x.shape
     if cols % n != 0:
         raise ValueError(f"cols={cols} is not a multiple of the block size {n}")
-    h = normalized_hadamard(n)
+    h = sylvester_hadamard(n)
     blocks = x.reshape(rows, cols // n, n)
     # For each block vector v (a row of `blocks`), v @ h.T == (h @ v) as a row.
-    y = blocks @ h.T
+    y = (blocks @ h.T) / math.sqrt(n)
     return y.reshape(rows, cols)
 
 

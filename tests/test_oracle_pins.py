@@ -105,6 +105,44 @@ def test_blockwise_hadamard_round_trip():
         assert np.max(np.abs(back - x)) <= 1e-13
 
 
+def test_blockwise_hadamard_exact_sums_for_bf16_inputs():
+    """For inputs with 8-bit significands (bf16) the +-1 sums of a block are exact in float64, so each output
+    is the exactly summed value divided once by sqrt(n): here the sums are taken over Python integers (every
+    input times 2^27 is one) with H from the closed form (-1)^popcount(k & c), an independent construction."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(17)
+    n, rows, cols = 128, 3, 256
+    mant = rng.integers(128, 256, size=(rows, cols))
+    expo = rng.integers(-20, 5, size=(rows, cols))
+    sign = rng.choice([-1, 1], size=(rows, cols))
+    x = sign * mant * np.exp2(expo - 7.0)
+    y = qo.blockwise_hadamard(x, n)
+    xi = [[int(round(v * 2.0 ** 27)) for v in row] for row in x]
+    for r in range(rows):
+        for blk in range(cols // n):
+            for k in range(0, n, 7):
+                s_ = sum(xi[r][blk * n + c] * (-1) ** bin(k & c).count("1") for c in range(n))
+                ref = float(Fraction(s_, 2 ** 27)) / math.sqrt(n)
+                assert y[r, blk * n + k] == ref, (r, blk, k)
+
+
+def test_sparse24_keeps_exact_ties_by_index_after_the_transform():
+    """Two entries of a group equal in magnitude by construction stay equal through the transform, and the
+    lower index is kept: x = H t / n for an integer target t, so that y = t / sqrt(n) exactly up to the one
+    division; the first group's magnitudes are 3, 5, 3, 1 (tie between entries 0 and 2 for second place)."""
+    n = 128
+    h = np.array([[(-1) ** bin(k & c).count("1") for c in range(n)] for k in range(n)], dtype=np.float64)
+    t = np.zeros(n)
+    t[:8] = [3.0, -5.0, -3.0, 1.0, 2.0, 2.0, -2.0, 7.0]
+    x = (h @ t / n)[None, :]
+    y = qo.blockwise_hadamard(x, n)
+    assert np.array_equal(np.abs(y[0, :8]), np.abs(t[:8]) / math.sqrt(n))
+    keep = qo.sparse24_keep(y)
+    # group 0: 5 first, then of the two 3s the lower index; group 1: 7, then the first of the three 2s
+    assert keep[0, :8].tolist() == [True, True, False, False, True, False, False, True]
+
+
 def test_blockwise_hadamard_rejects_bad_shapes():
     with pytest.raises(ValueError):
         qo.blockwise_hadamard(np.zeros((2, 100)), 64)
