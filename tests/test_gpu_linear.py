@@ -81,6 +81,10 @@ def close(got: torch.Tensor, ref: np.ndarray, what: str, tols, skip=None, block=
         raise AssertionError(f"{what}: {int(bad.sum())} entries off, first at ({r},{c}): got {got[r, c]!r} "
                              f"ref {ref[r, c]!r}; worst error / max(|ref|, rms) {ratio.max()!r}")
     keep = np.ones_like(bad) if skip is None else ~skip
+    if not keep.any() or not np.any(ref[keep]):
+        # at b >= 5 a band entry in every row or Hadamard block can reach the whole tensor
+        log(f"{what}: every entry within a band entry's reach; norm-wise check skipped")
+        return
     rel = np.linalg.norm((got - ref)[keep]) / np.linalg.norm(ref[keep])
     assert rel <= tol_norm, f"{what}: relative Frobenius error {rel} (outside the band's reach)"
 
