@@ -427,7 +427,7 @@ def qat_linear_step(torch, dev, reps):
     against torch's BF16 linear, each as
     `reps` back-to-back forward + backward passes (torch.autograd.grad, so no
     gradient accumulation) between events on the launch stream, over rotating
-    copies of the inputs.
+    copies of the inputs; three interleaved rounds of the two, medians.
     """
     from quantization_aware_amd.linear import quest_linear
     from quest_inputs import LAYER_ACT_2048, TensorSpec, layer_products, make_tensor
@@ -465,10 +465,17 @@ def qat_linear_step(torch, dev, reps):
         y = torch.nn.functional.linear(xs[i], ws[i])
         torch.autograd.grad(y, (xs[i], ws[i]), dys[i])
 
-    t_q, t_b = timed(quest), timed(bf16)
+    # Interleaved rounds, medians: the two layers see the same clock and power
+    # history instead of one always running after the other.
+    rounds_q, rounds_b = [], []
+    for _ in range(3):
+        rounds_q.append(timed(quest))
+        rounds_b.append(timed(bf16))
+    t_q, t_b = sorted(rounds_q)[1], sorted(rounds_b)[1]
     return {"layer": "q projection", "tokens": x0.shape[0], "in_features": x0.shape[1], "out_features": w0.shape[0],
             "bits": 4, "block": BLOCK, "compute_dtype": "bf16", "quest_step_us": 1000 * t_q,
             "bf16_step_us": 1000 * t_b, "quest_over_bf16": t_q / t_b, "input_sets": sets,
+            "rounds_us": {"quest": [round(1000 * t, 1) for t in rounds_q], "bf16": [round(1000 * t, 1) for t in rounds_b]},
             "note": "training step of the QuEST layer (quantisers, FP6 forward product, BF16 gradient products, "
                     "trust backwards) vs a plain BF16 linear layer"}
 
