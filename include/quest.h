@@ -313,6 +313,43 @@ quest_status quest_quantize_fwd_op(const void* x, quest_dtype x_dtype, int64_t r
                                    uint8_t* operand, void* stream);
 
 /*
+ * The forward of quest_quantize_fwd_op on several tensors in one call: the
+ * outputs are those of calling quest_quantize_fwd_op on each tensor in turn
+ * (same block, bit width, trust factor and input dtype), bit for bit.  A
+ * quantisation-aware layer quantises its activations and its weights before
+ * every product (pith.science review of QuEST, "What carries the argument";
+ * Figure 2 caption); with bf16 inputs the library launches the tensors whose
+ * rows have 512, 1024 or 2048 entries together (one launch per width for up
+ * to four tensors) and launches the others one by one.
+ *
+ *   tensors  host array of `count` descriptors, read during the call only;
+ *            each names x, rows, cols, codes, scale, mask and operand as the
+ *            arguments of quest_quantize_fwd_op (codes and mask may be NULL;
+ *            a tensor with rows == 0 is skipped and its pointers are not
+ *            read)
+ *   count    >= 0 (0: nothing is done)
+ *   x_dtype, block, b, trust, stream: as for quest_quantize_fwd_op, for
+ *            every tensor
+ * Errors: everything quest_quantize_fwd_op rejects for any tensor, with the
+ * same status; count < 0 or tensors NULL with count > 0 is QUEST_EINVAL; an
+ * output of one tensor overlapping an input or output of another is
+ * QUEST_EINVAL (inputs may overlap each other).  Validation covers every
+ * tensor before the first launch, so on error nothing is written.
+ */
+typedef struct {
+  const void* x;
+  int64_t rows;
+  int64_t cols;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* mask;
+  uint8_t* operand;
+} quest_fwd_op_tensor;
+
+quest_status quest_quantize_fwd_op_group(const quest_fwd_op_tensor* tensors, int count, quest_dtype x_dtype,
+                                         int block, int b, double trust, void* stream);
+
+/*
  * Product of two quantised operands along their quantised axis:
  *   out[i, j] = Delta_a[i] Delta_b[j] * sum_c h_a[i, c] h_b[j, c],
  *   Delta = 2 s / (L - 1) from each operand's clip scale and bit width,

@@ -28,6 +28,7 @@ __all__ = [
     "operand_bytes",
     "codes_to_operand",
     "gemm",
+    "quantize_fwd_op_group",
     "quantize_fwd_fp4",
     "quantize_fwd_sparse24",
     "dequantize_fp4",
@@ -51,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "quest_quantize_fwd_dq",
     "quest_quantize_fwd_ex",
     "quest_quantize_fwd_op",
+    "quest_quantize_fwd_op_group",
     "quest_gemm",
     "quest_operand_bytes",
     "quest_codes_to_operand",
@@ -87,6 +89,14 @@ class _FwdTensor(ctypes.Structure):
                 ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
 
 
+class _FwdOpTensor(ctypes.Structure):
+    """quest_fwd_op_tensor of include/quest.h."""
+
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("operand", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libquest.so (once) and declare the C signatures."""
     global _lib
@@ -111,6 +121,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quest_quantize_fwd_ex.restype = c_int
     lib.quest_quantize_fwd_op.argtypes = [vp, c_int, i64, i64, c_int, c_int, ctypes.c_double, vp, vp, vp, vp, vp]
     lib.quest_quantize_fwd_op.restype = c_int
+    lib.quest_quantize_fwd_op_group.argtypes = [ctypes.POINTER(_FwdOpTensor), c_int, c_int, c_int, c_int,
+                                                ctypes.c_double, vp]
+    lib.quest_quantize_fwd_op_group.restype = c_int
     lib.quest_gemm.argtypes = [vp, vp, i64, c_int, vp, vp, i64, c_int, i64, vp, c_int, vp]
     lib.quest_gemm.restype = c_int
     lib.quest_codes_to_operand.argtypes = [vp, i64, i64, c_int, vp, vp]
@@ -385,6 +398,64 @@ def quantize_fwd_op(x: torch.Tensor, block: int, b: int, trust: float = 1.0, wit
     )
     _check("quest_quantize_fwd_op", st)
     return codes, scale, mask, operand
+
+
+def quantize_fwd_op_group(xs, block: int, b: int, trust: float = 1.0, outs=None, stream=None):
+    """quantize_fwd_op of several 2-D tensors of one dtype and device in one call (quest_quantize_fwd_op_group).
+
+    outs: None, or one dict per tensor of caller buffers with the keyword
+    names of quantize_fwd_op (operand, scale, and optionally codes and mask;
+    operand and scale are allocated when missing).  Returns a list of
+    (codes or None, scale, mask or None, operand), equal to what
+    quantize_fwd_op returns for each tensor.  bf16 tensors of 512, 1024 or
+    2048 columns share launches.
+    """
+    lib = load_library()
+    xs = list(xs)
+    if not xs:
+        return []
+    if outs is None:
+        outs = [{} for _ in xs]
+    if len(outs) != len(xs):
+        raise ValueError(f"{len(xs)} tensors but {len(outs)} output sets")
+    dev = xs[0].device
+    res, checked, descs = [], [], (_FwdOpTensor * len(xs))()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"xs[{i}] must be a 2-D tensor (rows x cols)")
+        if x.dtype != xs[0].dtype or x.device != dev:
+            raise ValueError("every tensor of a group must share the first one's dtype and device")
+        unknown = set(o) - {"codes", "scale", "mask", "operand"}
+        if unknown:
+            raise ValueError(f"outs[{i}] has unknown keys {sorted(unknown)}")
+        rows, cols = x.shape
+        scale = o.get("scale")
+        if scale is None:
+            scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+        operand = o.get("operand")
+        if operand is None:
+            operand = torch.empty((max(operand_bytes(rows, cols), 1),), dtype=torch.uint8, device=dev)
+        codes, mask = o.get("codes"), o.get("mask")
+        _buffer(f"outs[{i}].scale", scale, torch.float32, rows)
+        _buffer(f"outs[{i}].operand", operand, torch.uint8, operand_bytes(rows, cols))
+        bufs = {}
+        if codes is not None:
+            _buffer(f"outs[{i}].codes", codes, torch.uint8, codes_bytes(rows, cols, b))
+            bufs[f"outs[{i}].codes"] = codes
+        if mask is not None:
+            _buffer(f"outs[{i}].mask", mask, torch.uint8, mask_bytes(rows, cols))
+            bufs[f"outs[{i}].mask"] = mask
+        bufs.update({f"xs[{i}]": x, f"outs[{i}].scale": scale, f"outs[{i}].operand": operand})
+        checked.append(bufs)
+        res.append((codes, scale, mask, operand))
+        descs[i] = _FwdOpTensor(x.data_ptr(), rows, cols, codes.data_ptr() if codes is not None else None,
+                                scale.data_ptr(), mask.data_ptr() if mask is not None else None, operand.data_ptr())
+    for bufs in checked:  # every size first, then the devices
+        _on_device(dev, **bufs)
+    st = lib.quest_quantize_fwd_op_group(descs, len(xs), _dtype_code(xs[0]), int(block), int(b), float(trust),
+                                         _stream_handle(dev, stream))
+    _check("quest_quantize_fwd_op_group", st)
+    return res
 
 
 def codes_to_operand(codes: torch.Tensor, rows: int, cols: int, b: int, operand=None, stream=None) -> torch.Tensor:

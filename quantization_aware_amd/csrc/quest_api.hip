@@ -327,6 +327,73 @@ quest_status quest_quantize_fwd_op(const void* x, quest_dtype x_dtype, int64_t r
                              QUEST_BF16, false, rows > 0 ? operand : nullptr, stream);
 }
 
+quest_status quest_quantize_fwd_op_group(const quest_fwd_op_tensor* tensors, int count, quest_dtype x_dtype,
+                                         int block, int b, double trust, void* stream) {
+  if (count < 0 || (count > 0 && !tensors)) return QUEST_EINVAL;
+  // Every tensor as quest_quantize_fwd_op would check it ...
+  for (int i = 0; i < count; ++i) {
+    const quest_fwd_op_tensor& t = tensors[i];
+    if (t.rows > 0 && !t.operand) return QUEST_EINVAL;
+    const quest_status st = check_fwd(t.x, x_dtype, t.rows, t.cols, block, b, trust, t.codes, false, t.scale, t.mask,
+                                      false, nullptr, QUEST_BF16, false, t.rows > 0 ? t.operand : nullptr);
+    if (st != QUEST_OK) return st;
+  }
+  // ... and no output of one tensor on an input or output of another.
+  auto spans = [&](const quest_fwd_op_tensor& t, const void* (&p)[5], size_t (&n)[5]) {
+    p[0] = t.x;
+    p[1] = t.codes;
+    p[2] = t.scale;
+    p[3] = t.mask;
+    p[4] = t.operand;
+    n[0] = static_cast<size_t>(t.rows * t.cols) * dtype_size(x_dtype);
+    n[1] = t.codes ? quest_codes_bytes(t.rows, t.cols, b) : 0;
+    n[2] = static_cast<size_t>(t.rows) * sizeof(float);
+    n[3] = t.mask ? quest_mask_bytes(t.rows, t.cols) : 0;
+    n[4] = quest_operand_bytes(t.rows, t.cols);
+  };
+  for (int i = 0; i < count; ++i) {
+    if (tensors[i].rows == 0) continue;
+    const void* bi[5];
+    size_t ni[5];
+    spans(tensors[i], bi, ni);
+    for (int j = i + 1; j < count; ++j) {
+      if (tensors[j].rows == 0) continue;
+      const void* bj[5];
+      size_t nj[5];
+      spans(tensors[j], bj, nj);
+      for (int p = 0; p < 5; ++p)
+        for (int q = 0; q < 5; ++q)
+          if ((p > 0 || q > 0) && overlaps(bi[p], ni[p], bj[q], nj[q])) return QUEST_EINVAL;
+    }
+  }
+  std::call_once(g_env_once, read_env);
+  const int lb = log2_block(block);
+  const double alpha = quest_fit_alpha(b);
+  // bf16 tensors of 512, 1024 or 2048 columns go in grouped launches, one
+  // per width; the others as quest_quantize_fwd_op.
+  std::vector<quest::FwdOpGroupItem> group[3];
+  const bool grouped = x_dtype == QUEST_BF16 && g_allow_mfma;
+  for (int i = 0; i < count; ++i) {
+    const quest_fwd_op_tensor& t = tensors[i];
+    if (t.rows == 0) continue;
+    if (grouped && quest::fwd_group_tile_cols(t.cols)) {
+      group[t.cols == 512 ? 0 : t.cols == 1024 ? 1 : 2].push_back({t.x, t.rows, t.codes, t.scale, t.mask, t.operand});
+    } else {
+      const quest_status st = quantize_fwd_common(t.x, x_dtype, t.rows, t.cols, block, b, trust, t.codes, false,
+                                                  t.scale, t.mask, false, nullptr, QUEST_BF16, false, t.operand,
+                                                  stream);
+      if (st != QUEST_OK) return st;
+    }
+  }
+  for (int w = 0; w < 3; ++w) {
+    if (group[w].empty()) continue;
+    const hipError_t e = quest::launch_fwd_op_group(group[w].data(), static_cast<int>(group[w].size()), 512 << w, lb,
+                                                    b, alpha, trust, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return QUEST_EHIP;
+  }
+  return QUEST_OK;
+}
+
 quest_status quest_gemm(const uint8_t* a, const float* a_scale, int64_t m, int a_bits, const uint8_t* b,
                         const float* b_scale, int64_t n, int b_bits, int64_t k, void* out, quest_dtype out_dtype,
                         void* stream) {

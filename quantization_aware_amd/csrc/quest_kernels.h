@@ -922,6 +922,58 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
                                            nullptr);
 }
 
+// Several operand forwards in one launch (quest_quantize_fwd_op_group): bf16
+// tensors whose rows all have 512, 1024 or 2048 entries.  Each tensor starts
+// at a workgroup of its own, so a workgroup's four tiles are consecutive
+// tiles of one tensor and stage its operand pieces together as in
+// quest_fwd_mfma_kernel (a wave past its tensor's last tile computes on
+// zeros, and its stores are dropped or land in the operand's padding rows);
+// the XCD mapping of fwd_wg_index runs over the whole launch.  Per tensor the
+// work is quest_fwd_mfma_kernel's, tile for tile, so the outputs are those
+// of one call per tensor.
+constexpr int kFwdOpGroupMax = 4;
+
+struct FwdOpGroup {
+  int count;                               // tensors in this launch, 1 .. kFwdOpGroupMax
+  int64_t first_wg[kFwdOpGroupMax + 1];    // running workgroup counts; first_wg[count] = the grid
+  int64_t total_runs[kFwdOpGroupMax];
+  const uint16_t* x[kFwdOpGroupMax];
+  uint8_t* codes[kFwdOpGroupMax];          // may be null (not written)
+  float* scale[kFwdOpGroupMax];
+  uint32_t* mask[kFwdOpGroupMax];          // may be null (not written)
+  uint8_t* operand[kFwdOpGroupMax];
+};
+
+template <int LOGN, int B, int LOGR, bool kQuant>
+__global__ void __launch_bounds__(256) quest_fwd_mfma_op_group_kernel(FwdOpGroup g, FwdConsts k) {
+  constexpr int ROWS = 64 >> LOGR;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t wg = fwd_wg_index<OperandOut>();
+  const uint16_t* x = g.x[0];
+  uint8_t* codes = g.codes[0];
+  float* scale = g.scale[0];
+  uint32_t* mask = g.mask[0];
+  uint8_t* operand = g.operand[0];
+  int64_t runs = g.total_runs[0], first = 0;
+#pragma unroll
+  for (int i = 1; i < kFwdOpGroupMax; ++i) {
+    if (i < g.count && wg >= g.first_wg[i]) {
+      x = g.x[i];
+      codes = g.codes[i];
+      scale = g.scale[i];
+      mask = g.mask[i];
+      operand = g.operand[i];
+      runs = g.total_runs[i];
+      first = g.first_wg[i];
+    }
+  }
+  __shared__ __attribute__((aligned(16))) uint8_t opstage[64 * (24 * 4 * ROWS + kOpStagePad)];
+  fwd_mfma_tile<LOGN, B, LOGR, OperandOut, kQuant>(x, runs, k, codes, scale, mask,
+                                                   reinterpret_cast<OperandOut*>(operand), (wg - first) * 4 + wave,
+                                                   lane, wave, opstage);
+}
+
 
 // LDS of the row-per-workgroup kernels, sized at launch by their wave count:
 // per wave a staging area of 64 * US 16-byte slots, then one float per lane
@@ -1217,6 +1269,32 @@ hipError_t fwd_group_dispatch(const FwdGroup& g, int64_t cols, double alpha, hip
     default:
       hipLaunchKernelGGL((quest_fwd_mfma_group_kernel<LOGN, B, 6>), grid, dim3(256), 0, stream, g, k);
       break;
+  }
+  return hipGetLastError();
+}
+
+// One grouped operand launch: every tensor of `g` is bf16 with rows of
+// `cols` entries (512, 1024 or 2048), b <= 4.  quant: some tensor asks for
+// codes or mask (those of the others are null, so their stores are dropped).
+template <int LOGN, int B>
+hipError_t fwd_op_group_dispatch(const FwdOpGroup& g, int64_t cols, double alpha, double trust, bool quant,
+                                 hipStream_t stream) {
+  const FwdConsts k = fwd_consts<LOGN, B>(alpha, trust, cols);
+  const dim3 grid(static_cast<uint32_t>(g.first_wg[g.count]));
+  auto run = [&](auto logr, auto q) {
+    hipLaunchKernelGGL((quest_fwd_mfma_op_group_kernel<LOGN, B, decltype(logr)::value, decltype(q)::value>), grid,
+                       dim3(256), 0, stream, g, k);
+  };
+  auto run_logr = [&](auto logr) {
+    if (quant)
+      run(logr, std::true_type{});
+    else
+      run(logr, std::false_type{});
+  };
+  switch (cols / RUN) {
+    case 16: run_logr(std::integral_constant<int, 4>{}); break;
+    case 32: run_logr(std::integral_constant<int, 5>{}); break;
+    default: run_logr(std::integral_constant<int, 6>{}); break;
   }
   return hipGetLastError();
 }

@@ -54,6 +54,22 @@ inline bool fwd_group_wide_cols(int64_t cols) { return cols > 2048 && cols <= 81
 hipError_t launch_fwd_group(const FwdGroupItem* items, int count, int64_t cols, const FwdGroupItem* wide,
                             int wide_count, int log_block, int bits, double alpha, hipStream_t stream);
 
+// One tensor of a grouped operand forward (quest_quantize_fwd_op_group).
+struct FwdOpGroupItem {
+  const void* x;  // bf16
+  int64_t rows;   // >= 1
+  uint8_t* codes;  // may be null
+  float* scale;
+  uint8_t* mask;  // may be null
+  uint8_t* operand;
+};
+
+// Operand forwards of bf16 tensors (bits <= 4) whose rows all have `cols`
+// entries, 512, 1024 or 2048, in launches of at most four tensors.  All
+// arguments already validated.
+hipError_t launch_fwd_op_group(const FwdOpGroupItem* items, int count, int64_t cols, int log_block, int bits,
+                               double alpha, double trust, hipStream_t stream);
+
 // Packed codes (bits <= 4, cols a multiple of 128) to the tiled FP6 operand.
 hipError_t launch_codes_to_operand(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint8_t* operand,
                                    hipStream_t stream);

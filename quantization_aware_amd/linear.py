@@ -15,8 +15,9 @@ Quantisation, masking and both transforms run in libquest's kernels
 (quest_quantize_fwd_ex, or the FP4 and 2:4-sparse forwards, and
 quest_trust_bwd).  On the int grid with b <= 4 and K a multiple of 128 the
 forward product is libquest's FP6 product of the two operands
-(quest_quantize_fwd_op with codes and mask, then quest_gemm: exact sums, one
-rounding to the compute dtype), and the backward rebuilds Q(x) and Q(w) from
+(quest_quantize_fwd_op with codes and mask, both operands in one
+quest_quantize_fwd_op_group launch when they share dtype and trust factor,
+then quest_gemm: exact sums, one rounding to the compute dtype), and the backward rebuilds Q(x) and Q(w) from
 the saved codes (quest_dequantize, the same values as the dequantised
 forward output).  The two gradient products, and the forward product of the
 other configurations, are plain library GEMMs through torch.  ``grid`` picks the format the operands are quantised to: "int"
@@ -36,7 +37,8 @@ from __future__ import annotations
 
 import torch
 
-from . import dequantize, gemm, quantize_fwd_ex, quantize_fwd_fp4, quantize_fwd_op, quantize_fwd_sparse24, trust_bwd
+from . import (dequantize, gemm, quantize_fwd_ex, quantize_fwd_fp4, quantize_fwd_op, quantize_fwd_op_group,
+               quantize_fwd_sparse24, trust_bwd)
 
 __all__ = ["QuestLinearFunction", "quest_linear", "quest_linear_operand", "QuestLinear", "default_trust",
            "ONE_BIT_OUTER_TRUST", "GRIDS"]
@@ -92,10 +94,15 @@ class QuestLinearFunction(torch.autograd.Function):
                 codes = torch.empty((n + m, k * bits_x // 8), dtype=torch.uint8, device=dev)
                 scale = torch.empty((n + m,), dtype=torch.float32, device=dev)
                 mask = torch.empty((n + m, k // 8), dtype=torch.uint8, device=dev)
-                cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, codes=codes[:n],
-                                                     scale=scale[:n], mask=mask[:n])
-                cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, codes=codes[n:],
-                                                     scale=scale[n:], mask=mask[n:])
+                outs = [dict(codes=codes[:n], scale=scale[:n], mask=mask[:n]),
+                        dict(codes=codes[n:], scale=scale[n:], mask=mask[n:])]
+                if trust_x == trust_w and x.dtype == w.dtype:
+                    # one launch for both operands (quest_quantize_fwd_op_group)
+                    (cx, sx, mask_x, ox), (cw, sw, mask_w, ow) = quantize_fwd_op_group([x, w], block, bits_x,
+                                                                                      trust=trust_x, outs=outs)
+                else:
+                    cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, **outs[0])
+                    cw, sw, mask_w, ow = quantize_fwd_op(w, block, bits_w, trust=trust_w, **outs[1])
             else:
                 cx, sx, mask_x, ox = quantize_fwd_op(x, block, bits_x, trust=trust_x, with_codes=True,
                                                      with_mask=True)

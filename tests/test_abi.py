@@ -401,6 +401,64 @@ def test_fwd_op_rejects(lib, kw, status):
     assert fwd_op(lib, **kw) == status
 
 
+def op_group(lib, items, dt=qa.QUEST_BF16, block=128, b=4, trust=1.0, count=None):
+    descs = (qa._FwdOpTensor * max(len(items), 1))()
+    for i, it in enumerate(items):
+        descs[i] = qa._FwdOpTensor(it.get("x"), it.get("rows", 4), it.get("cols", 256), it.get("codes"),
+                                   it.get("scale"), it.get("mask"), it.get("op"))
+    return lib.quest_quantize_fwd_op_group(descs, len(items) if count is None else count, dt, block, b, trust, None)
+
+
+# A second operand tensor's buffers, apart from fwd_op's defaults (fake addresses, never dereferenced).
+OP_GOOD = dict(x=F_, scale=G_, op=H_)
+
+
+def test_op_group_empty_calls_are_noops(lib):
+    assert op_group(lib, []) == qa.QUEST_OK
+    assert lib.quest_quantize_fwd_op_group(None, 0, qa.QUEST_BF16, 128, 4, 1.0, None) == qa.QUEST_OK
+    assert op_group(lib, [dict(rows=0), dict(rows=0, cols=2048)]) == qa.QUEST_OK
+
+
+@pytest.mark.parametrize("kw,status", [(kw, st) for kw, st in test_fwd_op_rejects.pytestmark[0].args[1]
+                                       if not {"dt", "block", "b", "trust"} & set(kw)])
+def test_op_group_rejects_what_fwd_op_rejects(lib, kw, status):
+    """A bad tensor anywhere in a group gives quest_quantize_fwd_op's status for it; nothing launches."""
+    bad = dict(x=A, scale=C_, op=E_, rows=4, cols=256)
+    bad.update(kw)
+    assert op_group(lib, [dict(OP_GOOD), bad]) == status
+    assert op_group(lib, [bad, dict(OP_GOOD)]) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(block=32), qa.QUEST_EUNSUPPORTED), (dict(b=5), qa.QUEST_EUNSUPPORTED),
+                                       (dict(dt=7), qa.QUEST_EINVAL), (dict(trust=-0.5), qa.QUEST_EINVAL)])
+def test_op_group_rejects_bad_common_arguments(lib, kw, status):
+    assert op_group(lib, [dict(OP_GOOD)], **kw) == status
+
+
+def test_op_group_rejects_bad_counts(lib):
+    assert op_group(lib, [dict(OP_GOOD)], count=-1) == qa.QUEST_EINVAL
+    assert lib.quest_quantize_fwd_op_group(None, 2, qa.QUEST_BF16, 128, 4, 1.0, None) == qa.QUEST_EINVAL
+
+
+@pytest.mark.parametrize("second", [
+    dict(x=F_, scale=G_, op=E_),  # operand of the second on the first's operand
+    dict(x=F_, scale=G_, op=A),  # operand of the second on the first's input
+    dict(x=F_, scale=C_, op=H_),  # scale of the second on the first's scale
+    dict(x=E_, scale=G_, op=H_),  # input of the second on the first's operand
+    dict(x=F_, scale=G_, op=H_, codes=D_),  # codes of the second on the first's mask
+])
+def test_op_group_rejects_outputs_across_tensors(lib, second):
+    first = dict(x=A, scale=C_, mask=D_, op=E_)
+    assert op_group(lib, [first, dict(second, rows=4, cols=256)]) == qa.QUEST_EINVAL
+
+
+def test_op_group_shared_input_and_rows_zero_pointers_unread(lib):
+    """Inputs may overlap; a rows == 0 tensor's pointers are not read."""
+    first = dict(x=A, scale=C_, op=E_)
+    assert op_group(lib, [first, dict(x=A, scale=G_, op=H_ + 8)]) == qa.QUEST_EALIGN
+    assert op_group(lib, [dict(x=A + 1, rows=0, op=None), dict(first, op=None)]) == qa.QUEST_EINVAL
+
+
 @pytest.mark.parametrize(
     "kw,status",
     [

@@ -84,6 +84,28 @@ def test_fwd_op_rejects_small_or_mistyped_codes_and_mask():
         qa.quantize_fwd_op(x, 128, 4, codes=u8(33 * 128), mask=u8(33 * 32))
 
 
+def test_fwd_op_group_checks_every_tensors_buffers():
+    xs = [torch.zeros((33, 256), dtype=torch.bfloat16), torch.zeros((40, 512), dtype=torch.bfloat16)]
+    ok = [dict(operand=u8(qa.operand_bytes(33, 256)), scale=f32(33)),
+          dict(operand=u8(qa.operand_bytes(40, 512)), scale=f32(40))]
+    with pytest.raises(ValueError, match=r"outs\[1\].operand too small"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[ok[0], dict(ok[1], operand=u8(qa.operand_bytes(40, 512) - 1))])
+    with pytest.raises(ValueError, match=r"outs\[0\].scale too small"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[dict(ok[0], scale=f32(32)), ok[1]])
+    with pytest.raises(ValueError, match=r"outs\[1\].codes too small"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[ok[0], dict(ok[1], codes=u8(40 * 256 - 1))])
+    with pytest.raises(ValueError, match=r"outs\[0\].mask too small"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[dict(ok[0], mask=u8(33 * 32 - 1)), ok[1]])
+    with pytest.raises(ValueError, match="unknown keys"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[dict(ok[0], dq=u8(1)), ok[1]])
+    with pytest.raises(ValueError, match="2 tensors but 1 output sets"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=[ok[0]])
+    with pytest.raises(ValueError, match="share the first one's dtype"):
+        qa.quantize_fwd_op_group([xs[0], xs[1].float()], 128, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=ok)
+
+
 def test_grid_dequantisers_reject_small_inputs():
     with pytest.raises(ValueError, match="codes too small"):
         qa.dequantize_fp4(u8(16 * 256 // 2 - 1), f32(16), 16, 256)

@@ -122,6 +122,84 @@ def test_fwd_op_leaves_bytes_outside_the_operand_alone(dev):
 
 
 # ---------------------------------------------------------------------------
+# Grouped operand forward (quest_quantize_fwd_op_group): every output equal,
+# bit for bit, to one quest_quantize_fwd_op call per tensor.  Operands start
+# zeroed on both sides, so the padding rows the launches leave alone compare
+# too; guard bytes around each operand must stay untouched.
+# ---------------------------------------------------------------------------
+OP_GROUP_CASES = [
+    # (rows, cols, with codes and mask) per tensor, block, b, trust
+    ([(77, 2048, True), (130, 2048, True), (1, 2048, False), (64, 2048, True), (33, 2048, False),
+      (200, 2048, True)], 128, 4, 1.0),  # six tensors of one width: two launches
+    ([(45, 512, True), (33, 1024, False), (0, 2048, True), (96, 2048, True), (21, 5632, True),
+      (37, 384, False)], 64, 2, 1.0),  # three widths, an empty tensor, two tensors outside the grouped widths
+    ([(300, 1024, True), (129, 512, True)], 256, 3, 1.3),
+    ([(31, 2048, False), (2, 512, False)], 128, 1, 1.0),  # neither codes nor mask
+]
+
+
+@pytest.mark.parametrize("specs,block,b,trust", OP_GROUP_CASES)
+def test_fwd_op_group_equals_single_calls(dev, specs, block, b, trust):
+    log(f"fwd_op_group {specs} block {block} b={b} trust {trust}")
+    xs = [make_tensor(TensorSpec(f"opg.x{i}", r, c, "bf16", "student_t", 4, 7300 + 13 * i + r, outlier_cols=max(1, c // 100),
+                                 outlier_scale=20.0), dev) for i, (r, c, _) in enumerate(specs)]
+    guard = 256
+
+    def buffers():
+        outs, bufs = [], []
+        for (r, c, q) in specs:
+            n = qa.operand_bytes(r, c)
+            buf = torch.full((n + 2 * guard,), 0xA5, dtype=torch.uint8, device=dev)
+            buf[guard:guard + n].zero_()
+            o = dict(operand=buf[guard:guard + n], scale=torch.zeros((r,), dtype=torch.float32, device=dev))
+            if q:
+                o["codes"] = torch.zeros((r, c * b // 8), dtype=torch.uint8, device=dev)
+                o["mask"] = torch.zeros((r, c // 8), dtype=torch.uint8, device=dev)
+            outs.append(o)
+            bufs.append(buf)
+        return outs, bufs
+
+    single, single_bufs = buffers()
+    for x, o in zip(xs, single):
+        qa.quantize_fwd_op(x, block, b, trust=trust, **o)
+    grouped, grouped_bufs = buffers()
+    res = qa.quantize_fwd_op_group(xs, block, b, trust=trust, outs=grouped)
+    torch.cuda.synchronize()
+    for i, ((r, c, q), o1, o2, b1, b2) in enumerate(zip(specs, single, grouped, single_bufs, grouped_bufs)):
+        assert res[i][3].data_ptr() == o2["operand"].data_ptr()
+        n = qa.operand_bytes(r, c)
+        assert bool((b2[:guard] == 0xA5).all()) and bool((b2[guard + n:] == 0xA5).all()), f"tensor {i}: guard bytes"
+        for key in o1:
+            assert torch.equal(o1[key], o2[key]), f"tensor {i} ({r}x{c}): {key} differs from the single call"
+    # the first ragged tensor against the oracle as well (the single calls are checked in the tests above)
+    i = next((j for j, (r, c, q) in enumerate(specs) if q and r > 0), None)
+    if i is None:
+        log("fwd_op_group ok (no tensor with codes)")
+        return
+    r, c, _ = specs[i]
+    st = check_fwd(to_float64(xs[i]), block, b, grouped[i]["codes"].cpu().numpy(), grouped[i]["scale"].cpu().numpy(),
+                   grouped[i]["mask"].cpu().numpy(), trust=trust)
+    log(f"fwd_op_group ok, tensor {i} {r}x{c} {st}")
+
+
+def test_fwd_op_group_at_the_layer_shapes(dev):
+    """The two operand forwards of a 2048-feature layer at 16384 tokens, as the layer launches them."""
+    shapes = [(16384, 2048), (2048, 2048)]
+    log(f"fwd_op_group at {shapes}")
+    xs = [make_tensor(TensorSpec("opg.act", 16384, 2048, "bf16", "student_t", 4, 7400, outlier_cols=20,
+                                 outlier_scale=20.0), dev),
+          make_tensor(TensorSpec("opg.wt", 2048, 2048, "bf16", "normal", 0.02, 7401), dev)]
+    singles = [qa.quantize_fwd_op(x, 128, 4, with_codes=True, with_mask=True) for x in xs]
+    outs = [dict(codes=torch.empty_like(s[0]), scale=torch.empty_like(s[1]), mask=torch.empty_like(s[2]),
+                 operand=torch.empty_like(s[3])) for s in singles]
+    qa.quantize_fwd_op_group(xs, 128, 4, outs=outs)
+    torch.cuda.synchronize()
+    for (r, c), s, o in zip(shapes, singles, outs):
+        assert torch.equal(s[0], o["codes"]) and torch.equal(s[1], o["scale"]) and torch.equal(s[2], o["mask"])
+        assert torch.equal(s[3], o["operand"])  # rows are whole 32-row blocks: no padding
+
+
+# ---------------------------------------------------------------------------
 # The product on oracle-built operands.
 # ---------------------------------------------------------------------------
 

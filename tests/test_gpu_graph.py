@@ -110,3 +110,23 @@ def test_operand_forward_and_product_in_a_graph(dev, out_dtype):
         qa.gemm(oa, sa, m, 4, ow, sw, n, 4, k, out=y)
 
     replay_and_check(capture(step), [sa, oa, sw, ow, y], [sa_e, oa_e, sw_e, ow_e, y_e], "operand forwards + product")
+
+
+def test_grouped_operand_forwards_in_a_graph(dev):
+    shapes = [(1024, 2048), (512, 2048), (96, 512)]
+    log(f"graph of one grouped operand forward over {shapes}")
+    xs = [make_tensor(TensorSpec(f"graph.ox{i}", r, c, "bf16", "student_t", 4, 9900 + i), dev)
+          for i, (r, c) in enumerate(shapes)]
+    refs = qa.quantize_fwd_op_group(xs, 128, 4, outs=[
+        dict(codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
+             mask=torch.empty((r, c // 8), dtype=torch.uint8, device=dev)) for r, c in shapes])
+    torch.cuda.synchronize()
+    outs = [{k: torch.empty_like(t) for k, t in zip(("codes", "scale", "mask", "operand"), ref)} for ref in refs]
+
+    def step():
+        qa.quantize_fwd_op_group(xs, 128, 4, outs=outs)
+
+    graph = capture(step)
+    keys = ("codes", "scale", "mask", "operand")
+    replay_and_check(graph, [o[k] for o in outs for k in keys], [t for ref in refs for t in ref],
+                     "grouped operand forward")

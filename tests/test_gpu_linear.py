@@ -195,6 +195,31 @@ def test_linear_matches_oracle(dev, n, k, m, block, bx, bw, fp6, compute_dtype):
     close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
 
 
+@pytest.mark.parametrize("trust_x,trust_w", [(1.0, 1.3), (1.3, 1.3)])
+def test_linear_fp6_with_outer_trust_factors(dev, trust_x, trust_w):
+    """The FP6 layer with one bit width and explicit trust factors: equal ones quantise both operands
+    in one grouped launch, different ones in two calls; both against the oracle with those factors."""
+    n, k, m, block, bits, compute_dtype = 128, 1024, 96, 128, 3, torch.bfloat16
+    log(f"linear {n}x{k} by {m}x{k}, b={bits}, trust x {trust_x} w {trust_w}")
+    x = make_tensor(TensorSpec("tr.x", n, k, "bf16", "student_t", 4, 9400, outlier_cols=k // 100,
+                               outlier_scale=20.0), dev)
+    w = make_tensor(TensorSpec("tr.w", m, k, "bf16", "normal", 0.02, 9401), dev)
+    dy = make_tensor(TensorSpec("tr.dy", n, m, "bf16", "normal", 1e-3, 9402), dev)
+    xg, wg = x.clone().requires_grad_(True), w.clone().requires_grad_(True)
+    y = quest_linear(xg, wg, block=block, bits_x=bits, bits_w=bits, compute_dtype=compute_dtype,
+                     trust_x=trust_x, trust_w=trust_w)
+    assert layer_node(y).fp6 is True
+    y.backward(dy)
+    torch.cuda.synchronize()
+    f = qo.qat_linear_fwd(to_float64(x), to_float64(w), block, bits, bits, trust_x, trust_w)
+    dx_ref, dw_ref = qo.qat_linear_bwd(to_float64(dy), f, block)
+    skip_y, skip_dx, skip_dw = band_reach(f, bits, bits, block, trust_x, trust_w)
+    tols = TOLS[compute_dtype]
+    close_relative(y.detach(), f["y"], "y", Y_TOL_FP6[compute_dtype], skip_y, oracle_slack(f))
+    close(xg.grad, dx_ref, "dx", tols, skip_dx, block)
+    close(wg.grad, dw_ref, "dw", tols, skip_dw, block)
+
+
 @pytest.mark.parametrize("compute_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("grid,bx,bw", [("fp4", 4, 4), ("sparse24", 4, 4), ("sparse24", 2, 3)])
 def test_linear_grids_match_oracle(dev, grid, bx, bw, compute_dtype):
