@@ -110,6 +110,50 @@ __device__ __forceinline__ CodeWords<B> quantise_run(const float (&v)[RUN], floa
   return cw;
 }
 
+// b = 2 or 4: the codes of 8 transformed values as bytes, 8 / b entries
+// interleaved over the dwords: entry (8 / b) k + j is byte k of acc[j]
+// (v_cvt_pk_u8_f32 rounds to nearest even and saturates, as grid_code).
+template <int B>
+__device__ __forceinline__ void quantise8_bytes(const float* v, float kk, uint32_t (&acc)[8 / B]) {
+  static_assert(B == 2 || B == 4, "byte codes of 2 or 4 bits");
+  constexpr int PER_BYTE = 8 / B;
+  constexpr float L = static_cast<float>(1 << B);
+  const float off = 0.5f * (L - 1.f);
+#pragma unroll
+  for (int j = 0; j < PER_BYTE; ++j) acc[j] = 0u;
+#pragma unroll
+  for (int k = 0; k < 8 / PER_BYTE; ++k) {
+#pragma unroll
+    for (int j = 0; j < PER_BYTE; ++j) {
+      const float t = __builtin_fminf(__builtin_fmaf(v[k * PER_BYTE + j], kk, off), L - 1.f);
+      acc[j] = __builtin_amdgcn_cvt_pk_u8_f32(t, k, acc[j]);
+    }
+  }
+}
+
+// The byte codes of quantise8_bytes packed LSB-first (entry i in bits
+// [b i, b i + b)).
+template <int B>
+__device__ __forceinline__ uint32_t pack8_bytes(const uint32_t (&acc)[8 / B]) {
+  uint32_t w = acc[0];
+#pragma unroll
+  for (int j = 1; j < 8 / B; ++j) w |= acc[j] << (B * j);
+  return w;
+}
+
+// The levels h = u - (L - 1)/2 of the byte codes of quantise8_bytes, entry
+// order (each byte converted by one v_cvt_f32_ubyte).
+template <int B>
+__device__ __forceinline__ void levels8_from_bytes(const uint32_t (&acc)[8 / B], float* h) {
+  constexpr int PER_BYTE = 8 / B;
+  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
+#pragma unroll
+  for (int k = 0; k < 8 / PER_BYTE; ++k)
+#pragma unroll
+    for (int j = 0; j < PER_BYTE; ++j)
+      h[k * PER_BYTE + j] = static_cast<float>((acc[j] >> (8 * k)) & 0xFFu) - kHalf;
+}
+
 // Quantise 8 transformed values (a quarter run) into b-bit codes packed
 // LSB-first into the low 8 b bits of the result: the same arithmetic as
 // quantise_run, on 8 entries.
@@ -126,23 +170,9 @@ __device__ __forceinline__ uint32_t quantise8(const float* v, float kk) {
     for (int j = 7; j >= 0; --j) s = __builtin_amdgcn_alignbit(s, __float_as_uint(__builtin_fmaf(v[j], kk, 0.f)), 31);
     return ~s & 0xFFu;
   } else if constexpr (B == 2 || B == 4) {
-    constexpr int PER_BYTE = 8 / B;
-    const float off = 0.5f * (L - 1.f);
-    uint32_t acc[PER_BYTE];
-#pragma unroll
-    for (int j = 0; j < PER_BYTE; ++j) acc[j] = 0u;
-#pragma unroll
-    for (int k = 0; k < 8 / PER_BYTE; ++k) {
-#pragma unroll
-      for (int j = 0; j < PER_BYTE; ++j) {
-        const float t = __builtin_fminf(__builtin_fmaf(v[k * PER_BYTE + j], kk, off), L - 1.f);
-        acc[j] = __builtin_amdgcn_cvt_pk_u8_f32(t, k, acc[j]);
-      }
-    }
-    uint32_t w = acc[0];
-#pragma unroll
-    for (int j = 1; j < PER_BYTE; ++j) w |= acc[j] << (B * j);
-    return w;
+    uint32_t acc[8 / B];
+    quantise8_bytes<B>(v, kk, acc);
+    return pack8_bytes<B>(acc);
   } else {
     uint32_t w = 0u;
 #pragma unroll
@@ -317,14 +347,8 @@ __device__ __forceinline__ void store_operand_run(const float (&v)[RUN], float k
 // (48 bits) are split into a low dword and a high half-word, and a
 // transpose between lane quarters and slots hands lane l the four quarters
 // of run l: its six dwords, in field order.
-template <int B>
-__device__ __forceinline__ void mfma_operand_words(const float (&v)[RUN], const float (&kk)[4], uint32_t (&w)[6]) {
-  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
-  float h[RUN];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[8 * j + i] = grid_code<B>(v[8 * j + i], kk[j]) - kHalf;
+// The operand words of levels h already computed (in the layout of v).
+__device__ __forceinline__ void mfma_operand_words_of_levels(const float (&h)[RUN], uint32_t (&w)[6]) {
   uint32_t d[6];
   e2m3_pack32(h, d);
   uint32_t lo[4] = {d[0], (d[1] >> 16) | (d[2] << 16), d[3], (d[4] >> 16) | (d[5] << 16)};
@@ -337,6 +361,17 @@ __device__ __forceinline__ void mfma_operand_words(const float (&v)[RUN], const 
   w[3] = lo[2];
   w[4] = hi[2] | (lo[3] << 16);
   w[5] = (lo[3] >> 16) | (hi[3] << 16);
+}
+
+template <int B>
+__device__ __forceinline__ void mfma_operand_words(const float (&v)[RUN], const float (&kk)[4], uint32_t (&w)[6]) {
+  constexpr float kHalf = 0.5f * static_cast<float>((1 << B) - 1);
+  float h[RUN];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[8 * j + i] = grid_code<B>(v[8 * j + i], kk[j]) - kHalf;
+  mfma_operand_words_of_levels(h, w);
 }
 
 // Six operand dwords (one run) to byte offset `off` of `op_r` (kNowhere drops them).
@@ -524,14 +559,26 @@ __device__ __forceinline__ float e2m1_mag(uint32_t c) {
 // per run).
 // kFp4: FP4 codes (E2M1 patterns of the nearest level, B = 4) instead of the
 // midrise grid's.
-template <int B, bool kFp4 = false>
+// kLevels (b = 2 or 4, midrise grid): also returns in h the levels
+// h = u - (L - 1)/2 of the codes, in the layout of v, converted from the code
+// bytes (for the matrix-core operand, which holds those levels).
+template <int B, bool kFp4 = false, bool kLevels = false>
 __device__ __forceinline__ void mfma_quantise_store(const float (&v)[RUN], const float (&kk)[4],
-                                                    const float (&thr)[4], int lane, rsrc_t codes_r, rsrc_t mask_r) {
+                                                    const float (&thr)[4], int lane, rsrc_t codes_r, rsrc_t mask_r,
+                                                    float* h = nullptr) {
   static_assert(!kFp4 || B == 4, "FP4 codes are 4 bits");
+  static_assert(!kLevels || (!kFp4 && (B == 2 || B == 4)), "levels from byte codes: midrise grid, b = 2 or 4");
   uint32_t cp[4], mp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cp[j] = kFp4 ? fp4_codes8(v + 8 * j, kk[j]) : quantise8<B>(v + 8 * j, kk[j]);
+    if constexpr (kLevels) {
+      uint32_t acc[8 / B];
+      quantise8_bytes<B>(v + 8 * j, kk[j], acc);
+      cp[j] = pack8_bytes<B>(acc);
+      levels8_from_bytes<B>(acc, h + 8 * j);
+    } else {
+      cp[j] = kFp4 ? fp4_codes8(v + 8 * j, kk[j]) : quantise8<B>(v + 8 * j, kk[j]);
+    }
     mp[j] = 0u;
     push8_abs_le(mp[j], v + 8 * j, thr[j]);
   }
@@ -665,14 +712,22 @@ __device__ __forceinline__ void fwd_mfma_tile(const uint16_t* __restrict__ x, in
       }
     }
     const int64_t run0 = t * 64;
+    // With codes and an operand, the operand's levels come from the code
+    // bytes (b = 2, 4) instead of a second rounding of v.
+    constexpr bool kLevels = kIsOperand<Dq> && kQuant && !kFp4 && (B == 2 || B == 4);
+    float h[kLevels ? RUN : 1];
     if (kQuant)
-      mfma_quantise_store<B, kFp4>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
-                                   window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4));
+      mfma_quantise_store<B, kFp4, kLevels>(v, kk, thr, lane,
+                                            window_at(codes, run0 * 4 * B, codes_total, 64 * 4 * B),
+                                            window_at(mask, run0 * 4, mask ? total_runs * 4 : 0, 64 * 4), h);
     if constexpr (kIsOperand<Dq>) {
       // After the transpose lane l holds run l of the tile.  The workgroup's
       // four tiles are 4 ROWS consecutive rows of one 32-row block.
       uint32_t w[6];
-      mfma_operand_words<B>(v, kk, w);
+      if constexpr (kLevels)
+        mfma_operand_words_of_levels(h, w);
+      else
+        mfma_operand_words<B>(v, kk, w);
       stage_operand_words(opstage, lane & ((1 << LOGR) - 1), wave * ROWS + (lane >> LOGR), 4 * ROWS, w);
       __syncthreads();
       const int64_t row0 = (t - wave) * ROWS;
@@ -832,9 +887,14 @@ __device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, in
   // belong to the next workgroup.
   const int64_t run0 = wg_first_run + 64 * wave;
   const int64_t run_end = wg_first_run + wg_runs < total_runs ? wg_first_run + wg_runs : total_runs;
+  // With codes and an operand, the operand's levels come from the code bytes
+  // (b = 2, 4) instead of a second rounding of v.
+  constexpr bool kLevels = kIsOperand<Dq> && kQuant && (B == 2 || B == 4);
+  float h[kLevels ? RUN : 1];
   if (kQuant)
-    mfma_quantise_store<B>(v, kk, thr, lane, window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
-                           window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4));
+    mfma_quantise_store<B, false, kLevels>(v, kk, thr, lane,
+                                           window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
+                                           window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4), h);
   if constexpr (kIsOperand<Dq>) {
     // After the transpose lane l holds run 64 w + l of the workgroup.  The
     // workgroup's rows lie in one 32-row block (rows_per_wg divides 32 and
@@ -849,7 +909,10 @@ __device__ __forceinline__ void fwd_mfma_rows(const uint16_t* __restrict__ x, in
     const int wr = 64 * wave + lane;
     const int lrow = wr / runs_per_row;
     uint32_t w[6];
-    mfma_operand_words<B>(v, kk, w);
+    if constexpr (kLevels)
+      mfma_operand_words_of_levels(h, w);
+    else
+      mfma_operand_words<B>(v, kk, w);
     uint8_t* st = reinterpret_cast<uint8_t*>(rows_lds);
     if (lrow < rows_per_wg) stage_operand_words(st, wr - lrow * runs_per_row, lrow, rows_per_wg, w);
     __syncthreads();
