@@ -420,8 +420,9 @@ def qat_linear_step(torch, dev, reps):
     """One training step (forward and backward) of the QuEST linear layer against BF16.
 
     The q projection of the block (16384 tokens x 2048 by 2048 x 2048), b = 4
-    for both operands, block 128, bf16 compute: quest_linear (two operand
-    forwards with codes and mask, the FP6 product; in the backward both
+    for both operands, block 128, bf16 compute: quest_linear (both operand
+    forwards with codes and mask in one grouped launch, the FP6 product; in
+    the backward both
     operands rebuilt from their codes in one launch, the two BF16 gradient
     products, and both gradients masked and transformed back in one launch)
     against torch's BF16 linear, each as

@@ -182,6 +182,26 @@ def test_fwd_op_group_equals_single_calls(dev, specs, block, b, trust):
     log(f"fwd_op_group ok, tensor {i} {r}x{c} {st}")
 
 
+def test_fwd_op_group_fp32_tensors_equal_single_calls(dev):
+    """fp32 tensors take one quest_quantize_fwd_op launch each inside the group call."""
+    shapes = [(50, 2048), (37, 384), (29, 640)]
+    log(f"fwd_op_group fp32 {shapes}")
+    xs = [make_tensor(TensorSpec(f"opg.f{i}", r, c, "f32", "student_t", 4, 7500 + i, outlier_cols=max(1, c // 100),
+                                 outlier_scale=20.0), dev) for i, (r, c) in enumerate(shapes)]
+    singles = [qa.quantize_fwd_op(x, 128, 3, trust=1.3, with_codes=True, with_mask=True) for x in xs]
+    outs = [dict(codes=torch.empty_like(s[0]), mask=torch.empty_like(s[2]),
+                 operand=torch.zeros_like(s[3])) for s in singles]
+    for s in singles:
+        s[3].zero_()
+    singles = [qa.quantize_fwd_op(x, 128, 3, trust=1.3, with_codes=True, with_mask=True, operand=s[3])
+               for x, s in zip(xs, singles)]
+    res = qa.quantize_fwd_op_group(xs, 128, 3, trust=1.3, outs=outs)
+    torch.cuda.synchronize()
+    for i, (s, r) in enumerate(zip(singles, res)):
+        for a, b, what in zip(s, r, ("codes", "scale", "mask", "operand")):
+            assert torch.equal(a, b), f"tensor {i}: {what} differs from the single call"
+
+
 def test_fwd_op_group_at_the_layer_shapes(dev):
     """The two operand forwards of a 2048-feature layer at 16384 tokens, as the layer launches them."""
     shapes = [(16384, 2048), (2048, 2048)]
