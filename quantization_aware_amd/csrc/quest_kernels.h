@@ -941,6 +941,78 @@ __global__ void __launch_bounds__(1024)
                                      fwd_wg_index<Dq>());
 }
 
+// The operand output of bf16 rows of 16 m runs, 4 < m <= 4 NC, one row per
+// wave and four rows per workgroup.  The wave loads its whole row at once (m 16-run groups as
+// in quest_fwd_mfma_kernel; groups past the row read zeros), adds the
+// groups' sums of squares in group order (the row kernel's order, so the
+// scale is the same) and then transforms and quantises the row 64 runs at a
+// time: no barrier before the quantisation.  The operand output stages the
+// four rows' pieces in LDS (one barrier) and writes them as 96-byte pieces,
+// as the row kernel does.
+template <int LOGN, int B, typename Dq, bool kQuant, int NC>
+__global__ void __launch_bounds__(256)
+    quest_fwd_mfma_rowwave_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, FwdConsts k,
+                                  uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                  uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
+  constexpr int R = 4;  // rows per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
+  const int64_t row0 = fwd_wg_index<Dq>() * R;
+  const int64_t row = row0 + wave;
+  const int groups = runs_per_row >> 4;
+  const int64_t total_runs = rows * runs_per_row;
+  const int64_t run_first = row * runs_per_row;  // past the tensor for rows past `rows`
+  const int64_t run_end = run_first + runs_per_row < total_runs ? run_first + runs_per_row : total_runs;
+  const bf16x8_t h0 = hadamard_fragment(lane, 0);
+  const bf16x8_t h1 = hadamard_fragment(lane, 1);
+  const rsrc_t in_r = window_at(x, run_first * 64, total_runs * 64, static_cast<uint32_t>(runs_per_row) * 64);
+  const int in_off = 64 * (lane & 15) + 16 * (lane >> 4);
+  u32x4 f[4 * NC];
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j) f[j] = __builtin_amdgcn_raw_buffer_load_b128(in_r, in_off + 1024 * j, 0, kNonTemporal);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4 * NC; ++j)
+    if (j < groups) ss += group_sum(sum_squares_fragment(f[j]), 6);
+  static_assert(kIsOperand<Dq>, "the operand output");
+  uint8_t* st = reinterpret_cast<uint8_t*>(rows_lds);
+  float row_scale = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v[RUN];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mfma_run_outputs(h0, h1, f[4 * c + j], v + 8 * j);
+    const float tau = fwht_cross_lanes<LOGN, true>(v, lane);
+    const RowConsts rc = row_consts(ss, tau, k);
+    row_scale = rc.scale;
+    const float kk[4] = {rc.kk, rc.kk, rc.kk, rc.kk};
+    const float thr[4] = {rc.thr, rc.thr, rc.thr, rc.thr};
+    const int64_t run0 = run_first + 64 * c;
+    constexpr bool kLevels = kQuant && (B == 2 || B == 4);
+    float h[kLevels ? RUN : 1];
+    if (kQuant)
+      mfma_quantise_store<B, false, kLevels>(v, kk, thr, lane,
+                                             window_at(codes, run0 * 4 * B, codes ? run_end * 4 * B : 0, 64 * 4 * B),
+                                             window_at(mask, run0 * 4, mask ? run_end * 4 : 0, 64 * 4), h);
+    // After the transpose lane l holds run 64 c + l of the row.
+    uint32_t w[6];
+    if constexpr (kLevels)
+      mfma_operand_words_of_levels(h, w);
+    else
+      mfma_operand_words<B>(v, kk, w);
+    if (64 * c + lane < runs_per_row) stage_operand_words(st, 64 * c + lane, wave, R, w);
+  }
+  const rsrc_t scale_r = window_at(scale, row0 * 4, rows * 4, R * 4);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(row_scale), scale_r, lane == 0 ? wave * 4 : kNowhere, 0, 0);
+  // The four rows lie in one 32-row block (row0 is a multiple of 4); rows
+  // past `rows` land in the last block's padding rows.
+  const int64_t rb_bytes = static_cast<int64_t>(k.chunks) * kOpBlockBytes;
+  const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
+                                static_cast<uint32_t>(rb_bytes));
+  __syncthreads();
+  flush_operand(st, R, runs_per_row, static_cast<int>(row0 & 31), op_r, static_cast<int>(threadIdx.x), 256);
+}
+
 template <int LOGN, int B, int LOGR>
 __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, FwdConsts k) {
   const int lane = threadIdx.x & 63;
@@ -1371,6 +1443,38 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
   Dq* dq = static_cast<Dq*>(a.dq);
   hipStream_t stream = a.stream;
   if constexpr (sizeof(In) == 2 && B <= 4) {
+    if constexpr (kIsOperand<Dq>) {
+      if (a.allow_mfma && runs_per_row > 64 && runs_per_row <= 256 && runs_per_row % 16 == 0) {
+        // The operand of rows up to 8192 columns: one row per wave
+        // (quest_fwd_mfma_rowwave_kernel).  At 16384 x 5632 46.2-47.2 us
+        // against 62.4-62.5 for the row kernel below, and 64.8-67.5 against
+        // 80.7-83.0 with codes and mask.  The other outputs keep the row
+        // kernel, which was faster for them (codes and mask alone: 46.2-47.4
+        // against 58.1-58.2 us with one row per wave).
+        const int nc = (runs_per_row / 16 + 3) / 4;  // 64-run chunks per row: 2, 3 or 4
+        const int64_t grid = (rows + 3) / 4;
+        const size_t lds = static_cast<size_t>(runs_per_row) * (24 * 4 + kOpStagePad);
+        auto run = [&](auto chunks, auto quant) {
+          hipLaunchKernelGGL(
+              (quest_fwd_mfma_rowwave_kernel<LOGN, B, Dq, decltype(quant)::value, decltype(chunks)::value>),
+              dim3(static_cast<uint32_t>(grid)), dim3(256), lds, stream, x, rows, runs_per_row, k, a.codes, a.scale,
+              mask32, dq);
+        };
+        auto run_nc = [&](auto quant) {
+          if (nc == 2)
+            run(std::integral_constant<int, 2>{}, quant);
+          else if (nc == 3)
+            run(std::integral_constant<int, 3>{}, quant);
+          else
+            run(std::integral_constant<int, 4>{}, quant);
+        };
+        if (a.codes || a.mask)
+          run_nc(std::true_type{});
+        else
+          run_nc(std::false_type{});
+        return hipGetLastError();
+      }
+    }
     if (a.allow_mfma && runs_per_row > 64 && runs_per_row % 16 == 0) {
       // One row per workgroup when its last wave leaves at most an eighth of
       // the lanes idle (5632 columns: 176 runs in 3 waves): small workgroups

@@ -55,8 +55,9 @@ def gpu_fields(op: torch.Tensor, rows: int, cols: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # The operand forward, every kernel family: matrix-core tiles (16, 32, 64
-# runs per row), matrix-core wide rows, run-per-lane tiles and rows (fp32,
-# and run counts that are not powers of two); ragged row counts.
+# runs per row), matrix-core wide rows (one row per wave up to 8192 columns,
+# the row kernel beyond), run-per-lane tiles and rows (fp32, and run counts
+# that are not powers of two); ragged row counts.
 # ---------------------------------------------------------------------------
 FWD_OP_CASES = [
     # rows, cols, dtype, block, b, trust
@@ -70,8 +71,10 @@ FWD_OP_CASES = [
     (29, 640, "f32", 128, 3, 1.0),
     (64, 128, "bf16", 128, 4, 1.0),
     (1, 256, "f32", 256, 1, 1.3),
-    (7, 10752, "bf16", 128, 4, 1.0),  # wide rows, 3 rows per workgroup: unstaged stores
-    (130, 4096, "bf16", 128, 2, 1.0),  # wide rows, 1 row per workgroup
+    (7, 10752, "bf16", 128, 4, 1.0),  # rows wider than 8192 columns: the row kernel, 3 rows per workgroup
+    (130, 4096, "bf16", 128, 2, 1.0),  # one row per wave, 2 chunks of 64 runs
+    (9, 8192, "bf16", 128, 3, 1.0),  # one row per wave, 4 full chunks
+    (33, 7168, "bf16", 64, 4, 1.3),  # one row per wave, 4 chunks, the last one half empty
 ]
 
 
