@@ -949,12 +949,14 @@ __global__ void __launch_bounds__(1024)
 // time: no barrier before the quantisation.  The operand output stages the
 // four rows' pieces in LDS (one barrier) and writes them as 96-byte pieces,
 // as the row kernel does.
+constexpr int kRowWaveRows = 4;  // rows (waves) per workgroup of quest_fwd_mfma_rowwave_kernel
+
 template <int LOGN, int B, typename Dq, bool kQuant, int NC>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * kRowWaveRows)
     quest_fwd_mfma_rowwave_kernel(const uint16_t* __restrict__ x, int64_t rows, int runs_per_row, FwdConsts k,
                                   uint8_t* __restrict__ codes, float* __restrict__ scale,
                                   uint32_t* __restrict__ mask, Dq* __restrict__ dq) {
-  constexpr int R = 4;  // rows per workgroup
+  constexpr int R = kRowWaveRows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   const int64_t row0 = fwd_wg_index<Dq>() * R;
@@ -1010,7 +1012,7 @@ __global__ void __launch_bounds__(256)
   const rsrc_t op_r = window_at(dq, (row0 >> 5) * rb_bytes, ((rows + 31) >> 5) * rb_bytes,
                                 static_cast<uint32_t>(rb_bytes));
   __syncthreads();
-  flush_operand(st, R, runs_per_row, static_cast<int>(row0 & 31), op_r, static_cast<int>(threadIdx.x), 256);
+  flush_operand(st, R, runs_per_row, static_cast<int>(row0 & 31), op_r, static_cast<int>(threadIdx.x), 64 * R);
 }
 
 template <int LOGN, int B, int LOGR>
@@ -1452,13 +1454,13 @@ hipError_t fwd_dispatch(const In* x, const FwdLaunch& a) {
         // kernel, which was faster for them (codes and mask alone: 46.2-47.4
         // against 58.1-58.2 us with one row per wave).
         const int nc = (runs_per_row / 16 + 3) / 4;  // 64-run chunks per row: 2, 3 or 4
-        const int64_t grid = (rows + 3) / 4;
-        const size_t lds = static_cast<size_t>(runs_per_row) * (24 * 4 + kOpStagePad);
+        const int64_t grid = (rows + kRowWaveRows - 1) / kRowWaveRows;
+        const size_t lds = static_cast<size_t>(runs_per_row) * (24 * kRowWaveRows + kOpStagePad);
         auto run = [&](auto chunks, auto quant) {
           hipLaunchKernelGGL(
               (quest_fwd_mfma_rowwave_kernel<LOGN, B, Dq, decltype(quant)::value, decltype(chunks)::value>),
-              dim3(static_cast<uint32_t>(grid)), dim3(256), lds, stream, x, rows, runs_per_row, k, a.codes, a.scale,
-              mask32, dq);
+              dim3(static_cast<uint32_t>(grid)), dim3(64 * kRowWaveRows), lds, stream, x, rows, runs_per_row, k,
+              a.codes, a.scale, mask32, dq);
         };
         auto run_nc = [&](auto quant) {
           if (nc == 2)
