@@ -779,7 +779,8 @@ __global__ void __launch_bounds__(256)
 // scalar registers; per tensor the work is quest_fwd_mfma_kernel's, and a
 // workgroup may span two tensors, with no barrier in this path), then the
 // rows of wider tensors (2560 to 8192 columns), one row per workgroup as in
-// the matrix-core row kernel.
+// the matrix-core row kernel.  The launch takes the wide rows' workgroups
+// first, then the tile workgroups.
 constexpr int kFwdGroupMax = 8;
 constexpr int kFwdGroupWideMax = 4;
 
@@ -792,7 +793,7 @@ struct FwdGroup {
   float* scale[kFwdGroupMax];
   uint32_t* mask[kFwdGroupMax];
   // Wide tensors (rows of 16 m runs, 4 < m <= 16): one row per workgroup,
-  // after the tile workgroups.
+  // before the tile workgroups.
   int wide_count;                               // 0 .. kFwdGroupWideMax
   int64_t wide_first_row[kFwdGroupWideMax + 1];  // running row counts
   int wide_runs[kFwdGroupWideMax];               // runs per row
@@ -1019,12 +1020,15 @@ template <int LOGN, int B, int LOGR>
 __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, FwdConsts k) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
-  const int64_t tile_wgs = (g.first_tile[g.count] + 3) / 4;
-  if (static_cast<int64_t>(blockIdx.x) >= tile_wgs) {
+  const int64_t wide_wgs = g.wide_first_row[g.wide_count];
+  if (static_cast<int64_t>(blockIdx.x) < wide_wgs) {
     // A row of a wide tensor: the row kernel's work with one row per
     // workgroup of four waves (runs past the row read zeros and store
-    // nothing; a wave wholly past it only joins the barrier).
-    const int64_t row = static_cast<int64_t>(blockIdx.x) - tile_wgs;
+    // nothing; a wave wholly past it only joins the barrier).  These
+    // workgroups, each a longer chain (row load, barrier, quantise), are
+    // dispatched first so that the short tile workgroups fill in behind them
+    // instead of leaving them as the launch's tail.
+    const int64_t row = static_cast<int64_t>(blockIdx.x);
     int i = 0;
 #pragma unroll
     for (int j = 1; j < kFwdGroupWideMax; ++j)
@@ -1036,7 +1040,7 @@ __global__ void __launch_bounds__(256) quest_fwd_mfma_group_kernel(FwdGroup g, F
                                              nullptr, row - g.wide_first_row[i]);
     return;
   }
-  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t tile = (static_cast<int64_t>(blockIdx.x) - wide_wgs) * 4 + wave;
   const uint16_t* x = g.x[0];
   uint8_t* codes = g.codes[0];
   float* scale = g.scale[0];
